@@ -1,0 +1,186 @@
+/*
+ * dsa.h -- C ABI of the sparse MQA attention step for AMD Instinct MI355X (gfx950).
+ *
+ * The step has three stages, each a call here (all asynchronous on the
+ * caller's HIP stream, none allocating device memory):
+ *
+ *   dsa_index_scores  score every compressed KV row for every query
+ *   dsa_topk          keep the index_topk best visible rows per query
+ *   dsa_window_idx    the sliding-window part of each query's index row
+ *   dsa_sparse_attn   attend all heads over the rows an index row names
+ *
+ * Citations refer to the DeepSeek V4.1 model pages ("attention/attend/selected",
+ * "reindex-layer/read-weights") by the class or function that holds the step.
+ *
+ * Conventions shared by every call:
+ *  - Device pointers are caller-owned memory on the current HIP device; the
+ *    library never frees or retains them past the call.  Every call only
+ *    enqueues kernels on `stream` (NULL = the legacy default stream) and
+ *    returns without synchronising.
+ *  - Tensors are dense, row-major, in the stated layout.  Where a batch stride
+ *    is taken, it is in elements (rows * row length for a dense batch), so a
+ *    cache slice [:B, :n] of a larger [max_B, max_n, D] buffer can be passed
+ *    without a copy.
+ *  - Return value: DSA_OK (0) on success, a negative DSA_ERR_* code otherwise.
+ *    Invalid arguments are rejected before anything is enqueued; the reason
+ *    is available from dsa_last_error() (thread-local text, valid until the
+ *    next call on the same thread).  No C++ exception crosses the ABI.
+ *  - Index values inside idx rows are not range-checked on the device (as on
+ *    the pages, an out-of-range index is a caller error); -1 marks an empty
+ *    slot.
+ */
+#ifndef DSA_H_
+#define DSA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_ABI_VERSION 1
+
+typedef struct ihipStream_t* dsa_stream_t; /* a hipStream_t */
+
+enum dsa_status {
+  DSA_OK = 0,
+  DSA_ERR_NULL = -1,        /* a required pointer is NULL */
+  DSA_ERR_SHAPE = -2,       /* a size is negative, zero where it may not be, or inconsistent */
+  DSA_ERR_DTYPE = -3,       /* unknown dtype or format code */
+  DSA_ERR_UNSUPPORTED = -4, /* valid arguments with no instantiated kernel (e.g. head_dim 96) */
+  DSA_ERR_HIP = -5,         /* the HIP runtime reported an error at launch */
+  DSA_ERR_WORKSPACE = -6    /* workspace NULL or smaller than the size the query returns */
+};
+
+enum dsa_dtype {
+  DSA_F32 = 0,  /* IEEE binary32 */
+  DSA_BF16 = 1  /* bfloat16 */
+};
+
+enum dsa_kv_format {
+  DSA_KV_DENSE = 0,        /* rows of D elements in the call's dtype */
+  DSA_KV_FP4_E4M3_G16 = 1  /* rows of D/2 bytes of e2m1 nibbles (element 2k in the low
+                              nibble of byte k) plus D/16 E4M3 scale bytes, one per 16
+                              consecutive elements (compressed KV of `_compress_kv`);
+                              only with dtype DSA_BF16 */
+};
+
+/* Library identity. */
+int dsa_abi_version(void);
+const char* dsa_last_error(void);
+
+/*
+ * Index scores (`Indexer.forward`: einsum of the index query heads with the
+ * shared index key per compressed row, ReLU, weighted by `weights_proj`,
+ * summed over heads; invisible groups masked to -inf):
+ *
+ *   scores[b,t,j] = w_scale * sum_h w[b,t,h] * max(0, sum_d q_idx[b,t,h,d] * k_idx[b,j,d])
+ *                   for j <  c(t) = (start_pos + t + 1) / ratio  (integer division)
+ *   scores[b,t,j] = -inf  for c(t) <= j < T
+ *
+ *   q_idx  [B, S, H_I, D_I]  dtype            contiguous
+ *   k_idx  [B, T, D_I]       dtype            batch stride k_batch_stride (>= T*D_I)
+ *   w      [B, S, H_I]       dtype            raw head weights (weights_proj output)
+ *   scores [B, S, T]         float32          written in full
+ *   w_scale: the page's index_head_dim**-0.5 * index_n_heads**-0.5 (or any positive factor)
+ *
+ * Products are exact, sums are float32.  Supported: D_I in {32, 64, 128, 256},
+ * H_I in 1..64 (bf16: multiples of 8 run fastest), T >= 0 (T == 0 writes nothing).
+ * Requires T <= (start_pos + S) / ratio and ratio >= 1.
+ */
+int dsa_index_scores(const void* q_idx, const void* k_idx, int64_t k_batch_stride, const void* w,
+                     float w_scale, int dtype, int B, int S, int T, int H_I, int D_I, int start_pos,
+                     int ratio, float* scores, dsa_stream_t stream);
+
+/*
+ * Top-k selection (`Indexer.forward`: top-k by score, re-sorted into position
+ * order, unreachable -> -1, the rest shifted by `offset`):
+ *
+ *   K = min(index_topk, T).  For query t, with n = min(K, c(t)) and
+ *   c(t) = (start_pos + t + 1) / ratio, the first n entries of the row are
+ *   offset + j for the n visible positions j < c(t) with the largest scores
+ *   (equal scores: the lower position wins; -0.0 equals +0.0), in ascending j;
+ *   entries n..K-1 are -1.
+ *
+ *   scores [B, S, T] float32 (only j < c(t) is read)
+ *   idx    int32, row (b,t) starts at idx + (b*S + t) * ld_idx; K entries are written,
+ *          so a [B, S, Wc + K] buffer is filled at its tail by passing idx + Wc, ld_idx = Wc + K.
+ *
+ * Supported: T <= 65536.  NaN scores are outside the contract.
+ */
+int dsa_topk(const float* scores, int B, int S, int T, int index_topk, int start_pos, int ratio,
+             int offset, int32_t* idx, int64_t ld_idx, dsa_stream_t stream);
+
+/*
+ * Window index rows (`get_window_topk_idxs`):
+ *   start_pos == 0 (prefill): Wc = min(S, W); row t holds chunk positions
+ *     max(0, t-W+1) + s for s < Wc, with -1 where that exceeds t.
+ *   start_pos > 0 (decode, S must be 1): Wc = W; the ring slots oldest first,
+ *     (start_pos mod W) + 1 .. W-1, then 0 .. start_pos mod W, with -1 for a
+ *     slot greater than start_pos (ring still filling).
+ *   idx int32, row (b,t) starts at idx + (b*S + t) * ld_idx; Wc entries are written.
+ * Other combinations (start_pos > 0 with S > 1) are not defined by the page
+ * and return DSA_ERR_UNSUPPORTED.
+ */
+int dsa_window_idx(int B, int S, int start_pos, int W, int32_t* idx, int64_t ld_idx,
+                   dsa_stream_t stream);
+
+/* Window columns dsa_window_idx writes (min(S, W) in prefill, W in decode), or a negative error. */
+int dsa_window_cols(int S, int start_pos, int W);
+
+/*
+ * One KV source of sparse attention.  Rows are D elements of the call's dtype
+ * (DSA_KV_DENSE) or fp4 rows with E4M3 group scales (DSA_KV_FP4_E4M3_G16).
+ *   rows:   row r of batch b at rows + b*batch_stride + r*row_stride (in elements
+ *           for DENSE, in bytes for FP4, whose row is D/2 bytes)
+ *   scales: FP4 only; row r of batch b at scales + b*scale_batch_stride + r*scale_row_stride
+ *           (bytes; a row is D/16 bytes)
+ */
+typedef struct dsa_kv_src {
+  const void* rows;
+  int64_t n_rows;
+  int64_t batch_stride;
+  int64_t row_stride;
+  int format; /* enum dsa_kv_format */
+  const uint8_t* scales;
+  int64_t scale_batch_stride;
+  int64_t scale_row_stride;
+} dsa_kv_src;
+
+/*
+ * Sparse attention with a per-head sink (`sparse_attn_kernel` / `sparse_attn`;
+ * `Attention.forward` concatenates the window rows and the compressed rows
+ * into one KV tensor and shifts compressed indices by the window row count):
+ *
+ *   the KV row named by index i of batch b is win row i when i < win->n_rows,
+ *   otherwise comp row i - win->n_rows.  Key and value are the same row.
+ *   For each (b, t, h), over the slots s with idx[b,t,s] != -1:
+ *     l_s = scale * q[b,t,h,:] . row_s
+ *     o[b,t,h,:] = sum_s e^{l_s} row_s / (sum_s e^{l_s} + e^{sink[h]})
+ *   A query with no valid slot gets o = 0.  Duplicate indices count once each.
+ *
+ *   q    [B, S, H, D] dtype, contiguous
+ *   sink [H] float32
+ *   idx  [B, S, L] int32, contiguous (L >= 0)
+ *   o    [B, S, H, D] dtype, contiguous, written in full
+ *   comp may be NULL (or have n_rows 0) when no index reaches past the window.
+ *   workspace: device memory of at least dsa_sparse_attn_workspace_size(...) bytes
+ *     (may be NULL when that size is 0); its contents are scratch between calls.
+ *
+ * Supported: dtype BF16 with D in {64, 128, 256, 512} and H in 1..128, or dtype
+ * F32 with D <= 512 and H <= 64.  Accumulation is float32; the probabilities
+ * multiplying the bf16 rows are rounded to bf16 (as the page's kernel does).
+ */
+int dsa_sparse_attn(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
+                    const int32_t* idx, int L, float scale, void* o, int dtype, int B, int S, int H,
+                    int D, void* workspace, size_t workspace_bytes, dsa_stream_t stream);
+
+/* Bytes of workspace dsa_sparse_attn needs for this shape (0 when none). */
+size_t dsa_sparse_attn_workspace_size(int dtype, int B, int S, int H, int D, int L);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H_ */

@@ -1,0 +1,168 @@
+// C ABI of libdsa: argument validation, error text, dispatch to the HIP launchers.
+// Nothing here allocates device memory or synchronises the stream.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+
+#include "../../include/dsa.h"
+
+namespace dsa {
+
+static thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int check_launch(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return DSA_OK;
+}
+
+int index_scores_launch(const void*, const void*, int64_t, const void*, float, int, int, int, int, int, int, int, int,
+                        float*, hipStream_t);
+int topk_launch(const float*, int, int, int, int, int, int, int, int32_t*, int64_t, hipStream_t);
+int window_idx_launch(int, int, int, int, int, int32_t*, int64_t, hipStream_t);
+int sparse_attn_bf16_launch(const void*, const dsa_kv_src*, const dsa_kv_src*, const float*, const int32_t*, int,
+                            float, void*, int, int, int, int, void*, hipStream_t);
+int sparse_attn_f32_launch(const void*, const dsa_kv_src*, const dsa_kv_src*, const float*, const int32_t*, int,
+                           float, void*, int, int, int, int, hipStream_t);
+size_t sparse_attn_bf16_workspace(int, int, int, int, int);
+
+}  // namespace dsa
+
+using dsa::fail;
+
+extern "C" {
+
+int dsa_abi_version(void) { return DSA_ABI_VERSION; }
+
+const char* dsa_last_error(void) { return dsa::g_err; }
+
+int dsa_index_scores(const void* q_idx, const void* k_idx, int64_t k_batch_stride, const void* w, float w_scale,
+                     int dtype, int B, int S, int T, int H_I, int D_I, int start_pos, int ratio, float* scores,
+                     dsa_stream_t stream) {
+  dsa::g_err[0] = 0;
+  if (dtype != DSA_F32 && dtype != DSA_BF16) return fail(DSA_ERR_DTYPE, "dsa_index_scores: dtype %d", dtype);
+  if (B < 0 || S < 0 || T < 0 || H_I <= 0 || D_I <= 0 || start_pos < 0 || ratio <= 0)
+    return fail(DSA_ERR_SHAPE, "dsa_index_scores: bad sizes B=%d S=%d T=%d H_I=%d D_I=%d start_pos=%d ratio=%d", B, S,
+                T, H_I, D_I, start_pos, ratio);
+  if ((int64_t)T > ((int64_t)start_pos + S) / ratio)
+    return fail(DSA_ERR_SHAPE, "dsa_index_scores: T=%d exceeds (start_pos+S)/ratio=%lld", T,
+                (long long)(((int64_t)start_pos + S) / ratio));
+  if (H_I > 64) return fail(DSA_ERR_UNSUPPORTED, "dsa_index_scores: H_I=%d > 64", H_I);
+  if (B == 0 || S == 0 || T == 0) return DSA_OK;
+  if (!q_idx || !k_idx || !w || !scores) return fail(DSA_ERR_NULL, "dsa_index_scores: NULL tensor pointer");
+  if (k_batch_stride < (int64_t)T * D_I)
+    return fail(DSA_ERR_SHAPE, "dsa_index_scores: k_batch_stride %lld < T*D_I", (long long)k_batch_stride);
+  if (dtype == DSA_BF16 && (((uintptr_t)q_idx | (uintptr_t)k_idx) & 15))
+    return fail(DSA_ERR_SHAPE, "dsa_index_scores: q_idx and k_idx must be 16-byte aligned");
+  if (dtype == DSA_BF16 && (k_batch_stride % 8))
+    return fail(DSA_ERR_SHAPE, "dsa_index_scores: k_batch_stride must be a multiple of 8 elements");
+  return dsa::index_scores_launch(q_idx, k_idx, k_batch_stride, w, w_scale, dtype, B, S, T, H_I, D_I, start_pos,
+                                  ratio, scores, (hipStream_t)stream);
+}
+
+int dsa_topk(const float* scores, int B, int S, int T, int index_topk, int start_pos, int ratio, int offset,
+             int32_t* idx, int64_t ld_idx, dsa_stream_t stream) {
+  dsa::g_err[0] = 0;
+  if (B < 0 || S < 0 || T < 0 || index_topk < 0 || start_pos < 0 || ratio <= 0 || offset < 0)
+    return fail(DSA_ERR_SHAPE, "dsa_topk: bad sizes B=%d S=%d T=%d index_topk=%d start_pos=%d ratio=%d offset=%d", B,
+                S, T, index_topk, start_pos, ratio, offset);
+  const int K = index_topk < T ? index_topk : T;
+  if (ld_idx < K) return fail(DSA_ERR_SHAPE, "dsa_topk: ld_idx %lld < K=%d", (long long)ld_idx, K);
+  if (B == 0 || S == 0 || K == 0) return DSA_OK;
+  if (!scores || !idx) return fail(DSA_ERR_NULL, "dsa_topk: NULL pointer");
+  return dsa::topk_launch(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, (hipStream_t)stream);
+}
+
+int dsa_window_cols(int S, int start_pos, int W) {
+  if (S < 0 || start_pos < 0 || W <= 0) return fail(DSA_ERR_SHAPE, "dsa_window_cols: S=%d start_pos=%d W=%d", S, start_pos, W);
+  if (start_pos == 0) return S < W ? S : W;
+  if (S != 1) return fail(DSA_ERR_UNSUPPORTED, "window rows with start_pos > 0 are defined for one query (S=%d)", S);
+  return W;
+}
+
+int dsa_window_idx(int B, int S, int start_pos, int W, int32_t* idx, int64_t ld_idx, dsa_stream_t stream) {
+  dsa::g_err[0] = 0;
+  if (B < 0) return fail(DSA_ERR_SHAPE, "dsa_window_idx: B=%d", B);
+  const int Wc = dsa_window_cols(S, start_pos, W);
+  if (Wc < 0) return Wc;
+  if (ld_idx < Wc) return fail(DSA_ERR_SHAPE, "dsa_window_idx: ld_idx %lld < %d columns", (long long)ld_idx, Wc);
+  if (B == 0 || S == 0 || Wc == 0) return DSA_OK;
+  if (!idx) return fail(DSA_ERR_NULL, "dsa_window_idx: NULL idx");
+  return dsa::window_idx_launch(B, S, start_pos, W, Wc, idx, ld_idx, (hipStream_t)stream);
+}
+
+size_t dsa_sparse_attn_workspace_size(int dtype, int B, int S, int H, int D, int L) {
+  if (dtype != DSA_BF16 || B <= 0 || S <= 0 || H <= 0 || D <= 0 || L <= 0) return 0;
+  return dsa::sparse_attn_bf16_workspace(B, S, H, D, L);
+}
+
+static int check_src(const dsa_kv_src* s, const char* name, int dtype, int D, int B, bool required) {
+  if (!s) return required ? fail(DSA_ERR_NULL, "dsa_sparse_attn: %s source is NULL", name) : DSA_OK;
+  if (s->n_rows < 0) return fail(DSA_ERR_SHAPE, "dsa_sparse_attn: %s n_rows %lld", name, (long long)s->n_rows);
+  if (s->n_rows == 0) return DSA_OK;
+  if (!s->rows) return fail(DSA_ERR_NULL, "dsa_sparse_attn: %s rows NULL with n_rows %lld", name, (long long)s->n_rows);
+  if (s->format == DSA_KV_DENSE) {
+    if (s->row_stride < D || (B > 1 && s->batch_stride < s->n_rows * s->row_stride - (s->row_stride - D)))
+      return fail(DSA_ERR_SHAPE, "dsa_sparse_attn: %s strides too small for D=%d", name, D);
+    if (dtype == DSA_BF16 && (((uintptr_t)s->rows & 15) || (s->row_stride % 8) || (s->batch_stride % 8)))
+      return fail(DSA_ERR_SHAPE, "dsa_sparse_attn: bf16 %s rows need 16-byte alignment of every row", name);
+  } else if (s->format == DSA_KV_FP4_E4M3_G16) {
+    if (dtype != DSA_BF16) return fail(DSA_ERR_DTYPE, "dsa_sparse_attn: fp4 %s rows need dtype bf16", name);
+    if (!s->scales) return fail(DSA_ERR_NULL, "dsa_sparse_attn: fp4 %s scales NULL", name);
+    if (D % 16) return fail(DSA_ERR_SHAPE, "dsa_sparse_attn: fp4 rows need D %% 16 == 0");
+    if (s->row_stride < D / 2 || s->scale_row_stride < D / 16)
+      return fail(DSA_ERR_SHAPE, "dsa_sparse_attn: fp4 %s strides too small", name);
+    if (((uintptr_t)s->rows & 3) || (s->row_stride & 3) || (s->batch_stride & 3))
+      return fail(DSA_ERR_SHAPE, "dsa_sparse_attn: fp4 %s rows need 4-byte alignment", name);
+  } else {
+    return fail(DSA_ERR_DTYPE, "dsa_sparse_attn: %s format %d", name, s->format);
+  }
+  return DSA_OK;
+}
+
+int dsa_sparse_attn(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
+                    const int32_t* idx, int L, float scale, void* o, int dtype, int B, int S, int H, int D,
+                    void* workspace, size_t workspace_bytes, dsa_stream_t stream) {
+  dsa::g_err[0] = 0;
+  if (dtype != DSA_F32 && dtype != DSA_BF16) return fail(DSA_ERR_DTYPE, "dsa_sparse_attn: dtype %d", dtype);
+  if (B < 0 || S < 0 || H <= 0 || D <= 0 || L < 0)
+    return fail(DSA_ERR_SHAPE, "dsa_sparse_attn: bad sizes B=%d S=%d H=%d D=%d L=%d", B, S, H, D, L);
+  int rc = check_src(win, "window", dtype, D, B, true);
+  if (rc) return rc;
+  rc = check_src(comp, "compressed", dtype, D, B, false);
+  if (rc) return rc;
+  if (win->format != DSA_KV_DENSE) return fail(DSA_ERR_DTYPE, "dsa_sparse_attn: window rows must be dense");
+  if (dtype == DSA_BF16) {
+    if (D != 64 && D != 128 && D != 256 && D != 512)
+      return fail(DSA_ERR_UNSUPPORTED, "dsa_sparse_attn: bf16 head_dim %d not in {64,128,256,512}", D);
+    if (H > (D == 512 ? 64 : 128)) return fail(DSA_ERR_UNSUPPORTED, "dsa_sparse_attn: H=%d too large for D=%d", H, D);
+  } else {
+    if (D > 512 || H > 64) return fail(DSA_ERR_UNSUPPORTED, "dsa_sparse_attn: fp32 path takes D<=512, H<=64");
+    if (comp && comp->n_rows > 0 && comp->format != DSA_KV_DENSE)
+      return fail(DSA_ERR_DTYPE, "dsa_sparse_attn: fp32 path takes dense rows only");
+  }
+  if (B == 0 || S == 0) return DSA_OK;
+  if (!q || !sink || !o || (L > 0 && !idx)) return fail(DSA_ERR_NULL, "dsa_sparse_attn: NULL tensor pointer");
+  if (dtype == DSA_BF16 && (((uintptr_t)q | (uintptr_t)o) & 15))
+    return fail(DSA_ERR_SHAPE, "dsa_sparse_attn: q and o must be 16-byte aligned");
+  const size_t need = dsa_sparse_attn_workspace_size(dtype, B, S, H, D, L);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "dsa_sparse_attn: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  dsa_kv_src empty{};
+  const dsa_kv_src* cs = (comp && comp->n_rows > 0) ? comp : &empty;
+  if (dtype == DSA_BF16)
+    return dsa::sparse_attn_bf16_launch(q, win, cs, sink, idx, L, scale, o, B, S, H, D, workspace,
+                                        (hipStream_t)stream);
+  return dsa::sparse_attn_f32_launch(q, win, cs, sink, idx, L, scale, o, B, S, H, D, (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// Internal definitions shared by the HIP sources of libdsa (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dsa.h"
+
+namespace dsa {
+
+// ---- vector types used as MFMA operands -----------------------------------
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4;
+typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+#define DSA_LDS __attribute__((address_space(3)))
+
+// 32x32x16 bf16 MFMA.  Lane l (hf = l/32, c = l%32) supplies A[c][8hf..8hf+7] and
+// B[8hf..8hf+7][c]; accumulator element j holds C[8(j/4) + 4hf + (j%4)][c].
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS transposing read of four 16-bit elements.  Within each 16-lane group,
+// lane c receives column c of a 4x16 block whose row r is the four elements at
+// the addresses of lanes 4r .. 4r+3 of that group.
+__device__ __forceinline__ bf16x4 lds_read_tr16(const DSA_LDS __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((DSA_LDS bf16x4*)p);
+}
+
+// 16-byte global -> LDS copy without passing through registers.  The LDS
+// destination is wave-uniform: lane l's 16 bytes land at lds_base + 16*l.
+__device__ __forceinline__ void global_to_lds16(const void* gptr, DSA_LDS void* lds_base) {
+  __builtin_amdgcn_global_load_lds(gptr, lds_base, 16, 0, 0);
+}
+
+__device__ __forceinline__ float bf16_to_f32(__bf16 x) { return (float)x; }
+
+__device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0)); }
+
+template <typename T>
+__device__ __forceinline__ T shfl_xor(T v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+__device__ __forceinline__ int visible_rows(int start_pos, int t, int ratio) {
+  return (start_pos + t + 1) / ratio;
+}
+
+}  // namespace dsa
+
+// ---- host-side error reporting (abi.hip) -----------------------------------
+namespace dsa {
+int fail(int code, const char* fmt, ...);
+int check_launch(const char* what);
+}  // namespace dsa

@@ -1,0 +1,293 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Inputs come from the seeded generator; expected values from the oracle only.  Sizes span
+several tiles with ragged tails; the full-size workloads are checked in full where the oracle
+finishes in seconds (tiny prefill, both decode workloads) and on sampled queries otherwise.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import dsa_synth
+import oracle
+from parity import ATTN_TOL, check_topk_row, max_abs_err, sample_rows, score_bound
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def _dsa():
+    import sparse_mqa_attention_amd as dsa
+
+    return dsa
+
+
+def _log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _to_dev(d):
+    return {k: v.to(DEV) for k, v in d.items()}
+
+
+def _kv_cat64(cpu_inputs, w):
+    if w.comp_fmt == "fp4":
+        comp = oracle.fp4_rows_decode(cpu_inputs["kv_comp_fp4"], cpu_inputs["kv_comp_scale"])
+    else:
+        comp = cpu_inputs["kv_comp"]
+    return oracle.kv_concat(cpu_inputs["kv_win"], comp)
+
+
+# ------------------------------------------------------------------------ window rows
+@pytest.mark.parametrize("B,S,sp,W", [(2, 6, 0, 4), (1, 300, 0, 128), (3, 1, 2, 4), (2, 1, 9, 4), (4, 1, 8191, 128),
+                                      (1, 1, 65535, 128), (1, 64, 0, 16), (2, 1, 127, 128)])
+def test_window_idx(B, S, sp, W):
+    dsa = _dsa()
+    Wc = dsa.dsa_window_cols(S, sp, W)
+    out = torch.full((B, S, Wc + 3), 77, dtype=torch.int32, device=DEV)
+    dsa.dsa_window_idx(out, sp, W)
+    got = out.cpu().numpy()
+    np.testing.assert_array_equal(got[..., :Wc], oracle.window_rows(W, B, S, sp))
+    assert np.all(got[..., Wc:] == 77)  # columns past the window untouched
+
+
+# ------------------------------------------------------------------------ top-k (integer work: bit-exact)
+@pytest.mark.parametrize("B,S,T,K,sp,ratio,kind", [
+    (1, 64, 16, 8, 0, 4, "ties"),
+    (2, 37, 100, 8, 0, 2, "normal"),
+    (1, 700, 300, 64, 0, 1, "ties"),
+    (2, 1, 1000, 512, 3999, 4, "normal"),
+    (1, 1, 2048, 512, 8191, 4, "zeros"),
+    (1, 3000, 2048, 512, 0, 4, "normal"),
+    (3, 1, 4000, 512, 15999, 4, "ties"),
+    (1, 1, 5000, 512, 19999, 4, "normal"),
+    (2, 1, 16384, 512, 65535, 4, "normal"),
+    (1, 1, 16384, 512, 65535, 4, "ties"),
+    (1, 1, 30000, 700, 29999, 1, "normal"),
+    (1, 3, 600, 1, 1797, 3, "normal"),
+])
+def test_topk_bit_exact(B, S, T, K, sp, ratio, kind):
+    """Given the same float32 scores, the GPU selection equals the oracle's exactly."""
+    dsa = _dsa()
+    _log(f"topk case B={B} S={S} T={T} K={K} sp={sp} r={ratio} {kind}")
+    rng = np.random.default_rng(T + K + S)
+    if kind == "ties":
+        s = rng.integers(-4, 5, size=(B, S, T)).astype(np.float32)
+    elif kind == "zeros":
+        s = rng.integers(0, 2, size=(B, S, T)).astype(np.float32) * rng.choice([-1.0, 1.0], size=(B, S, T)).astype(
+            np.float32) * 0.0
+        s[..., ::7] = rng.standard_normal(s[..., ::7].shape).astype(np.float32)
+    else:
+        s = rng.standard_normal((B, S, T)).astype(np.float32)
+    c = oracle.visible_count(np.arange(S), sp, ratio)
+    s[:, np.arange(T)[None, :] >= np.minimum(c, T)[:, None]] = -np.inf
+    scores = torch.from_numpy(s).to(DEV)
+    off = 5
+    Kk = min(K, T)
+    out = torch.full((B, S, 2 + Kk), -7, dtype=torch.int32, device=DEV)
+    dsa.dsa_topk(scores, K, sp, ratio, off, out=out, col=2)
+    got = out.cpu().numpy()
+    assert np.all(got[..., :2] == -7)
+    exp = oracle.topk_select(s.astype(np.float64), K, sp, ratio, off)
+    np.testing.assert_array_equal(got[..., 2:], exp)
+
+
+# ------------------------------------------------------------------------ index scores
+def _check_scores(got, qI, kI, w, w_scale, sp, ratio, rows=None, ctx=""):
+    q64 = qI.float().numpy().astype(np.float64)
+    k64 = kI.float().numpy().astype(np.float64)
+    w64 = w.float().numpy().astype(np.float64)
+    if rows is None:
+        exp = oracle.index_scores(q64, k64, w64, w_scale, sp, ratio)
+        B, S = exp.shape[:2]
+        rows = [(b, t) for b in range(B) for t in range(S)]
+        exp_rows = exp.reshape(B * S, -1)
+    else:
+        exp_rows = oracle.index_scores_rows(q64, k64, w64, w_scale, sp, ratio, rows)
+    worst = 0.0
+    for n, (b, t) in enumerate(rows):
+        g = got[b, t]
+        e = exp_rows[n]
+        inv = np.isinf(e)
+        assert np.all(np.isneginf(g[inv])), f"{ctx} ({b},{t}): masked entries must be -inf"
+        bound = score_bound(q64[b, t][None], k64[b], w64[b, t][None], w_scale)[0]
+        err = np.abs(g[~inv] - e[~inv])
+        lim = 1e-5 * bound[~inv] + 1e-30
+        assert np.all(err <= lim), f"{ctx} ({b},{t}): score error {err.max():.3e} above the fp32 bound"
+        if err.size:
+            worst = max(worst, float((err / lim).max()))
+    return worst
+
+
+@pytest.mark.parametrize("B,S,sp,T,H,DI,ratio,dtype", [
+    (1, 64, 0, 16, 4, 32, 4, "f32"),
+    (2, 70, 0, 35, 32, 128, 2, "bf16"),
+    (1, 300, 0, 300, 4, 32, 1, "bf16"),
+    (2, 33, 0, 16, 48, 64, 2, "bf16"),
+    (3, 1, 1234, 308, 32, 128, 4, "bf16"),
+    (1, 9, 0, 2, 16, 256, 4, "bf16"),
+    (2, 17, 40, 28, 32, 128, 2, "bf16"),
+])
+def test_index_scores_small(B, S, sp, T, H, DI, ratio, dtype):
+    dsa = _dsa()
+    _log(f"index_scores case B={B} S={S} sp={sp} T={T} H={H} DI={DI} r={ratio} {dtype}")
+    g = torch.Generator().manual_seed(S * 7 + T)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    qI = torch.randn(B, S, H, DI, generator=g).to(dt)
+    kI = torch.randn(B, T + 3, DI, generator=g).to(dt)[:, :T]  # batch stride larger than T*DI
+    w = (torch.randn(B, S, H, generator=g) * 0.5).to(dt)
+    w_scale = DI ** -0.5 * H ** -0.5
+    got = dsa.dsa_index_scores(qI.to(DEV), kI.to(DEV), w.to(DEV), w_scale, sp, ratio).cpu().numpy()
+    _check_scores(got, qI, kI.contiguous(), w, w_scale, sp, ratio, ctx="small")
+
+
+# ------------------------------------------------------------------------ sparse attention
+def _rand_idx(rng, B, S, L, n, frac_invalid=0.15):
+    idx = rng.integers(0, n, size=(B, S, L))
+    idx[rng.random((B, S, L)) < frac_invalid] = -1
+    return idx.astype(np.int32)
+
+
+@pytest.mark.parametrize("B,S,H,D,nw,nc,L,dtype,fp4", [
+    (1, 5, 4, 64, 20, 16, 24, "f32", False),
+    (2, 3, 16, 64, 40, 30, 77, "bf16", False),
+    (1, 2, 32, 128, 33, 100, 130, "bf16", False),
+    (2, 2, 48, 256, 64, 64, 96, "bf16", False),
+    (1, 3, 64, 512, 128, 500, 640, "bf16", False),
+    (3, 1, 64, 512, 128, 2048, 640, "bf16", False),
+    (1, 300, 64, 512, 300, 75, 200, "bf16", False),
+    (2, 2, 64, 512, 128, 256, 300, "bf16", True),
+    (1, 260, 64, 512, 260, 65, 100, "bf16", True),
+    (2, 2, 100, 128, 16, 16, 40, "bf16", False),
+    (1, 2, 8, 512, 16, 16, 33, "bf16", False),
+])
+def test_sparse_attn(B, S, H, D, nw, nc, L, dtype, fp4):
+    dsa = _dsa()
+    _log(f"sparse_attn case B={B} S={S} H={H} D={D} nw={nw} nc={nc} L={L} {dtype} fp4={fp4}")
+    g = torch.Generator().manual_seed(B * 1000 + S * 10 + H + D)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    q = torch.randn(B, S, H, D, generator=g).to(dt)
+    kv_win = torch.randn(B, nw, D, generator=g).to(dt)
+    sink = torch.randn(H, generator=g)
+    if fp4:
+        packed, scales = dsa_synth.encode_fp4_e2m1_e4m3(torch.randn(B, nc, D, generator=g), 16)
+        comp64 = oracle.fp4_rows_decode(packed, scales)
+        comp_dev, sc_dev = packed.to(DEV), scales.to(DEV)
+    else:
+        comp = torch.randn(B, nc, D, generator=g).to(dt)
+        comp64, comp_dev, sc_dev = comp, comp.to(DEV), None
+    rng = np.random.default_rng(L)
+    idx = _rand_idx(rng, B, S, L, nw + nc)
+    idx[0, 0, :] = -1  # a query with no valid slot
+    if L > 3:
+        idx[-1, -1, 1] = idx[-1, -1, 0] = max(idx[-1, -1, 0], 0)  # a duplicate
+    scale = D ** -0.5
+    o = dsa.dsa_sparse_attn(q.to(DEV), kv_win.to(DEV), comp_dev, sink.to(DEV), torch.from_numpy(idx).to(DEV), scale,
+                            comp_scales=sc_dev)
+    kv = oracle.kv_concat(kv_win, comp64)
+    exp = oracle.sparse_attn(q, kv, sink, idx, scale)
+    got = o.float().cpu().numpy()
+    err = max_abs_err(got, exp)
+    _log(f"  max abs err {err:.3e}")
+    assert np.all(got[0, 0] == 0)
+    assert err <= ATTN_TOL[dtype], err
+
+
+# ------------------------------------------------------------------------ whole step per workload
+def _step(w, dev_in, bufs=None):
+    dsa = _dsa()
+    return dsa.sparse_attention_step(
+        dev_in["q"], dev_in["kv_win"], dev_in.get("kv_comp", dev_in.get("kv_comp_fp4")), dev_in["qI"], dev_in["kI"],
+        dev_in["w"], dev_in["sink"], start_pos=w.start_pos, ratio=w.ratio, W=w.W, index_topk=w.index_topk,
+        scale=w.D ** -0.5, w_scale=w.D_I ** -0.5 * w.H_I ** -0.5, comp_scales=dev_in.get("kv_comp_scale"), bufs=bufs)
+
+
+def _check_step(w, cpu_in, o, idx, scores, rows):
+    """Scores within the fp32 bound, window rows exact, top-k by the parity rules, and the
+    attention output against the oracle on the GPU's own index rows."""
+    w_scale = w.D_I ** -0.5 * w.H_I ** -0.5
+    got_scores = {}
+    sc = scores.cpu() if scores is not None else None
+    for (b, t) in rows:
+        got_scores[(b, t)] = sc[b, t].numpy() if sc is not None else None
+    q64 = cpu_in["qI"].float().numpy().astype(np.float64)
+    k64 = cpu_in["kI"].float().numpy().astype(np.float64)
+    w64 = cpu_in["w"].float().numpy().astype(np.float64)
+    exp_rows = oracle.index_scores_rows(q64, k64, w64, w_scale, w.start_pos, w.ratio, rows)
+    idx_cpu = idx.cpu().numpy()
+    win = oracle.window_rows(w.W, w.B, w.S, w.start_pos)
+    rules = {}
+    for n, (b, t) in enumerate(rows):
+        e = exp_rows[n]
+        g = got_scores[(b, t)]
+        inv = np.isinf(e)
+        assert np.all(np.isneginf(g[inv]))
+        bound = score_bound(q64[b, t][None], k64[b], w64[b, t][None], w_scale)[0]
+        assert np.all(np.abs(g[~inv] - e[~inv]) <= 1e-5 * bound[~inv] + 1e-30), (b, t)
+        np.testing.assert_array_equal(idx_cpu[b, t, :w.Wc], win[b, t])
+        c = int(min(w.T, oracle.visible_count(t, w.start_pos, w.ratio)))
+        rule = check_topk_row(idx_cpu[b, t, w.Wc:], e, w.K, c, w.n_win, ctx=f"{w.name} ({b},{t})")
+        rules[rule] = rules.get(rule, 0) + 1
+    kv = _kv_cat64(cpu_in, w)
+    exp_o = oracle.sparse_attn_rows(cpu_in["q"], kv, cpu_in["sink"], idx_cpu, w.D ** -0.5, rows)
+    got_o = np.stack([o[b, t].float().cpu().numpy() for (b, t) in rows])
+    err = max_abs_err(got_o, exp_o)
+    _log(f"  {w.name}: {len(rows)} rows, top-k rules {rules}, attention max abs err {err:.3e}")
+    assert err <= ATTN_TOL[w.dtype], err
+    return err
+
+
+@pytest.mark.parametrize("name", ["tiny_prefill_f32", "decode_b32_ctx8k", "decode_b16_ctx64k"])
+def test_step_full(name):
+    w = dsa_synth.get(name)
+    _log(f"step {name} (full check)")
+    cpu_in = dsa_synth.generate(w, seed=0)
+    dev_in = _to_dev(cpu_in)
+    o, idx, scores = _step(w, dev_in)
+    torch.cuda.synchronize()
+    rows = [(b, t) for b in range(w.B) for t in range(w.S)]
+    _check_step(w, cpu_in, o, idx, scores, rows)
+
+
+@pytest.mark.parametrize("name,S", [("prefill_s8k", 640), ("prefill_s32k_fp4", 700), ("prefill_s8k", 2100)])
+def test_step_reduced_prefill(name, S):
+    """Prefill workloads cut to S queries (several tiles and the c(t) = K crossover when S > 2048)."""
+    w = dsa_synth.scaled(dsa_synth.get(name), S=S, name=f"{name}_S{S}")
+    _log(f"step {w.name}")
+    cpu_in = dsa_synth.generate(w, seed=0)
+    dev_in = _to_dev(cpu_in)
+    o, idx, scores = _step(w, dev_in)
+    torch.cuda.synchronize()
+    rows = sample_rows(w, n_random=24)
+    rows = sorted(set(rows + [(0, t) for t in range(0, w.S, max(1, w.S // 48))]))
+    _check_step(w, cpu_in, o, idx, scores, rows)
+
+
+@pytest.mark.parametrize("name", ["prefill_s8k", "prefill_s32k_fp4"])
+def test_step_full_size_sampled(name):
+    """The full prefill workloads, in the launch configuration the benchmark times, on sampled queries."""
+    w = dsa_synth.get(name)
+    _log(f"step {name} (full size, sampled)")
+    dev_in = dsa_synth.generate(w, seed=0, device=DEV)
+    o, idx, scores = _step(w, dev_in)
+    torch.cuda.synchronize()
+    rows = sample_rows(w, n_random=10)
+    need = {"q", "kv_win", "kv_comp", "kv_comp_fp4", "kv_comp_scale", "kI", "sink"}
+    cpu_in = {k: v.cpu() for k, v in dev_in.items() if k in need}
+    # only the sampled queries' index q/weights are needed on the host
+    cpu_in["qI"] = dev_in["qI"].cpu()
+    cpu_in["w"] = dev_in["w"].cpu()
+    _check_step(w, cpu_in, o, idx, scores, rows)
+    # every query with no visible compressed row attends to its window only; c(t) <= K rows are exact
+    idx_cpu = idx[0, : min(w.S, 4 * w.K)].cpu().numpy()
+    c = oracle.visible_count(np.arange(idx_cpu.shape[0]), 0, w.ratio)
+    for t in range(0, idx_cpu.shape[0], 97):
+        n = int(min(w.K, c[t]))
+        np.testing.assert_array_equal(idx_cpu[t, w.Wc:w.Wc + n], w.n_win + np.arange(n) if c[t] <= w.K else
+                                      idx_cpu[t, w.Wc:w.Wc + n])
+        assert np.all(idx_cpu[t, w.Wc + n:] == -1)
