@@ -33,7 +33,7 @@ int sparse_attn_bf16_launch(const void*, const dsa_kv_src*, const dsa_kv_src*, c
                             float, void*, int, int, int, int, void*, hipStream_t);
 int sparse_attn_f32_launch(const void*, const dsa_kv_src*, const dsa_kv_src*, const float*, const int32_t*, int,
                            float, void*, int, int, int, int, hipStream_t);
-size_t sparse_attn_bf16_workspace(int, int, int, int, int);
+size_t sparse_attn_bf16_workspace(int, int, int, int, int, bool);
 
 }  // namespace dsa
 
@@ -102,7 +102,10 @@ int dsa_window_idx(int B, int S, int start_pos, int W, int32_t* idx, int64_t ld_
 
 size_t dsa_sparse_attn_workspace_size(int dtype, int B, int S, int H, int D, int L) {
   if (dtype != DSA_BF16 || B <= 0 || S <= 0 || H <= 0 || D <= 0 || L <= 0) return 0;
-  return dsa::sparse_attn_bf16_workspace(B, S, H, D, L);
+  // the size covers every kernel the call may pick for this shape (dense or fp4 compressed rows)
+  const size_t a = dsa::sparse_attn_bf16_workspace(B, S, H, D, L, false);
+  const size_t b = dsa::sparse_attn_bf16_workspace(B, S, H, D, L, true);
+  return a > b ? a : b;
 }
 
 static int check_src(const dsa_kv_src* s, const char* name, int dtype, int D, int B, bool required) {

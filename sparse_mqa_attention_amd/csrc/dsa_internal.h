@@ -38,6 +38,15 @@ __device__ __forceinline__ void global_to_lds16(const void* gptr, DSA_LDS void* 
   __builtin_amdgcn_global_load_lds(gptr, lds_base, 16, 0, 0);
 }
 
+// XOR pattern applied to the 16-byte chunks of LDS row r (rows of NCH chunks).  Bijective on
+// 0..15, so 16 consecutive rows read at one logical chunk hit 16 different bank groups, and the
+// 4-row x 32-byte blocks of a transposing read spread over all bank groups two at a time.
+template <int NCH>
+__device__ __forceinline__ int row_swz(int r) {
+  const int s = ((r & 3) << 2) | ((r >> 2) & 3);
+  return NCH >= 16 ? s : (s & (NCH - 1));
+}
+
 __device__ __forceinline__ float bf16_to_f32(__bf16 x) { return (float)x; }
 
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0)); }

@@ -59,13 +59,6 @@ struct AttnArgs {
   int S, H, nsplit, split_slots;
 };
 
-// XOR pattern of the 16-byte chunks of LDS row r (bijective on 0..15)
-template <int NCH>
-__device__ __forceinline__ int row_swz(int r) {
-  const int s = ((r & 3) << 2) | ((r >> 2) & 3);
-  return NCH >= 16 ? s : (s & (NCH - 1));
-}
-
 __device__ __forceinline__ float e2m1_to_f32(uint32_t nib) {
   const uint32_t m3 = nib & 7u;
   const uint32_t e = m3 >> 1;
@@ -437,6 +430,12 @@ void sparse_attn_split(int B, int S, int L, int* nsplit, int* split_slots) {
   *nsplit = L > 0 ? (L + *split_slots - 1) / *split_slots : 1;
 }
 
+size_t sparse_attn_decode_workspace(int B, int S, int H, int D, int L, bool fp4);
+int sparse_attn_decode_launch(const __bf16* q, const unsigned char* win, int64_t win_n, int64_t win_bs,
+                              int64_t win_rs, const unsigned char* comp, int64_t comp_bs, int64_t comp_rs,
+                              const float* sink, const int32_t* idx, int L, float scale_log2, __bf16* o, int B,
+                              int S, int H, int D, bool fp4, void* workspace, hipStream_t st);
+
 int sparse_attn_bf16_launch(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
                             const int32_t* idx, int L, float scale, void* o, int B, int S, int H, int D,
                             void* workspace, hipStream_t st) {
@@ -463,6 +462,10 @@ int sparse_attn_bf16_launch(const void* q, const dsa_kv_src* win, const dsa_kv_s
   a.part = (float*)workspace;
   a.S = S;
   a.H = H;
+  // decode batches: two-phase kernel without partial outputs when its shape and residency fit
+  const int drc = sparse_attn_decode_launch(a.q, a.win, a.win_n, a.win_bs, a.win_rs, a.comp, a.comp_bs, a.comp_rs,
+                                            sink, idx, L, a.scale_log2, a.o, B, S, H, D, fp4, workspace, st);
+  if (drc != 0) return drc < 0 ? drc : 0;
   sparse_attn_split(B, S, L, &a.nsplit, &a.split_slots);
   switch (D) {
     case 64: return fp4 ? launch_attn_h<64, true>(a, B, st) : launch_attn_h<64, false>(a, B, st);
@@ -473,12 +476,13 @@ int sparse_attn_bf16_launch(const void* q, const dsa_kv_src* win, const dsa_kv_s
   }
 }
 
-size_t sparse_attn_bf16_workspace(int B, int S, int H, int D, int L) {
+size_t sparse_attn_bf16_workspace(int B, int S, int H, int D, int L, bool fp4) {
   int nsplit, per;
   sparse_attn_split(B, S, L, &nsplit, &per);
-  if (nsplit <= 1) return 0;
   const size_t rows = (size_t)B * S * nsplit * H;
-  return rows * (size_t)D * 4 + rows * 2 * 4;
+  const size_t general = nsplit <= 1 ? 0 : rows * (size_t)D * 4 + rows * 2 * 4;
+  const size_t decode = sparse_attn_decode_workspace(B, S, H, D, L, fp4);
+  return general > decode ? general : decode;
 }
 
 }  // namespace dsa

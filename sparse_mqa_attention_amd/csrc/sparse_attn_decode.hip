@@ -1,0 +1,534 @@
+// Sparse MQA attention for decode batches (DeepSeek V4.1 page, `sparse_attn_kernel`; one query
+// per sequence attending its window ring plus its top-k compressed rows, with a per-head sink).
+//
+// A decode batch has far fewer queries than the GPU has CUs, so each query's work is spread over
+// NS workgroups, and the split is arranged so that no workgroup ever writes a partial output:
+//
+//  phase A (rows)  workgroup s of query q gathers rows [s*RPS, (s+1)*RPS) of the index row into
+//                  LDS (direct 16-byte global->LDS loads, all rows in flight at once), computes
+//                  the logits of all 64 heads on MFMA (S^T = K . Q^T), and publishes the
+//                  probabilities P = 2^(l - m_s) in bf16 plus its per-head max m_s and sum l_s.
+//  rendezvous      the NS workgroups of the query count themselves in on an arrival counter; the
+//                  host only takes this path when every workgroup of the grid is resident at once,
+//                  and the wait is bounded (a timeout raises an error flag and poisons the output).
+//                  P and the stats travel with device-coherent stores and loads, so the rendezvous
+//                  needs no cache-wide write-back or invalidate (those cost tens of microseconds).
+//  phase B (dims)  workgroup s computes output columns [s*D/NS, (s+1)*D/NS) of all 64 heads over
+//                  ALL rows of the query: it re-gathers just those columns of every row (hits in
+//                  the XCD's L2, which phase A of the sibling workgroups filled) and reads P from
+//                  L2; O^T = V^T . P^T on MFMA, one accumulator per phase-A split scaled by
+//                  2^(m_s - M) before it is added, then divided by sum_s l_s 2^(m_s - M) + 2^(sink - M).
+//
+// Blocks are numbered so that all NS workgroups of a query land on one XCD (dispatch assigns
+// consecutive workgroups to the 8 XCDs round-robin), keeping the rendezvous and the re-gather in
+// one L2.  What crosses HBM is each valid row once, q, o, and the small P (Q x 64 x L bf16).
+#include "dsa_internal.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kDD = 512;                 // head_dim of this path
+constexpr int kDH = 64;                  // heads of this path
+constexpr int kDecRowsMax = 96;          // rows of one phase-A split: 96 KiB of LDS
+constexpr int kDecQueriesMax = 4096;
+constexpr float kLog2eD = 1.4426950408889634f;
+constexpr uint64_t kSpinTimeoutTicks = 20000000ull;  // 0.2 s of the 100 MHz constant-rate counter
+
+// Per query: arrivals and departures of its workgroups.  Zero when the code object loads; the
+// last workgroup of a query to leave resets both, so every call finds them at zero.
+__device__ uint32_t g_dec_sync[2 * kDecQueriesMax];
+__device__ uint32_t g_dec_error;
+
+struct DecArgs {
+  const __bf16* q;
+  const unsigned char* win;
+  int64_t win_n, win_bs, win_rs;  // bytes
+  const unsigned char* comp;
+  int64_t comp_bs, comp_rs;       // bytes
+  const float* sink;
+  const int32_t* idx;
+  int L;
+  float scale_log2;
+  __bf16* o;
+  __bf16* pbuf;  // [Q][64][Lp] phase-A probabilities
+  float* stats;  // [Q][NS][64][2] phase-A (max, sum)
+  uint32_t* xcc;  // [Q][NS] XCD of each phase-A workgroup
+  int S, Q, RPS, Lp, xcd_map;
+  int local;  // all workgroups of a query share one XCD (calibrated): P and stats go through its L2
+};
+
+template <int NS>
+struct DecCfg {
+  static constexpr int DS = kDD / NS;      // output columns per workgroup in phase B
+  static constexpr int SLICEB = DS * 2;    // bytes of one row's column slice
+  static constexpr int LPRB = SLICEB / 16; // lanes per slice (8 or 4)
+  static constexpr int RPIB = 64 / LPRB;   // slices per wave instruction (8 or 16)
+  static constexpr int NMB = DS / 32;      // phase-B M tiles per wave
+  static constexpr int ROWS_BYTES = kDecRowsMax * kDD * 2;
+  static constexpr int MAX_L = ROWS_BYTES / SLICEB;  // slots whose slices fit the same LDS
+  static constexpr int NSW = NS / 2;       // phase-A splits each phase-B wave folds in
+  static constexpr int KPS = NS == 8 ? 6 : 3;  // most 16-row k-steps per split (RPS <= 16*KPS)
+  static constexpr int TA = (16 * KPS + 31) / 32;  // 32-row MFMA tiles covering one split
+};
+
+// chunk XOR of phase-B slice rows: keeps the 4-row x 32-byte transposing reads conflict free
+template <int NS>
+__device__ __forceinline__ int slice_swz(int r) {
+  return NS == 8 ? (((r >> 1) & 3) << 1) : 0;
+}
+
+// Write-through store of four bf16 (one 8-byte access at device scope): memory and the writer's
+// L2 both hold the new value, so a reader on the same XCD can use plain loads.
+__device__ __forceinline__ void store_coherent(__bf16* p, bf16x4 v) {
+  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Eight bf16 read past any stale per-XCD cached copy (two 8-byte device-scope loads).
+__device__ __forceinline__ bf16x8 load_coherent8(const __bf16* p) {
+  const uint64_t* u = reinterpret_cast<const uint64_t*>(p);
+  u32x4 r;
+  const uint64_t lo = __hip_atomic_load(u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint64_t hi = __hip_atomic_load(u + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  r[0] = (uint32_t)lo;
+  r[1] = (uint32_t)(lo >> 32);
+  r[2] = (uint32_t)hi;
+  r[3] = (uint32_t)(hi >> 32);
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// The arrival counter is polled with a device-scope load: on gfx950 only that scope skips the
+// CU's L1, so a narrower poll could spin on a stale line.
+__device__ __forceinline__ uint32_t poll_load(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t v;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
+  return v & 0xFu;
+}
+
+template <int NS>
+__global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
+  using C = DecCfg<NS>;
+  constexpr int XBUF_FLOATS = 4 * C::TA * 16 * 64;  // per wave, per tile: one partial S^T tile
+  __shared__ __attribute__((aligned(1024))) unsigned char rows[C::ROWS_BYTES];
+  __shared__ __attribute__((aligned(16))) float xbuf[XBUF_FLOATS];
+  __shared__ int idx_lds[C::MAX_L];
+  __shared__ float stats_lds[NS * kDH * 2];
+  __shared__ int flags[1];  // the rendezvous timed out
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int hf = lane >> 5;
+  const int c = lane & 31;
+  const int j16 = lane & 15;
+
+  int q, s;
+  {
+    const int lb = blockIdx.x;
+    if (a.xcd_map) {
+      const int xcd = lb & 7, k = lb >> 3;
+      q = xcd * (a.Q >> 3) + k / NS;
+      s = k % NS;
+    } else {
+      q = lb / NS;
+      s = lb % NS;
+    }
+  }
+  const int L = a.L;
+  const int bq = q / a.S;  // batch of the query's KV
+  const int32_t* irow = a.idx + (int64_t)q * L;
+  const unsigned char* win_b = a.win + (int64_t)bq * a.win_bs;
+  const unsigned char* comp_b = a.comp + (int64_t)bq * a.comp_bs;
+
+  // =============================== phase A: logits of rows [a0, a0 + nr) for all heads
+  // wave (hg, dh): heads 32*hg .. +31 over head_dim half dh; partial logits are summed in LDS
+  const int a0 = s * a.RPS;
+  const int nr = max(0, min(L, a0 + a.RPS) - a0);
+  const int hg = wave & 1, dh = wave >> 1;
+  const int head = 32 * hg + c;
+  // the whole index row, once: phase A gathers its part, phase B every slot
+  int iv_reg[C::MAX_L / 256];
+#pragma unroll
+  for (int k = 0; k < C::MAX_L / 256; ++k) {
+    const int i = tid + 256 * k;
+    iv_reg[k] = i < L ? irow[i] : -1;
+  }
+  bf16x8 qreg[kDD / 32];
+  {
+    const __bf16* qp = a.q + ((int64_t)q * kDH + head) * kDD + (kDD / 2) * dh + hf * 8;
+#pragma unroll
+    for (int k = 0; k < kDD / 32; ++k) qreg[k] = *reinterpret_cast<const bf16x8*>(qp + 16 * k);
+  }
+#pragma unroll
+  for (int k = 0; k < C::MAX_L / 256; ++k)
+    if (tid + 256 * k < L) idx_lds[tid + 256 * k] = iv_reg[k];
+  __syncthreads();
+  // valid rows of this split as two 64-bit masks (rows 0..63, 64..95 of the split)
+  const uint64_t vm0 = __builtin_amdgcn_ballot_w64(lane < nr && idx_lds[a0 + lane] >= 0);
+  const uint64_t vm1 = __builtin_amdgcn_ballot_w64(64 + lane < nr && idx_lds[a0 + 64 + lane] >= 0);
+  for (int r = wave; r < C::TA * 32; r += 4) {
+    unsigned char* dst = rows + r * (kDD * 2);
+    const int iv = __builtin_amdgcn_readfirstlane(r < nr ? idx_lds[a0 + r] : -1);
+    const int lch = lane ^ row_swz<64>(r);
+    if (iv < 0) {
+      *reinterpret_cast<u32x4*>(dst + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+    } else if (iv < a.win_n) {
+      global_to_lds16(win_b + (int64_t)iv * a.win_rs + lch * 16, (DSA_LDS void*)dst);
+    } else {
+      global_to_lds16(comp_b + (int64_t)(iv - a.win_n) * a.comp_rs + lch * 16, (DSA_LDS void*)dst);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  float* xmine = xbuf + wave * (C::TA * 16 * 64);
+  const float* xpart = xbuf + (wave ^ 2) * (C::TA * 16 * 64);
+  f32x16 sacc[C::TA];
+  {
+    // one MFMA chain per tile, interleaved; rows past the split are masked below
+    const int sw = row_swz<64>(c);
+    const int ch0 = (kDD / 16) * dh + hf;  // logical chunk of k-step 0 in this half of D
+#pragma unroll
+    for (int ti = 0; ti < C::TA; ++ti) sacc[ti] = f32x16{};
+#pragma unroll
+    for (int k = 0; k < kDD / 32; ++k) {
+#pragma unroll
+      for (int ti = 0; ti < C::TA; ++ti) {
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8*>(rows + (ti * 32 + c) * (kDD * 2) + (((ch0 + 2 * k) ^ sw) << 4));
+        sacc[ti] = mfma32(kf, qreg[k], sacc[ti]);
+      }
+    }
+#pragma unroll
+    for (int ti = 0; ti < C::TA; ++ti)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f32x4 v = {sacc[ti][4 * g4], sacc[ti][4 * g4 + 1], sacc[ti][4 * g4 + 2], sacc[ti][4 * g4 + 3]};
+        *reinterpret_cast<f32x4*>(xmine + ((ti * 4 + g4) * 64 + lane) * 4) = v;
+      }
+  }
+  __syncthreads();
+  float sv[C::TA][16];
+  float mloc = -__builtin_inff();
+#pragma unroll
+  for (int ti = 0; ti < C::TA; ++ti) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 o4 = *reinterpret_cast<const f32x4*>(xpart + ((ti * 4 + g4) * 64 + lane) * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = 4 * g4 + i;
+        const int row = ti * 32 + 8 * g4 + 4 * hf + i;
+        const float full = dh == 0 ? sacc[ti][e] + o4[i] : o4[i] + sacc[ti][e];  // same sum in both halves
+        const bool ok = ((row < 64 ? (vm0 >> row) : (vm1 >> (row - 64))) & 1ull) != 0ull;
+        sv[ti][e] = ok ? full * a.scale_log2 : -__builtin_inff();
+        mloc = fmaxf(mloc, sv[ti][e]);
+      }
+    }
+  }
+  mloc = fmaxf(mloc, shfl_xor(mloc, 32));  // max over the split's rows for this lane's head
+  const float mref = mloc == -__builtin_inff() ? 0.f : mloc;
+  float lsum = 0.f;
+  __bf16* prow = a.pbuf + ((int64_t)q * kDH + head) * a.Lp + a0;
+#pragma unroll
+  for (int ti = 0; ti < C::TA; ++ti) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int rb = ti * 32 + 8 * g + 4 * hf;
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[i] = exp2f(sv[ti][4 * g + i] - mref);
+        lsum += rb < a.RPS ? p[i] : 0.f;
+      }
+      // each half of the pair writes half of the rows; rows past nr carry P = 0
+      if (rb < a.RPS && (g >> 1) == dh) {
+        const bf16x4 pv = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
+        if (a.local)
+          *reinterpret_cast<bf16x4*>(prow + rb) = pv;
+        else
+          store_coherent(prow + rb, pv);
+      }
+    }
+  }
+  lsum += shfl_xor(lsum, 32);
+  const uint32_t my_xcc = a.local ? 0u : xcc_id();
+  if (dh == 0 && hf == 0) {
+    float* st = a.stats + (((int64_t)q * NS + s) * kDH + head) * 2;
+    if (a.local) {
+      st[0] = mloc;
+      st[1] = lsum;
+    } else {
+      __hip_atomic_store(st, mloc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(st + 1, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  if (tid == 0 && !a.local) __hip_atomic_store(a.xcc + (int64_t)q * NS + s, my_xcc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  // =============================== phase B gather, independent of the other workgroups
+  // Columns [d0, d0 + DS) of every row of the query go into the LDS the split's rows used; this
+  // is issued before the rendezvous so its latency hides the wait.
+  const int d0 = s * C::DS;
+  const int Lk = (L + 15) & ~15;  // rows the MFMA k-steps touch
+  __syncthreads();  // every wave is done with phase A's rows
+  {
+    const int ngrp = Lk / C::RPIB;
+    for (int g = wave; g < ngrp; g += 4) {
+      const int r = g * C::RPIB + lane / C::LPRB;
+      const int p = lane % C::LPRB;
+      const int lch = p ^ slice_swz<NS>(r);
+      unsigned char* grp = rows + g * C::RPIB * C::SLICEB;
+      const int iv = r < L ? idx_lds[r] : -1;
+      if (iv < 0) {
+        *reinterpret_cast<u32x4*>(grp + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+      } else if (iv < a.win_n) {
+        global_to_lds16(win_b + (int64_t)iv * a.win_rs + d0 * 2 + lch * 16, (DSA_LDS void*)grp);
+      } else {
+        global_to_lds16(comp_b + (int64_t)(iv - a.win_n) * a.comp_rs + d0 * 2 + lch * 16, (DSA_LDS void*)grp);
+      }
+    }
+  }
+
+  // =============================== rendezvous of the query's NS workgroups
+  // P, the stats and the XCD ids were stored write-through at device scope; each wave waits for
+  // its stores (and its slice gathers) to complete before the barrier, so they are visible to
+  // every reader once the count reaches NS.  No cache-wide write-back or invalidate.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t* arrive = &g_dec_sync[2 * q];
+    uint32_t* depart = &g_dec_sync[2 * q + 1];
+    __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t t0 = wall_clock64();
+    int to = 0;
+    for (uint32_t it = 1; poll_load(arrive) < (uint32_t)NS; ++it) {
+      if ((it & 15u) == 0u && wall_clock64() - t0 > kSpinTimeoutTicks) {
+        to = 1;
+        atomicOr(&g_dec_error, 1u);
+        break;
+      }
+    }
+    if (__hip_atomic_fetch_add(depart, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(NS - 1)) {
+      // last one out clears the pair for the next call
+      __hip_atomic_exchange(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_exchange(depart, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    flags[0] = to;
+  }
+  __syncthreads();
+  // a writer on another XCD means P must be read past this XCD's L2
+  bool remote = false;
+  if (!a.local) {
+    const uint32_t wx = lane < NS ? __hip_atomic_load(a.xcc + (int64_t)q * NS + lane, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT) : my_xcc;
+    remote = __builtin_amdgcn_ballot_w64(wx != my_xcc) != 0ull;
+  }
+
+  // =============================== phase B: columns [d0, d0 + DS) of every head over all rows
+  const int hb = wave & 1, kh = wave >> 1;
+  const int headB = 32 * hb + c;
+  // this wave's P operands (B of O^T = V^T . P^T): every k-step of its splits, loaded at once
+  const __bf16* pcol = a.pbuf + ((int64_t)q * kDH + headB) * a.Lp + 8 * hf;
+  bf16x8 pre[C::NSW][C::KPS];
+#pragma unroll
+  for (int tl = 0; tl < C::NSW; ++tl)
+#pragma unroll
+    for (int k = 0; k < C::KPS; ++k) {
+      const int r0 = (kh + 2 * tl) * a.RPS + 16 * k;
+      const bool ok = 16 * k < a.RPS && r0 < Lk;
+      pre[tl][k] = !ok ? bf16x8{} : remote ? load_coherent8(pcol + r0) : *reinterpret_cast<const bf16x8*>(pcol + r0);
+    }
+  for (int i = tid; i < NS * kDH * 2; i += 256)
+    stats_lds[i] = a.local ? a.stats[(int64_t)q * NS * kDH * 2 + i]
+                           : __hip_atomic_load(a.stats + (int64_t)q * NS * kDH * 2 + i, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const float sink2 = a.sink[headB] * kLog2eD;
+  float M = sink2;
+#pragma unroll
+  for (int t = 0; t < NS; ++t) M = fmaxf(M, stats_lds[(t * kDH + headB) * 2]);
+  float den = exp2f(sink2 - M);
+#pragma unroll
+  for (int t = 0; t < NS; ++t) den += stats_lds[(t * kDH + headB) * 2 + 1] * exp2f(stats_lds[(t * kDH + headB) * 2] - M);
+  __builtin_amdgcn_s_waitcnt(0);
+
+  // lane-constant parts of the transposing reads
+  const int colq = 16 * ((lane >> 4) & 1) + 4 * (j16 & 3);
+  const int hoff = (j16 & 1) << 3;
+  f32x16 tot[C::NMB];
+#pragma unroll
+  for (int mb = 0; mb < C::NMB; ++mb) tot[mb] = f32x16{};
+#pragma unroll
+  for (int tl = 0; tl < C::NSW; ++tl) {
+    const int t = kh + 2 * tl;
+    const int rb = t * a.RPS;
+    if (rb >= Lk) break;
+    const float fs = exp2f(stats_lds[(t * kDH + headB) * 2] - M);
+    f32x16 acc[C::NMB];
+#pragma unroll
+    for (int mb = 0; mb < C::NMB; ++mb) acc[mb] = f32x16{};
+#pragma unroll
+    for (int k = 0; k < C::KPS; ++k) {
+      const int r0 = rb + 16 * k;
+      if (16 * k >= a.RPS || r0 >= Lk) break;
+#pragma unroll
+      for (int mb = 0; mb < C::NMB; ++mb) {
+        const int col = 32 * mb + colq;
+        const int lch = col >> 3;
+        const int R0 = r0 + 8 * hf + (j16 >> 2);
+        const bf16x4 lo = lds_read_tr16((const DSA_LDS __bf16*)(rows + R0 * C::SLICEB + ((lch ^ slice_swz<NS>(R0)) << 4) + hoff));
+        const int R1 = R0 + 4;
+        const bf16x4 hi = lds_read_tr16((const DSA_LDS __bf16*)(rows + R1 * C::SLICEB + ((lch ^ slice_swz<NS>(R1)) << 4) + hoff));
+        const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        acc[mb] = mfma32(vf, pre[tl][k], acc[mb]);
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < C::NMB; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) tot[mb][e] += fs * acc[mb][e];
+  }
+  __syncthreads();  // done with the slices: reuse the LDS for the row-half reduction
+  float* red = reinterpret_cast<float*>(rows);
+  if (kh == 1) {
+#pragma unroll
+    for (int mb = 0; mb < C::NMB; ++mb)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) red[((hb * C::NMB + mb) * 16 + e) * 64 + lane] = tot[mb][e];
+  }
+  __syncthreads();
+  if (kh == 0) {
+    const float inv = flags[0] ? __builtin_nanf("") : 1.f / den;
+    __bf16* op = a.o + ((int64_t)q * kDH + headB) * kDD + d0 + 4 * hf;
+#pragma unroll
+    for (int mb = 0; mb < C::NMB; ++mb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int e = 4 * g + i;
+          v[i] = (tot[mb][e] + red[((hb * C::NMB + mb) * 16 + e) * 64 + lane]) * inv;
+        }
+        const bf16x4 ov = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+        *reinterpret_cast<bf16x4*>(op + 32 * mb + 8 * g) = ov;
+      }
+  }
+}
+
+// One-time check of how workgroups land on XCDs: the XCD-local rendezvous needs every
+// workgroup with the same blockIdx mod 8 on the same XCD.
+__device__ uint32_t g_xcc_probe[2048];
+
+__global__ void xcc_probe_kernel() {
+  if (threadIdx.x == 0) g_xcc_probe[blockIdx.x] = xcc_id();
+}
+
+struct DecPlan {
+  int ns, rps, lp, ok;
+};
+
+int g_resident_blocks[64][2] = {};  // per device and split count: workgroups resident at once
+int g_xcd_local[64] = {};           // per device: 0 unknown, 1 XCD-local rendezvous valid, -1 not
+
+int xcd_local_mode(int dev, hipStream_t st) {
+  if (g_xcd_local[dev] != 0) return g_xcd_local[dev] > 0;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return 0;  // decide later
+  int ok = 1;
+  hipLaunchKernelGGL(xcc_probe_kernel, dim3(2048), dim3(64), 0, st);
+  uint32_t ids[2048];
+  if (hipGetLastError() != hipSuccess || hipStreamSynchronize(st) != hipSuccess ||
+      hipMemcpyFromSymbol(ids, HIP_SYMBOL(g_xcc_probe), sizeof(ids)) != hipSuccess) {
+    ok = 0;
+  } else {
+    for (int i = 8; i < 2048; ++i) ok &= ids[i] == ids[i & 7];
+  }
+  g_xcd_local[dev] = ok ? 1 : -1;
+  return ok;
+}
+
+template <int NS>
+int resident_blocks(int dev) {
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sparse_attn_decode_kernel<NS>, 256, 0) != hipSuccess)
+    return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return per_cu * cus;
+}
+
+DecPlan plan_decode(int Q, int H, int D, int L, bool fp4) {
+  DecPlan p{0, 0, 0, 0};
+  if (D != kDD || H != kDH || fp4 || Q <= 0 || Q >= 256 || Q > kDecQueriesMax || L <= 0) return p;
+  p.ns = Q > 16 ? 8 : 16;
+  const int per = (L + p.ns - 1) / p.ns;
+  p.rps = (per + 15) & ~15;
+  p.lp = p.ns * p.rps;
+  const int max_l = p.ns == 8 ? DecCfg<8>::MAX_L : DecCfg<16>::MAX_L;
+  const int kps = p.ns == 8 ? DecCfg<8>::KPS : DecCfg<16>::KPS;
+  if (p.rps > kDecRowsMax || p.rps > 16 * kps || ((L + 15) & ~15) > max_l) return p;
+  p.ok = 1;
+  return p;
+}
+
+}  // namespace
+
+size_t sparse_attn_decode_workspace(int B, int S, int H, int D, int L, bool fp4) {
+  const DecPlan p = plan_decode(B * S, H, D, L, fp4);
+  if (!p.ok) return 0;
+  const size_t Q = (size_t)B * S;
+  return Q * kDH * p.lp * 2 + Q * p.ns * kDH * 2 * 4 + Q * p.ns * 4;
+}
+
+// Returns 1 and launches when the two-phase decode path applies, 0 when the caller should use
+// the general kernel, or a negative error.
+int sparse_attn_decode_launch(const __bf16* q, const unsigned char* win, int64_t win_n, int64_t win_bs,
+                              int64_t win_rs, const unsigned char* comp, int64_t comp_bs, int64_t comp_rs,
+                              const float* sink, const int32_t* idx, int L, float scale_log2, __bf16* o, int B,
+                              int S, int H, int D, bool fp4, void* workspace, hipStream_t st) {
+  const DecPlan p = plan_decode(B * S, H, D, L, fp4);
+  if (!p.ok) return 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int& resident = g_resident_blocks[dev][p.ns == 8 ? 0 : 1];
+  if (resident == 0) resident = p.ns == 8 ? resident_blocks<8>(dev) : resident_blocks<16>(dev);
+  const int Q = B * S;
+  if (Q * p.ns > resident) return 0;  // the rendezvous needs every workgroup resident at once
+  DecArgs a{};
+  a.q = q;
+  a.win = win;
+  a.win_n = win_n;
+  a.win_bs = win_bs;
+  a.win_rs = win_rs;
+  a.comp = comp;
+  a.comp_bs = comp_bs;
+  a.comp_rs = comp_rs;
+  a.sink = sink;
+  a.idx = idx;
+  a.L = L;
+  a.scale_log2 = scale_log2;
+  a.o = o;
+  a.pbuf = (__bf16*)workspace;
+  a.stats = (float*)((char*)workspace + (size_t)Q * kDH * p.lp * 2);
+  a.xcc = (uint32_t*)(a.stats + (size_t)Q * p.ns * kDH * 2);
+  a.S = S;
+  a.Q = Q;
+  a.RPS = p.rps;
+  a.Lp = p.lp;
+  a.xcd_map = (Q % 8 == 0) ? 1 : 0;
+  a.local = a.xcd_map && xcd_local_mode(dev, st);
+  dim3 grid(Q * p.ns);
+  if (p.ns == 8)
+    hipLaunchKernelGGL(sparse_attn_decode_kernel<8>, grid, dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(sparse_attn_decode_kernel<16>, grid, dim3(256), 0, st, a);
+  const int rc = check_launch("sparse_attn_decode");
+  return rc ? rc : 1;
+}
+
+}  // namespace dsa

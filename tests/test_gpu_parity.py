@@ -291,3 +291,41 @@ def test_step_full_size_sampled(name):
         np.testing.assert_array_equal(idx_cpu[t, w.Wc:w.Wc + n], w.n_win + np.arange(n) if c[t] <= w.K else
                                       idx_cpu[t, w.Wc:w.Wc + n])
         assert np.all(idx_cpu[t, w.Wc + n:] == -1)
+
+
+# ------------------------------------------------------------------------ two-phase decode path
+@pytest.mark.parametrize("B,S,L,nc,inval", [
+    (32, 1, 640, 2048, 0.0),   # 8 splits, XCD-grouped blocks
+    (24, 1, 640, 1000, 0.1),   # 8 splits
+    (5, 1, 640, 700, 0.2),     # 16 splits, plain block order
+    (16, 1, 640, 16384, 0.0),  # 16 splits
+    (3, 1, 1000, 900, 0.3),    # 16 splits, L > 768
+    (2, 1, 17, 30, 0.0),       # most splits empty
+    (4, 2, 200, 100, 0.5),     # two queries per sequence
+])
+def test_sparse_attn_decode_path(B, S, L, nc, inval):
+    """H = 64, D = 512 bf16 with few queries: the two-phase kernel; three calls in a row check
+    that its per-query counters are left ready for the next call."""
+    dsa = _dsa()
+    _log(f"decode path B={B} S={S} L={L} nc={nc} invalid={inval}")
+    H, D, nw = 64, 512, 128
+    g = torch.Generator().manual_seed(B * 31 + L)
+    q = torch.randn(B, S, H, D, generator=g).to(torch.bfloat16)
+    kv_win = torch.randn(B, nw, D, generator=g).to(torch.bfloat16)
+    kv_comp = torch.randn(B, nc, D, generator=g).to(torch.bfloat16)
+    sink = torch.randn(H, generator=g)
+    rng = np.random.default_rng(B + L)
+    idx = _rand_idx(rng, B, S, L, nw + nc, frac_invalid=inval)
+    idx[0, 0, :] = -1
+    scale = D ** -0.5
+    kv = oracle.kv_concat(kv_win, kv_comp)
+    exp = oracle.sparse_attn(q, kv, sink, idx, scale)
+    args = (q.to(DEV), kv_win.to(DEV), kv_comp.to(DEV), sink.to(DEV), torch.from_numpy(idx).to(DEV), scale)
+    for call in range(3):
+        o = dsa.dsa_sparse_attn(*args)
+        got = o.float().cpu().numpy()
+        err = max_abs_err(got, exp)
+        _log(f"  call {call}: max abs err {err:.3e}")
+        assert np.all(np.isfinite(got))
+        assert np.all(got[0, 0] == 0)
+        assert err <= ATTN_TOL["bf16"], err
