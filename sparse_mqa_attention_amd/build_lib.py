@@ -10,11 +10,15 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = ["abi.cpp", "index_scores.hip", "topk.hip", "sparse_attn.hip", "sparse_attn_decode.hip", "sparse_attn_f32.hip"]
+SOURCES = ["abi.cpp", "index_scores.hip", "topk.hip", "sparse_attn.hip", "sparse_attn_decode.hip", "sparse_attn_prefill.hip",
+           "sparse_attn_f32.hip"]
 ARCH = "gfx950"
 # packed fp32 VALU forms are kept out of the generated code
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
              "-packed-fp32-ops", "-Wall", "-Wno-unused-result"]
+# per-source additions: the prefill attention kernel keeps its MFMA accumulators in VGPRs (its
+# softmax rescales them with VALU ops, and AGPR accumulators would be copied out every tile)
+EXTRA_FLAGS = {"sparse_attn_prefill.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:
@@ -28,7 +32,7 @@ def build(verbose: bool = False) -> str:
     with tempfile.TemporaryDirectory(prefix="dsa_build_") as tmp:
         def compile_one(src):
             obj = os.path.join(tmp, os.path.splitext(src)[0] + ".o")
-            cmd = [hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [hipcc, *HIP_FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
             r = subprocess.run(cmd, capture_output=True, text=True)
             if r.returncode != 0:
                 raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr}")

@@ -436,6 +436,10 @@ int sparse_attn_decode_launch(const __bf16* q, const unsigned char* win, int64_t
                               const float* sink, const int32_t* idx, int L, float scale_log2, __bf16* o, int B,
                               int S, int H, int D, bool fp4, void* workspace, hipStream_t st);
 
+int sparse_attn_prefill_launch(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
+                               const int32_t* idx, int L, float scale, void* o, int B, int S, int H, int D,
+                               hipStream_t st);
+
 int sparse_attn_bf16_launch(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
                             const int32_t* idx, int L, float scale, void* o, int B, int S, int H, int D,
                             void* workspace, hipStream_t st) {
@@ -466,6 +470,9 @@ int sparse_attn_bf16_launch(const void* q, const dsa_kv_src* win, const dsa_kv_s
   const int drc = sparse_attn_decode_launch(a.q, a.win, a.win_n, a.win_bs, a.win_rs, a.comp, a.comp_bs, a.comp_rs,
                                             sink, idx, L, a.scale_log2, a.o, B, S, H, D, fp4, workspace, st);
   if (drc != 0) return drc < 0 ? drc : 0;
+  // prefill batches at head_dim 512: deep-ring kernel, one workgroup per query
+  const int prc = sparse_attn_prefill_launch(q, win, comp, sink, idx, L, scale, o, B, S, H, D, st);
+  if (prc != 0) return prc < 0 ? prc : 0;
   sparse_attn_split(B, S, L, &a.nsplit, &a.split_slots);
   switch (D) {
     case 64: return fp4 ? launch_attn_h<64, true>(a, B, st) : launch_attn_h<64, false>(a, B, st);

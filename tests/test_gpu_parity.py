@@ -165,6 +165,11 @@ def _rand_idx(rng, B, S, L, n, frac_invalid=0.15):
     (1, 260, 64, 512, 260, 65, 100, "bf16", True),
     (2, 2, 100, 128, 16, 16, 40, "bf16", False),
     (1, 2, 8, 512, 16, 16, 33, "bf16", False),
+    # many queries at head_dim 512: the one-workgroup-per-query prefill kernel
+    (2, 160, 64, 512, 160, 300, 1024, "bf16", False),
+    (1, 256, 40, 512, 256, 100, 77, "bf16", True),
+    (1, 264, 16, 512, 264, 50, 33, "bf16", False),
+    (1, 256, 64, 512, 256, 1000, 1025, "bf16", False),
 ])
 def test_sparse_attn(B, S, H, D, nw, nc, L, dtype, fp4):
     dsa = _dsa()
@@ -184,6 +189,8 @@ def test_sparse_attn(B, S, H, D, nw, nc, L, dtype, fp4):
     rng = np.random.default_rng(L)
     idx = _rand_idx(rng, B, S, L, nw + nc)
     idx[0, 0, :] = -1  # a query with no valid slot
+    if L >= 96:
+        idx[0, min(1, S - 1), 32:64] = -1  # a whole 32-slot tile without a valid slot
     if L > 3:
         idx[-1, -1, 1] = idx[-1, -1, 0] = max(idx[-1, -1, 0], 0)  # a duplicate
     scale = D ** -0.5
