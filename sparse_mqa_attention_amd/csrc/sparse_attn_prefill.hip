@@ -61,7 +61,7 @@ struct PreCfg {
   static constexpr int RING = NST * TILE;
   static constexpr int RAWS = FP4 ? NST * RAW : 0;
   static constexpr int XBUF = 4 * 4 * 64 * 16;  // one partial S^T tile per wave
-  static constexpr int MASKS = 2 * NST * 4;     // per ring slot: valid rows, fp4 rows (one byte per wave)
+  static constexpr int MASKS = 2 * NST * 4 + 4;  // per ring slot: valid rows, fp4 rows (a byte per wave); tile set
   static constexpr int LDS = RING + RAWS + XBUF + MASKS + kPMaxSlots * 4;
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
@@ -71,12 +71,11 @@ __device__ __attribute__((aligned(1024))) unsigned char g_pre_zero_row[kPD * 2];
 
 __device__ __forceinline__ int p_slot(int r) { return (r & 16) | ((r & 3) << 2) | ((r >> 2) & 3); }
 
-__device__ __forceinline__ float p_e2m1(uint32_t nib) {
-  const uint32_t m3 = nib & 7u;
-  const uint32_t e = m3 >> 1;
-  uint32_t bits = e ? (((e + 126u) << 23) | ((m3 & 1u) << 22)) : ((m3 & 1u) ? 0x3F000000u : 0u);
-  bits |= (nib & 8u) << 28;
-  return __uint_as_float(bits);
+// e2m1 code in bits 3:0 of n -> its value times 2^-126: the three magnitude bits placed at bit 22
+// are the exponent field and top mantissa bit of the f32 (code 1, the e2m1 subnormal 0.5, lands on
+// the f32 subnormal 2^-127); f32 subnormals are kept in this code.
+__device__ __forceinline__ float p_e2m1_tiny(uint32_t n) {
+  return __uint_as_float(((n & 7u) << 22) | ((n & 8u) << 28));
 }
 
 __device__ __forceinline__ float p_e4m3(uint32_t sc) {
@@ -96,18 +95,50 @@ __device__ __forceinline__ float p_e4m3(uint32_t sc) {
 // so the compiler does not track them: it would otherwise wait for every outstanding copy before
 // each LDS access.  The kernel waits for the copies itself (wait_vmcnt).  The s_nop gives the one
 // wait state a copy needs after the M0 write that sets its LDS base.
+// A wave-uniform pointer, placed in scalar registers (the copies take their base from there).
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Base of a slot's row from its code: the zero row (bit 1), the compressed rows (bit 0) or the
+// window rows.  Written as scalar selects: as C++ the compiler turns the choice into a table in
+// private memory.
+__device__ __forceinline__ const void* slot_base(uint32_t code, const void* win, const void* comp, const void* zero) {
+  const void* r;
+  asm("s_bitcmp1_b32 %1, 0\n\ts_cselect_b64 %0, %3, %2\n\ts_bitcmp1_b32 %1, 1\n\ts_cselect_b64 %0, %4, %0"
+      : "=&s"(r)
+      : "s"(code), "s"(win), "s"(comp), "s"(zero)
+      : "scc");
+  return r;
+}
+
 __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, const DSA_LDS void* lds_base) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
                "{m0}"((uint32_t)(uintptr_t)lds_base)
                : "memory");
 }
 __device__ __forceinline__ void dma4_s(const void* sbase, uint32_t voff, const DSA_LDS void* lds_base) {
+  sbase = uniform_ptr(sbase);
   asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"((uint32_t)(uintptr_t)lds_base)
                : "memory");
 }
 __device__ __forceinline__ void dma16_v(const void* gptr, const DSA_LDS void* lds_base) {
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"((uint32_t)(uintptr_t)lds_base)
                : "memory");
+}
+
+// x *= f in the register x already holds: a plain multiply inside the rare rescale branch makes
+// the register allocator shuffle the whole accumulator set at the branch's merge.
+__device__ __forceinline__ void scale_in_place(f32x16& v, float f) {
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    float x = v[e];
+    asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(f));
+    v[e] = x;
+  }
 }
 
 template <int N>
@@ -124,6 +155,7 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_kernel(PreArgs a) {
   unsigned char* raw = smem + C::RING;
   float* xbuf = reinterpret_cast<float*>(smem + C::RING + C::RAWS);
   unsigned char* masks = smem + C::RING + C::RAWS + C::XBUF;  // [NST][2][4] bytes
+  uint32_t* tset = reinterpret_cast<uint32_t*>(masks + 2 * C::NST * 4);  // tiles with a valid slot
   int* idx_lds = reinterpret_cast<int*>(smem + C::RING + C::RAWS + C::XBUF + C::MASKS);
 
   const int tid = threadIdx.x;
@@ -147,39 +179,52 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_kernel(PreArgs a) {
   const int win_n = (int)a.win_n;
   // kept in scalar registers: left alone, the compiler re-reads the symbol's address for every row
   const unsigned char* zero_row = g_pre_zero_row;
+  const void* win_u = uniform_ptr(win_b);
+  const void* comp_u = uniform_ptr(comp_b);
+  const void* zero_u = uniform_ptr(zero_row);
   asm volatile("" : "+s"(zero_row));
 
   // Gather this wave's rows of tile ti into ring slot ti % NST: one copy per row (a -1 slot copies
   // the zero row), and record which rows are valid and which are fp4 rows still to decode.
-  auto issue = [&](int ti) {
-    const int slot = ti % C::NST;
-    const int myidx = idx_lds[ti * kPTile + 8 * wave + (lane & 7)];
-    unsigned char* tile = ring + slot * C::TILE;
-    unsigned char* rtile = FP4 ? raw + slot * C::RAW : nullptr;
-    uint32_t vbits = 0u, fbits = 0u;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int r = 8 * wave + k;
-      const int iv = __builtin_amdgcn_readlane(myidx, k);
-      vbits |= (iv >= 0 ? 1u : 0u) << k;
-      if (FP4 && iv >= win_n) {
-        // the raw row: 256 nibble bytes from lanes 0..15, then its 32 scale bytes from lanes 16..17
-        const int64_t cr = iv - win_n;
-        const unsigned char* src =
-            lane < 16 ? comp_b + cr * a.comp_rs + lane * 16 : csc_b + cr * a.csc_rs + (lane - 16) * 16;
-        if (lane < 18) dma16_v(src, (DSA_LDS void*)(rtile + r * 288));
-        fbits |= 1u << k;
-      } else {
-        const unsigned char* src = iv < 0 ? zero_row
-                                   : iv < win_n ? win_b + (int64_t)iv * a.win_rs
-                                                : comp_b + (int64_t)(iv - win_n) * a.comp_rs;
-        dma16_s(src, (uint32_t)lane * 16u, (DSA_LDS void*)(tile + p_slot(r) * kPRow));
-      }
-    }
+  // The copies of a tile are issued in parts (rows k0..k1-1 of this wave's 8), spread over the
+  // phases of the previous tile's work: a CU takes in copies at a bounded rate, and a copy issued
+  // while the queue is full stalls its wave.  `myidx` holds the tile's slots in lanes 0..7.
+  // slot codes (see the prologue): byte offset of the row from its base, bit 0 = compressed row,
+  // bit 1 = empty slot (the zero row); for an fp4 compressed row the offset field holds its row
+  auto tile_index = [&](int tile) { return idx_lds[tile * kPTile + 8 * wave + (lane & 7)]; };
+  auto issue_masks = [&](int k, int myidx) {
+    const int slot = k % C::NST;
+    const uint32_t vbits = (uint32_t)__builtin_amdgcn_ballot_w64(lane < 8 && !(myidx & 2));
+    const uint32_t fbits = FP4 ? (uint32_t)__builtin_amdgcn_ballot_w64(lane < 8 && (myidx & 1)) : 0u;
     if (lane == 0) {
       masks[slot * 8 + wave] = (unsigned char)vbits;
       masks[slot * 8 + 4 + wave] = (unsigned char)fbits;
     }
+  };
+  auto issue_rows = [&](int kpos, int myidx, int k0, int k1) {
+    const int slot = kpos % C::NST;
+    unsigned char* tile = ring + slot * C::TILE;
+    unsigned char* rtile = FP4 ? raw + slot * C::RAW : nullptr;
+#pragma unroll
+    for (int k = k0; k < k1; ++k) {
+      const int r = 8 * wave + k;
+      const uint32_t x = (uint32_t)__builtin_amdgcn_readlane(myidx, k);
+      if (FP4 && (x & 1u)) {
+        // the raw row: 256 nibble bytes from lanes 0..15, then its 32 scale bytes from lanes 16..17
+        const int64_t cr = x >> 4;
+        const unsigned char* src =
+            lane < 16 ? comp_b + cr * a.comp_rs + lane * 16 : csc_b + cr * a.csc_rs + (lane - 16) * 16;
+        if (lane < 18) dma16_v(src, (DSA_LDS void*)(rtile + r * 288));
+      } else {
+        dma16_s(slot_base(x, win_u, comp_u, zero_u), (uint32_t)lane * 16u + (x & ~15u),
+                (DSA_LDS void*)(tile + p_slot(r) * kPRow));
+      }
+    }
+  };
+  auto issue = [&](int k, int tile) {
+    const int myidx = tile_index(tile);
+    issue_masks(k, myidx);
+    issue_rows(k, myidx, 0, 8);
   };
 
   // ---- prologue: the index row into LDS (copies, -1 past L), this wave's query heads (its half of
@@ -188,6 +233,7 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_kernel(PreArgs a) {
     if (i0 + lane < L) dma4_s(irow + i0, (uint32_t)lane * 4u, (DSA_LDS void*)(idx_lds + i0));
   }
   for (int i = L + tid; i < ntiles * kPTile; i += 256) idx_lds[i] = -1;
+  if (tid == 0) *tset = 0u;
   bf16x8 qreg[16];
   {
     const __bf16* qp = a.q + ((int64_t)qi * a.H + min(head, a.H - 1)) * kPD + 256 * dh + hf * 8;
@@ -201,9 +247,38 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_kernel(PreArgs a) {
   const float sink2 = head < a.H ? a.sink[head] * kPLog2e : 0.f;
   wait_vmcnt<0>();
   __syncthreads();
+  // index -> slot code: byte offset from the window or compressed base (bit 0 set for the
+  // latter), or 2 for an empty slot; row offsets fit 32 bits (checked at launch)
+  for (int i = tid; i < ntiles * kPTile; i += 256) {
+    const int iv = idx_lds[i];
+    uint32_t code;
+    if (iv < 0)
+      code = 2u;
+    else if (iv < win_n)
+      code = (uint32_t)iv * (uint32_t)a.win_rs;
+    else
+      code = FP4 ? ((uint32_t)(iv - win_n) << 4) | 1u : (uint32_t)(iv - win_n) * (uint32_t)a.comp_rs | 1u;
+    idx_lds[i] = (int)code;
+  }
+  __syncthreads();
+  // The loop runs over the tiles that hold at least one valid slot (a tile of -1 slots adds
+  // nothing), in order; `pend` holds the tiles still to be issued.
+  for (int i0 = 64 * wave; i0 < ntiles * kPTile; i0 += 256) {
+    const uint64_t v = __builtin_amdgcn_ballot_w64(i0 + lane < ntiles * kPTile && !(idx_lds[i0 + lane] & 2));
+    const uint32_t bits = (v & 0xFFFFFFFFull ? 1u : 0u) | (v >> 32 ? 2u : 0u);
+    if (lane == 0 && bits) atomicOr(tset, bits << (i0 / kPTile));
+  }
+  __syncthreads();
+  uint32_t pend = __builtin_amdgcn_readfirstlane(*tset);
+  const int ntiles_live = __builtin_popcount(pend);
+  auto next_tile = [&]() {
+    const int tile = __builtin_ctz(pend);
+    pend &= pend - 1u;
+    return tile;
+  };
 #pragma unroll
   for (int j = 0; j < C::NST - 1; ++j)
-    if (j < ntiles) issue(j);
+    if (j < ntiles_live) issue(j, next_tile());
 
   f32x16 acc[8];
 #pragma unroll
@@ -217,25 +292,16 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_kernel(PreArgs a) {
   float* xmine = xbuf + wave * 4 * 64 * 4;
   const float* xpart = xbuf + (wave ^ 2) * 4 * 64 * 4;
 
-  for (int ti = 0; ti < ntiles; ++ti) {
-    // tile ti has landed once no more than the copies of the tiles issued after it are outstanding
-    const int later = min(C::NST - 2, ntiles - 1 - ti);
-    if (later >= 2)
-      wait_vmcnt<16>();
-    else if (later == 1)
-      wait_vmcnt<8>();
-    else
-      wait_vmcnt<0>();
-    __syncthreads();
-    const int slot = ti % C::NST;
-    const unsigned char* tile = ring + slot * C::TILE;
-    const uint32_t vmask = *reinterpret_cast<const uint32_t*>(masks + slot * 8);
+  auto tile_ptr = [&](int tj) -> const unsigned char* { return ring + (tj % C::NST) * C::TILE; };
+  auto tile_vmask = [&](int tj) { return *reinterpret_cast<const uint32_t*>(masks + (tj % C::NST) * 8); };
+
+  // decode tile tj's fp4 rows into bf16 (wave w takes rows w, w+4, ..., one 16-byte chunk per lane)
+  auto decode = [&](int tj) {
     if constexpr (FP4) {
-      // decode this tile's fp4 rows into bf16: wave w takes rows w, w+4, ..., one chunk per lane
+      const int slot = tj % C::NST;
       const uint32_t fmask = *reinterpret_cast<const uint32_t*>(masks + slot * 8 + 4);
       const unsigned char* rtile = raw + slot * C::RAW;
       unsigned char* wtile = ring + slot * C::TILE;
-      // fmask bit 8w+k marks row 8w+k
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
         const int r = 4 * k + wave;
@@ -245,79 +311,144 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_kernel(PreArgs a) {
           u32x4 v;
 #pragma unroll
           for (int kk = 0; kk < 4; ++kk) {
-            const bf16x2 pr = {(__bf16)(p_e2m1(word >> (8 * kk)) * sc), (__bf16)(p_e2m1(word >> (8 * kk + 4)) * sc)};
+            // value = e2m1 * scale, exact in f32 and in bf16
+            const float lo = __builtin_amdgcn_ldexpf(p_e2m1_tiny(word >> (8 * kk)), 126) * sc;
+            const float hi = __builtin_amdgcn_ldexpf(p_e2m1_tiny(word >> (8 * kk + 4)), 126) * sc;
+            const bf16x2 pr = {(__bf16)lo, (__bf16)hi};
             v[kk] = __builtin_bit_cast(uint32_t, pr);
           }
           *reinterpret_cast<u32x4*>(wtile + p_slot(r) * kPRow + lane * 16) = v;
         }
       }
+    }
+  };
+
+  // partial S^T of tile tj over this wave's half of D, in two independent chains
+  auto qk = [&](int tj, f32x16& s0, f32x16& s1) {
+    const unsigned char* kp = tile_ptr(tj) + k_base;
+    s0 = f32x16{};
+    s1 = f32x16{};
+#pragma unroll
+    for (int s = 0; s < 16; s += 2) {
+      const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kp + 32 * s);
+      const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kp + 32 * s + 32);
+      s0 = mfma32(k0, qreg[s], s0);
+      s1 = mfma32(k1, qreg[s + 1], s1);
+    }
+  };
+  auto xbuf_put = [&](const f32x16& s0, const f32x16& s1) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 v = {s0[4 * g4] + s1[4 * g4], s0[4 * g4 + 1] + s1[4 * g4 + 1], s0[4 * g4 + 2] + s1[4 * g4 + 2],
+                       s0[4 * g4 + 3] + s1[4 * g4 + 3]};
+      *reinterpret_cast<f32x4*>(xmine + (g4 * 64 + lane) * 4) = v;
+    }
+  };
+  // full q.k of the tile from both halves' partial sums; -inf where the slot is empty
+  auto xbuf_get = [&](uint32_t vmask, float (&sv)[16]) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const f32x4 mine = *reinterpret_cast<const f32x4*>(xmine + (g4 * 64 + lane) * 4);
+      const f32x4 part = *reinterpret_cast<const f32x4*>(xpart + (g4 * 64 + lane) * 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float full = dh == 0 ? mine[i] + part[i] : part[i] + mine[i];  // same sum in both halves
+        sv[4 * g4 + i] = full;
+      }
+    }
+    if (vmask != 0xFFFFFFFFu) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = 8 * (e >> 2) + 4 * hf + (e & 3);
+        if (!((vmask >> row) & 1u)) sv[e] = -__builtin_inff();
+      }
+    }
+  };
+
+  // Software pipeline over the live tiles (position k is ring slot k % NST): iteration k runs QK of
+  // tile k+1 on the matrix cores while the VALU does the softmax of tile k, then PV of tile k while
+  // the partial logits of tile k+1 are exchanged; the copies of tile k+NST-1 are issued in parts
+  // between those phases.  Before the loop: tile 0's logits.
+  const int nt = ntiles_live;
+  float sv[16];
+  if (nt > 0) {
+    const int later0 = min(C::NST - 2, nt - 1);
+    if (later0 >= 2)
+      wait_vmcnt<16>();
+    else if (later0 == 1)
+      wait_vmcnt<8>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
+    if constexpr (FP4) {
+      decode(0);
       __syncthreads();
     }
-    // refill the slot used at ti-1 (every wave is past it)
-    if (ti + C::NST - 1 < ntiles) issue(ti + C::NST - 1);
-
-    // ---- partial S^T over this wave's half of D: two independent chains ----
-    f32x16 s0 = {}, s1 = {};
-    if (vmask != 0u) {
-      const unsigned char* kp = tile + k_base;
-#pragma unroll
-      for (int s = 0; s < 16; s += 2) {
-        const bf16x8 k0 = *reinterpret_cast<const bf16x8*>(kp + 32 * s);
-        const bf16x8 k1 = *reinterpret_cast<const bf16x8*>(kp + 32 * s + 32);
-        s0 = mfma32(k0, qreg[s], s0);
-        s1 = mfma32(k1, qreg[s + 1], s1);
-      }
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 v = {s0[4 * g4] + s1[4 * g4], s0[4 * g4 + 1] + s1[4 * g4 + 1], s0[4 * g4 + 2] + s1[4 * g4 + 2],
-                         s0[4 * g4 + 3] + s1[4 * g4 + 3]};
-        *reinterpret_cast<f32x4*>(xmine + (g4 * 64 + lane) * 4) = v;
-      }
-    }
+    f32x16 s0, s1;
+    qk(0, s0, s1);
+    xbuf_put(s0, s1);
     __syncthreads();
-    if (vmask != 0u) {
-      float sv[16];
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const f32x4 mine = *reinterpret_cast<const f32x4*>(xmine + (g4 * 64 + lane) * 4);
-        const f32x4 part = *reinterpret_cast<const f32x4*>(xpart + (g4 * 64 + lane) * 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float full = dh == 0 ? mine[i] + part[i] : part[i] + mine[i];  // same sum in both halves
-          sv[4 * g4 + i] = full * a.scale_log2;
-        }
-      }
-      if (vmask != 0xFFFFFFFFu) {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = 8 * (e >> 2) + 4 * hf + (e & 3);
-          if (!((vmask >> row) & 1u)) sv[e] = -__builtin_inff();
-        }
-      }
+    xbuf_get(tile_vmask(0), sv);
+  }
+
+  for (int k = 0; k < nt; ++k) {
+    const bool has_next = k + 1 < nt;
+    // tile k+1 has landed once at most the copies of tile k+2 (issued one iteration ago) are out
+    if (has_next) {
+      if (k + 2 < nt && C::NST >= 4)
+        wait_vmcnt<8>();
+      else
+        wait_vmcnt<0>();
+    }
+    __syncthreads();  // also: every wave is done with tile k-1, whose slot is refilled below
+    if constexpr (FP4) {
+      if (has_next) decode(k + 1);
+      __syncthreads();
+    }
+    const int kn = k + C::NST - 1;
+    const bool refill = kn < nt;
+    int nidx = 0;
+    if (refill) {
+      nidx = tile_index(next_tile());
+      issue_masks(kn, nidx);
+      issue_rows(kn, nidx, 0, 2);
+    }
+    // ---- softmax of tile k, first part: its max, and the rare rescale of the accumulators ----
+    // (ahead of QK of tile k+1, so the accumulators are the only large live set there)
+    {
       float mloc = sv[0];
 #pragma unroll
       for (int e = 1; e < 16; ++e) mloc = fmaxf(mloc, sv[e]);
-      mloc = fmaxf(mloc, shfl_xor(mloc, 32));
+      mloc = fmaxf(mloc, shfl_xor(mloc, 32)) * a.scale_log2;  // scale > 0
       if (__builtin_amdgcn_ballot_w64(mloc > m_run + kPRescale) != 0ull) {
         const float m_new = fmaxf(m_run, mloc);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
         l_run *= alpha;
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[m][e] *= alpha;
+        for (int m = 0; m < 8; ++m) scale_in_place(acc[m], alpha);
       }
-      bf16x8 pb[2];
+    }
+    // ---- matrix cores: QK of tile k+1 ----
+    f32x16 s0, s1;
+    if (has_next) qk(k + 1, s0, s1);
+    if (refill) issue_rows(kn, nidx, 2, 4);
+
+    // ---- VALU: probabilities of tile k (a -1 slot's logit is -inf: p = 0) ----
+    bf16x8 pb[2];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(sv[e] - m_run);
-        l_run += p;
-        pb[e >> 3][e & 7] = (__bf16)p;
-      }
-      // ---- O^T += V^T . P^T on this wave's half of D (8 independent chains) ----
-      // k step ks, part pt reads tile rows 16ks + 8pt + 4hf + 0..3 = slots 16ks + 2pt + hf + 4*(0..3)
-      const unsigned char* vp = tile + v_base;
+    for (int e = 0; e < 16; ++e) {
+      const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[e], a.scale_log2, -m_run));
+      l_run += p;
+      pb[e >> 3][e & 7] = (__bf16)p;
+    }
+    // tile k+1's partial logits out to LDS (waits for its QK), which frees their registers
+    if (has_next) xbuf_put(s0, s1);
+    if (refill) issue_rows(kn, nidx, 4, 6);
+    // ---- matrix cores: O^T += V^T . P^T on this wave's half of D (8 independent chains); k step
+    // ks, part pt reads tile rows 16ks + 8pt + 4hf + 0..3 = slots 16ks + 2pt + hf + 4*(0..3) ----
+    {
+      const unsigned char* vp = tile_ptr(k) + v_base;
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
 #pragma unroll
@@ -328,6 +459,12 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_kernel(PreArgs a) {
           acc[m] = mfma32(vf, pb[ks], acc[m]);
         }
       }
+    }
+    if (refill) issue_rows(kn, nidx, 6, 8);
+    // ---- tile k+1's full logits from both halves ----
+    if (has_next) {
+      __syncthreads();
+      xbuf_get(tile_vmask(k + 1), sv);
     }
   }
 
@@ -377,6 +514,9 @@ int sparse_attn_prefill_launch(const void* q, const dsa_kv_src* win, const dsa_k
     return (((uintptr_t)p) & 15) != 0 || (rs & 15) != 0 || (bs & 15) != 0;
   };
   if (misaligned(a.win, a.win_rs, a.win_bs)) return 0;
+  // slot codes hold row byte offsets in 32 bits; the softmax folds a positive scale into exp2
+  if (!(scale > 0.f) || (uint64_t)a.win_n * (uint64_t)a.win_rs >= (1ull << 31)) return 0;
+  if (comp && comp->rows && (uint64_t)comp->n_rows * (uint64_t)(fp4 ? 16 : a.comp_rs) >= (1ull << 31)) return 0;
   if (a.comp && misaligned(a.comp, a.comp_rs, a.comp_bs)) return 0;
   if (fp4 && misaligned(a.csc, a.csc_rs, a.csc_bs)) return 0;
   a.sink = sink;
