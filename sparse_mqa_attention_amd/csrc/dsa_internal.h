@@ -38,6 +38,41 @@ __device__ __forceinline__ void global_to_lds16(const void* gptr, DSA_LDS void* 
   __builtin_amdgcn_global_load_lds(gptr, lds_base, 16, 0, 0);
 }
 
+// ---- global -> LDS copies tracked by the kernel itself ---------------------------------------
+// The same 16-byte (4-byte) copies as global_to_lds16, written as inline asm so the compiler does
+// not track them: it would otherwise wait for every outstanding copy before each LDS access.  A
+// kernel using them waits with wait_vmcnt, counting its own copies (each is one vector memory
+// instruction per wave).  The s_nop gives the one wait state a copy needs after the M0 write that
+// sets its LDS base.  _s forms take the row base in scalar registers and a per-lane 32-bit offset.
+
+// A wave-uniform pointer, placed in scalar registers.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, const DSA_LDS void* lds_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "{m0}"((uint32_t)(uintptr_t)lds_base)
+               : "memory");
+}
+__device__ __forceinline__ void dma4_s(const void* sbase, uint32_t voff, const DSA_LDS void* lds_base) {
+  sbase = uniform_ptr(sbase);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"((uint32_t)(uintptr_t)lds_base)
+               : "memory");
+}
+__device__ __forceinline__ void dma16_v(const void* gptr, const DSA_LDS void* lds_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"((uint32_t)(uintptr_t)lds_base)
+               : "memory");
+}
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  // gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt (6:4) and lgkmcnt (11:8) left at "no wait"
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // XOR pattern applied to the 16-byte chunks of LDS row r (rows of NCH chunks).  Bijective on
 // 0..15, so 16 consecutive rows read at one logical chunk hit 16 different bank groups, and the
 // 4-row x 32-byte blocks of a transposing read spread over all bank groups two at a time.

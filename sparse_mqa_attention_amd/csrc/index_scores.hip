@@ -182,6 +182,10 @@ int launch_bf16_mt(const void* q, const void* k, int64_t kbs, const void* w, flo
 
 }  // namespace
 
+int index_scores_prefill_launch(const void* q_idx, const void* k_idx, int64_t kbs, const void* w, float w_scale,
+                                int B, int S, int T, int H, int DI, int start_pos, int ratio, float* scores,
+                                hipStream_t st);
+
 int index_scores_launch(const void* q_idx, const void* k_idx, int64_t kbs, const void* w, float w_scale,
                         int dtype, int B, int S, int T, int H, int DI, int start_pos, int ratio,
                         float* scores, hipStream_t st) {
@@ -192,6 +196,10 @@ int index_scores_launch(const void* q_idx, const void* k_idx, int64_t kbs, const
                        scores);
     return check_launch("index_scores_f32");
   }
+  // prefill at index head dim 128: keys streamed past queries held in registers
+  const int prc = index_scores_prefill_launch(q_idx, k_idx, kbs, w, w_scale, B, S, T, H, DI, start_pos, ratio,
+                                              scores, st);
+  if (prc != 0) return prc < 0 ? prc : 0;
   switch (DI) {
     case 32: return launch_bf16_mt<32>(q_idx, k_idx, kbs, w, w_scale, B, S, T, H, start_pos, ratio, scores, st);
     case 64: return launch_bf16_mt<64>(q_idx, k_idx, kbs, w, w_scale, B, S, T, H, start_pos, ratio, scores, st);

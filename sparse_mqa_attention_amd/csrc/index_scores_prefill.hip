@@ -1,0 +1,165 @@
+// Index scores for prefill (DeepSeek V4.1 page, `Indexer.forward`; many queries per batch):
+//   scores[b,t,j] = w_scale * sum_h w[b,t,h] * relu(q_idx[b,t,h,:] . k_idx[b,j,:])  for j < c(t),
+//   -inf for c(t) <= j < T, with c(t) = (start_pos + t + 1) / ratio.
+//
+// As a matrix product this is (query, head) rows x compressed-key columns with a short K (the
+// index head dim, 128), reduced over heads in the epilogue.  With K that short, a tile loaded once
+// must be reused across many tiles of the other operand, so:
+//  * one workgroup owns 8 queries (2 per wave); their index heads stay in AGPRs as the MFMA A
+//    operand for the whole kernel (32 heads x 128 dims per query = 8 k-steps of 16);
+//  * the visible keys of the block stream through an LDS ring of 32-key tiles filled by direct
+//    global->LDS copies (keys are contiguous rows, so a tile is one 8 KiB coalesced read); the
+//    16-byte chunks of key row r are XOR-swizzled by r, so the B-operand reads (16 rows at one
+//    chunk) touch every bank group once;
+//  * v_mfma_f32_32x32x16_bf16 with heads as M and keys as N: the accumulator of lane (hf, c)
+//    holds 16 heads of key c, so ReLU, head weights and the head sum stay in registers and one
+//    cross-half shuffle finishes each key;
+//  * keys past the block's last visible row are never loaded; the score row's invisible tail is
+//    filled with -inf by plain stores; the blocks with the most visible keys are dispatched first.
+#include "dsa_internal.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kXDI = 128;                // index head dim of this kernel
+constexpr int kXKS = kXDI / 16;          // MFMA k-steps
+constexpr int kXQ = 8;                   // queries per workgroup
+constexpr int kXKT = 32;                 // keys per tile
+constexpr int kXRowB = kXDI * 2;         // bytes of one key row
+constexpr int kXTileB = kXKT * kXRowB;   // 8 KiB
+constexpr int kXNST = 4;                 // ring stages
+
+__global__ void __launch_bounds__(256, 2)
+index_scores_prefill_kernel(const __bf16* __restrict__ q_idx, const __bf16* __restrict__ k_idx, int64_t k_bstride,
+                            const __bf16* __restrict__ w, float w_scale, int S, int T, int H, int start_pos,
+                            int ratio, int nqb, float* __restrict__ scores) {
+  __shared__ __attribute__((aligned(1024))) unsigned char ring[kXNST * kXTileB];
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int hf = lane >> 5;
+  const int c = lane & 31;
+
+  // heaviest blocks (latest queries, most visible keys) first
+  const int b = blockIdx.x / nqb;
+  const int qb = nqb - 1 - blockIdx.x % nqb;
+  const int t0 = qb * kXQ;
+  const int nq = min(kXQ, S - t0);
+  const int c_blk = min(T, visible_rows(start_pos, t0 + nq - 1, ratio));
+  const int ntl = (c_blk + kXKT - 1) / kXKT;  // tiles holding a key visible to some query here
+
+  const __bf16* kb = k_idx + (int64_t)b * k_bstride;
+
+  // Copies of key tile i into ring slot i % NST: two wave instructions of 4 key rows each; lane l
+  // fills physical chunk l & 15 of row 4u + l/16, which holds logical chunk (l & 15) ^ (row & 15).
+  // Rows past T re-read row T-1 (in bounds; never scored).
+  auto issue = [&](int i) {
+    unsigned char* tile = ring + (i % kXNST) * kXTileB;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int blk = 2 * wave + u;
+      const int r = 4 * blk + (lane >> 4);
+      const int j = min(i * kXKT + r, T - 1);
+      const int chunk = (lane & 15) ^ (r & 15);
+      dma16_v(kb + (int64_t)j * kXDI + chunk * 8, (DSA_LDS void*)(tile + blk * 1024));
+    }
+  };
+
+#pragma unroll
+  for (int i = 0; i < kXNST - 1; ++i)
+    if (i < ntl) issue(i);
+
+  // this wave's two queries: index heads (A operand, AGPRs), head weights, visible counts
+  bf16x8 qa[2][kXKS];
+  float wv[2][16];
+  int ct[2];
+  bool live[2];
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    const int t = t0 + 2 * wave + m;
+    live[m] = t < S;
+    ct[m] = live[m] ? min(T, visible_rows(start_pos, t, ratio)) : 0;
+    const bool hv = live[m] && c < H;
+    const __bf16* qp = q_idx + (((int64_t)b * S + min(t, S - 1)) * H + min(c, H - 1)) * kXDI + hf * 8;
+#pragma unroll
+    for (int s = 0; s < kXKS; ++s) qa[m][s] = hv ? *reinterpret_cast<const bf16x8*>(qp + 16 * s) : bf16x8{};
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int h = 8 * (e >> 2) + 4 * hf + (e & 3);
+      const float wh = bf16_to_f32(w[((int64_t)b * S + min(t, S - 1)) * H + min(h, H - 1)]);
+      wv[m][e] = (live[m] && h < H) ? wh : 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < kXKS; ++s) asm volatile("" : "+a"(qa[m][s]));
+  }
+  wait_vmcnt<0>();  // the compiler's own loads above are done; only copies are counted below
+
+  const float ninf = -__builtin_inff();
+  // lane's B-operand base: key row c, chunk (2s + hf) ^ (c & 15)
+  const int kop_row = c * kXRowB;
+  const int kop_swz = c & 15;
+
+  for (int i = 0; i < ntl; ++i) {
+    const int later = min(kXNST - 2, ntl - 1 - i);
+    if (later >= 2)
+      wait_vmcnt<4>();
+    else if (later == 1)
+      wait_vmcnt<2>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();  // tile i is complete; every wave is past tile i-1, whose slot is refilled
+    if (i + kXNST - 1 < ntl) issue(i + kXNST - 1);
+
+    const unsigned char* tile = ring + (i % kXNST) * kXTileB;
+    bf16x8 kop[kXKS];
+#pragma unroll
+    for (int s = 0; s < kXKS; ++s)
+      kop[s] = *reinterpret_cast<const bf16x8*>(tile + kop_row + (((2 * s + hf) ^ kop_swz) << 4));
+    const int j = i * kXKT + c;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      if (!live[m]) continue;
+      float* out_row = scores + ((int64_t)b * S + t0 + 2 * wave + m) * T;
+      if (i * kXKT >= ct[m]) {  // nothing visible to this query in the tile
+        if (hf == 0 && j < T) out_row[j] = ninf;
+        continue;
+      }
+      f32x16 acc = {};
+#pragma unroll
+      for (int s = 0; s < kXKS; ++s) acc = mfma32(qa[m][s], kop[s], acc);
+      float sum = 0.f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sum += fmaxf(acc[e], 0.f) * wv[m][e];
+      sum += shfl_xor(sum, 32);
+      if (hf == 0 && j < T) out_row[j] = j < ct[m] ? w_scale * sum : ninf;
+    }
+  }
+
+  // invisible tail of each score row: [ntl * 32, T)
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+    if (!live[m]) continue;
+    float* out_row = scores + ((int64_t)b * S + t0 + 2 * wave + m) * T;
+    for (int j = ntl * kXKT + lane; j < T; j += 64) out_row[j] = ninf;
+  }
+}
+
+}  // namespace
+
+// Launches the prefill index kernel when it applies (bf16, index head dim 128, at most 32 index
+// heads, enough queries, 16-byte aligned key rows); returns 1 if launched, 0 if not, <0 on error.
+int index_scores_prefill_launch(const void* q_idx, const void* k_idx, int64_t kbs, const void* w, float w_scale,
+                                int B, int S, int T, int H, int DI, int start_pos, int ratio, float* scores,
+                                hipStream_t st) {
+  if (DI != kXDI || H > 32 || S < 64 || T < 1) return 0;
+  if (((uintptr_t)k_idx & 15) != 0 || ((kbs * 2) & 15) != 0) return 0;
+  const int nqb = (S + kXQ - 1) / kXQ;
+  hipLaunchKernelGGL(index_scores_prefill_kernel, dim3(B * nqb), dim3(256), 0, st, (const __bf16*)q_idx,
+                     (const __bf16*)k_idx, kbs, (const __bf16*)w, w_scale, S, T, H, start_pos, ratio, nqb, scores);
+  const int rc = check_launch("index_scores_prefill");
+  return rc ? rc : 1;
+}
+
+}  // namespace dsa

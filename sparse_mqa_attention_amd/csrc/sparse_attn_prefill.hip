@@ -91,18 +91,6 @@ __device__ __forceinline__ float p_e4m3(uint32_t sc) {
   return (sc & 0x80u) ? -v : v;
 }
 
-// 16-byte global -> LDS copies (lane l's 16 bytes land at lds_base + 16*l), written as inline asm
-// so the compiler does not track them: it would otherwise wait for every outstanding copy before
-// each LDS access.  The kernel waits for the copies itself (wait_vmcnt).  The s_nop gives the one
-// wait state a copy needs after the M0 write that sets its LDS base.
-// A wave-uniform pointer, placed in scalar registers (the copies take their base from there).
-__device__ __forceinline__ const void* uniform_ptr(const void* p) {
-  const uint64_t v = (uint64_t)(uintptr_t)p;
-  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
-  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
-  return (const void*)(uintptr_t)(((uint64_t)hi << 32) | lo);
-}
-
 // Base of a slot's row from its code: the zero row (bit 1), the compressed rows (bit 0) or the
 // window rows.  Written as scalar selects: as C++ the compiler turns the choice into a table in
 // private memory.
@@ -115,21 +103,6 @@ __device__ __forceinline__ const void* slot_base(uint32_t code, const void* win,
   return r;
 }
 
-__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, const DSA_LDS void* lds_base) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
-               "{m0}"((uint32_t)(uintptr_t)lds_base)
-               : "memory");
-}
-__device__ __forceinline__ void dma4_s(const void* sbase, uint32_t voff, const DSA_LDS void* lds_base) {
-  sbase = uniform_ptr(sbase);
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"((uint32_t)(uintptr_t)lds_base)
-               : "memory");
-}
-__device__ __forceinline__ void dma16_v(const void* gptr, const DSA_LDS void* lds_base) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"((uint32_t)(uintptr_t)lds_base)
-               : "memory");
-}
-
 // x *= f in the register x already holds: a plain multiply inside the rare rescale branch makes
 // the register allocator shuffle the whole accumulator set at the branch's merge.
 __device__ __forceinline__ void scale_in_place(f32x16& v, float f) {
@@ -139,12 +112,6 @@ __device__ __forceinline__ void scale_in_place(f32x16& v, float f) {
     asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(f));
     v[e] = x;
   }
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  // gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt (6:4) and lgkmcnt (11:8) left at "no wait"
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 template <bool FP4>

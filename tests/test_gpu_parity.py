@@ -132,6 +132,11 @@ def _check_scores(got, qI, kI, w, w_scale, sp, ratio, rows=None, ctx=""):
     (3, 1, 1234, 308, 32, 128, 4, "bf16"),
     (1, 9, 0, 2, 16, 256, 4, "bf16"),
     (2, 17, 40, 28, 32, 128, 2, "bf16"),
+    # 64+ queries at index head dim 128: the key-streaming prefill kernel
+    (1, 200, 37, 130, 20, 128, 1, "bf16"),
+    (2, 96, 0, 24, 32, 128, 4, "bf16"),
+    (1, 130, 5, 1, 32, 128, 4, "bf16"),
+    (1, 520, 0, 260, 32, 128, 2, "bf16"),
 ])
 def test_index_scores_small(B, S, sp, T, H, DI, ratio, dtype):
     dsa = _dsa()
