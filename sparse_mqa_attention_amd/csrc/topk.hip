@@ -79,13 +79,13 @@ __device__ __forceinline__ uint32_t block_reduce_and_or(uint32_t a, uint32_t o, 
 template <int NT, int KPT>
 __global__ void __launch_bounds__(NT)
 topk_kernel(const float* __restrict__ scores, int S, int T, int K, int start_pos, int ratio, int offset,
-            int32_t* __restrict__ idx, int64_t ld_idx) {
+            int32_t* __restrict__ idx, int64_t ld_idx, int row0) {
   __shared__ int hist[256];
   __shared__ int scan_scratch[NT / 64 + 2];
   __shared__ uint32_t red_scratch[2 * (NT / 64)];
   __shared__ int sel_info[2];
 
-  const int row = blockIdx.x;  // b*S + t
+  const int row = row0 + blockIdx.x;  // b*S + t
   const int t = row % S;
   const int tid = threadIdx.x;
   const int c = min(T, visible_rows(start_pos, t, ratio));
@@ -99,15 +99,17 @@ topk_kernel(const float* __restrict__ scores, int S, int T, int K, int start_pos
   const float* srow = scores + (int64_t)row * T;
   const int jbase = tid * KPT;
   uint32_t key[KPT];
+  // loads first (clamped, always in bounds), then branch-free keys, so the loads overlap
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) key[i] = __float_as_uint(srow[min(jbase + i, c - 1)]);
   uint32_t kand = 0xFFFFFFFFu, kor = 0u;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
-    const int j = jbase + i;
-    key[i] = j < c ? order_key(srow[j]) : 0u;  // invisible: below every real key
-    if (j < c) {
-      kand &= key[i];
-      kor |= key[i];
-    }
+    const bool vis = jbase + i < c;
+    const uint32_t k = order_key(__uint_as_float(key[i]));
+    key[i] = vis ? k : 0u;  // invisible: below every real key
+    kand &= vis ? k : 0xFFFFFFFFu;
+    kor |= vis ? k : 0u;
   }
   uint32_t all_or;
   const uint32_t all_and = block_reduce_and_or<NT>(kand, kor, red_scratch, &all_or);
@@ -178,6 +180,129 @@ topk_kernel(const float* __restrict__ scores, int S, int T, int K, int start_pos
   }
 }
 
+// Many rows (prefill): one wave per row and no workgroup barriers.  Lane l holds the keys of
+// positions 64g + l (g < KPL) in registers (invisible positions get key 0, below every real
+// key).  The radix select takes 8-bit digits, from the highest bit where the row's keys differ,
+// through a wave-private 256-bin LDS histogram.  The kept positions leave in
+// ascending order through ballot/mbcnt prefix counts per group g, which also hand the ties at the
+// threshold to the lowest positions.
+template <int KPL>
+__global__ void __launch_bounds__(256)
+topk_wave_kernel(const float* __restrict__ scores, int rows, int S, int T, int K, int start_pos, int ratio,
+                 int offset, int32_t* __restrict__ idx, int64_t ld_idx) {
+  __shared__ __attribute__((aligned(16))) int whist[4][256];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int row = blockIdx.x * 4 + wave;  // b*S + t
+  if (row >= rows) return;                // wave-uniform; no workgroup barrier below
+  int* hist = whist[wave];
+  const int t = row % S;
+  const int c = min(T, visible_rows(start_pos, t, ratio));
+  int32_t* out = idx + (int64_t)row * ld_idx;
+
+  if (c <= K) {  // every visible position is kept
+    for (int s = lane; s < K; s += 64) out[s] = s < c ? s + offset : -1;
+    return;
+  }
+  const float* srow = scores + (int64_t)row * T;
+  uint32_t key[KPL];
+  // all loads first, then branch-free keys (a branch per element would make the compiler wait
+  // for each load before issuing the next).  Positions past c are read but never used; the
+  // launcher keeps every read inside the scores buffer (rows whose 64*KPL positions would run
+  // past its end go to the per-row workgroup kernel).
+  const float* lrow = srow + lane;
+#pragma unroll
+  for (int g = 0; g < KPL; ++g) key[g] = __float_as_uint(lrow[64 * g]);
+  uint32_t kand = 0xFFFFFFFFu, kor = 0u;
+#pragma unroll
+  for (int g = 0; g < KPL; ++g) {
+    const bool vis = 64 * g + lane < c;
+    const uint32_t k = order_key(__uint_as_float(key[g]));
+    key[g] = vis ? k : 0u;
+    kand &= vis ? k : 0xFFFFFFFFu;
+    kor |= vis ? k : 0u;
+  }
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) {
+    kand &= __shfl_xor(kand, m, 64);
+    kor |= __shfl_xor(kor, m, 64);
+  }
+  const uint32_t diff = kand ^ kor;  // bits that differ among the visible keys
+  uint32_t prefix = kand & ~diff;
+  uint32_t mask = ~diff;
+  int remaining = K;
+  const int ng = (c + 63) / 64;  // groups holding a visible position
+  if (diff != 0u) {
+    int hb = 31 - __builtin_clz(diff);
+    while (true) {
+      const int lo = hb >= 7 ? hb - 7 : 0;
+      const int width = hb - lo + 1;
+      const uint32_t dmask = ((width == 32) ? 0xFFFFFFFFu : ((1u << width) - 1u)) << lo;
+      *reinterpret_cast<int4*>(hist + 4 * lane) = int4{0, 0, 0, 0};
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int g = 0; g < KPL; ++g) {
+        if (g >= ng) break;  // wave-uniform
+        if (64 * g + lane < c && (key[g] & mask) == prefix) atomicAdd(&hist[(key[g] & dmask) >> lo], 1);
+      }
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      // lane l takes digits 255-4l .. 252-4l (largest first); counts of keys in larger digits
+      const int4 h4 = *reinterpret_cast<const int4*>(hist + 252 - 4 * lane);
+      const int c0 = h4.w, c1 = h4.z, c2 = h4.y, c3 = h4.x;  // digits 255-4l, 254-4l, 253-4l, 252-4l
+      const int mine = c0 + c1 + c2 + c3;
+      int incl = mine;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const int u = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += u;
+      }
+      const int excl = incl - mine;  // keys in digits above this lane's four
+      const bool here = excl < remaining && incl >= remaining;
+      const uint64_t hmask = __builtin_amdgcn_ballot_w64(here);
+      const int src = __builtin_ctzll(hmask);
+      int digit = 0, above = 0;
+      if (lane == src) {
+        int a = excl;
+        if (a + c0 >= remaining) {
+          digit = 255 - 4 * lane;
+        } else if ((a += c0) + c1 >= remaining) {
+          digit = 254 - 4 * lane;
+        } else if ((a += c1) + c2 >= remaining) {
+          digit = 253 - 4 * lane;
+        } else {
+          a += c2;
+          digit = 252 - 4 * lane;
+        }
+        above = a;
+      }
+      digit = __shfl(digit, src, 64);
+      above = __shfl(above, src, 64);
+      remaining -= above;
+      prefix |= ((uint32_t)digit << lo);
+      mask |= dmask;
+      if (lo == 0) break;
+      hb = lo - 1;
+    }
+  }
+  const uint32_t tau = prefix;  // key of the K-th best visible score (a real key, so never 0)
+  // keep keys > tau and the first `remaining` keys == tau, in position order (invisible keys are 0)
+  int base = 0, eq_seen = 0;
+#pragma unroll
+  for (int g = 0; g < KPL; ++g) {
+    if (g >= ng) break;  // wave-uniform
+    const uint64_t eqb = __builtin_amdgcn_ballot_w64(key[g] == tau);
+    const int rank = eq_seen + __builtin_amdgcn_mbcnt_hi((uint32_t)(eqb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)eqb, 0));
+    eq_seen += __builtin_popcountll(eqb);
+    const bool keep = key[g] > tau || (key[g] == tau && rank < remaining);
+    const uint64_t kb = __builtin_amdgcn_ballot_w64(keep);
+    const int pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(kb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)kb, 0));
+    if (keep) out[pos] = 64 * g + lane + offset;
+    base += __builtin_popcountll(kb);
+  }
+}
+
 __global__ void window_idx_kernel(int S, int start_pos, int W, int Wc, int32_t* __restrict__ idx, int64_t ld_idx) {
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
   const int row = blockIdx.y;  // b*S + t
@@ -199,14 +324,37 @@ __global__ void window_idx_kernel(int S, int start_pos, int W, int Wc, int32_t* 
 template <int NT, int KPT>
 int launch_topk(const float* scores, int B, int S, int T, int K, int sp, int r, int off, int32_t* idx,
                 int64_t ld, hipStream_t st) {
-  hipLaunchKernelGGL((topk_kernel<NT, KPT>), dim3(B * S), dim3(NT), 0, st, scores, S, T, K, sp, r, off, idx, ld);
+  hipLaunchKernelGGL((topk_kernel<NT, KPT>), dim3(B * S), dim3(NT), 0, st, scores, S, T, K, sp, r, off, idx, ld, 0);
   return check_launch("topk");
 }
 
 }  // namespace
 
+// Rows 0 .. rows-tail-1 on the one-wave kernel, whose reads of 64*KPL positions per row stay inside
+// the buffer; the last `tail` rows on the per-row workgroup kernel (NT threads x KPT keys).
+template <int KPL, int NT, int KPT>
+int launch_topk_wave(const float* scores, int B, int S, int T, int K, int sp, int r, int off, int32_t* idx,
+                     int64_t ld, hipStream_t st) {
+  const int rows = B * S;
+  const int tail = (64 * KPL - T + T - 1) / T;  // rows whose read span would pass the end
+  const int head = rows - tail;
+  hipLaunchKernelGGL((topk_wave_kernel<KPL>), dim3((head + 3) / 4), dim3(256), 0, st, scores, head, S, T, K, sp, r,
+                     off, idx, ld);
+  int rc = check_launch("topk_wave");
+  if (rc || tail == 0) return rc;
+  hipLaunchKernelGGL((topk_kernel<NT, KPT>), dim3(tail), dim3(NT), 0, st, scores, S, T, K, sp, r, off, idx, ld,
+                     head);
+  return check_launch("topk");
+}
+
 int topk_launch(const float* scores, int B, int S, int T, int K, int start_pos, int ratio, int offset,
                 int32_t* idx, int64_t ld_idx, hipStream_t st) {
+  // many rows: one wave per row
+  if ((int64_t)B * S >= 1024) {
+    if (T <= 2048) return launch_topk_wave<32, 256, 8>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, st);
+    if (T <= 4096) return launch_topk_wave<64, 512, 8>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, st);
+    if (T <= 8192) return launch_topk_wave<128, 1024, 8>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, st);
+  }
   // T <= 256*KPT with KPT <= 32, or 1024 threads x 64 keys for the longest rows
   if (T <= 256) return launch_topk<256, 1>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, st);
   if (T <= 512) return launch_topk<256, 2>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, st);

@@ -70,6 +70,11 @@ def test_window_idx(B, S, sp, W):
     (1, 1, 16384, 512, 65535, 4, "ties"),
     (1, 1, 30000, 700, 29999, 1, "normal"),
     (1, 3, 600, 1, 1797, 3, "normal"),
+    # 1024+ rows: one wave per row (2048, 4096 and 8192 keys per lane group)
+    (1, 1100, 4000, 512, 0, 1, "ties"),
+    (2, 600, 8000, 300, 100, 2, "normal"),
+    (1, 1030, 8192, 512, 0, 4, "zeros"),
+    (1, 1500, 1999, 7, 0, 1, "ties"),
 ])
 def test_topk_bit_exact(B, S, T, K, sp, ratio, kind):
     """Given the same float32 scores, the GPU selection equals the oracle's exactly."""
