@@ -66,6 +66,18 @@ __device__ __forceinline__ void dma16_v(const void* gptr, const DSA_LDS void* ld
   asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"((uint32_t)(uintptr_t)lds_base)
                : "memory");
 }
+// Base of a gathered row from its slot code (the row's byte offset from its base, with bit 1 set
+// for an empty slot, read from a zero row, and bit 0 set for a compressed row; else a window row).  Written as scalar selects: as C++ the compiler turns the choice into a table in
+// private memory.
+__device__ __forceinline__ const void* slot_base(uint32_t code, const void* win, const void* comp, const void* zero) {
+  const void* r;
+  asm("s_bitcmp1_b32 %1, 0\n\ts_cselect_b64 %0, %3, %2\n\ts_bitcmp1_b32 %1, 1\n\ts_cselect_b64 %0, %4, %0"
+      : "=&s"(r)
+      : "s"(code), "s"(win), "s"(comp), "s"(zero)
+      : "scc");
+  return r;
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
   // gfx9 s_waitcnt: vmcnt in bits 3:0 and 15:14; expcnt (6:4) and lgkmcnt (11:8) left at "no wait"

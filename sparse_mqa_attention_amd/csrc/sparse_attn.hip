@@ -432,9 +432,9 @@ void sparse_attn_split(int B, int S, int L, int* nsplit, int* split_slots) {
 
 size_t sparse_attn_decode_workspace(int B, int S, int H, int D, int L, bool fp4);
 int sparse_attn_decode_launch(const __bf16* q, const unsigned char* win, int64_t win_n, int64_t win_bs,
-                              int64_t win_rs, const unsigned char* comp, int64_t comp_bs, int64_t comp_rs,
-                              const float* sink, const int32_t* idx, int L, float scale_log2, __bf16* o, int B,
-                              int S, int H, int D, bool fp4, void* workspace, hipStream_t st);
+                              int64_t win_rs, const unsigned char* comp, int64_t comp_n, int64_t comp_bs,
+                              int64_t comp_rs, const float* sink, const int32_t* idx, int L, float scale_log2,
+                              __bf16* o, int B, int S, int H, int D, bool fp4, void* workspace, hipStream_t st);
 
 int sparse_attn_prefill_launch(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
                                const int32_t* idx, int L, float scale, void* o, int B, int S, int H, int D,
@@ -467,8 +467,9 @@ int sparse_attn_bf16_launch(const void* q, const dsa_kv_src* win, const dsa_kv_s
   a.S = S;
   a.H = H;
   // decode batches: two-phase kernel without partial outputs when its shape and residency fit
-  const int drc = sparse_attn_decode_launch(a.q, a.win, a.win_n, a.win_bs, a.win_rs, a.comp, a.comp_bs, a.comp_rs,
-                                            sink, idx, L, a.scale_log2, a.o, B, S, H, D, fp4, workspace, st);
+  const int drc = sparse_attn_decode_launch(a.q, a.win, a.win_n, a.win_bs, a.win_rs, a.comp,
+                                            comp && comp->rows ? comp->n_rows : 0, a.comp_bs, a.comp_rs, sink, idx,
+                                            L, a.scale_log2, a.o, B, S, H, D, fp4, workspace, st);
   if (drc != 0) return drc < 0 ? drc : 0;
   // prefill batches at head_dim 512: deep-ring kernel, one workgroup per query
   const int prc = sparse_attn_prefill_launch(q, win, comp, sink, idx, L, scale, o, B, S, H, D, st);

@@ -104,6 +104,22 @@ __device__ __forceinline__ uint32_t poll_load(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Source of the copies for -1 slots (and rows past the index row): a zero row, so every row of a
+// gather costs one copy and no branch.
+__device__ __attribute__((aligned(1024))) unsigned char g_dec_zero_row[kDD * 2];
+
+// Slot code: the row's byte offset from its base, bit 0 = compressed row, bit 1 = empty slot.
+__device__ __forceinline__ uint32_t dec_slot_code(int iv, int win_n, uint32_t win_rs, uint32_t comp_rs) {
+  return iv < 0 ? 2u : iv < win_n ? (uint32_t)iv * win_rs : ((uint32_t)(iv - win_n) * comp_rs) | 1u;
+}
+
+// Row base of a slot code, per lane (vector selects).
+__device__ __forceinline__ const unsigned char* dec_lane_base(uint32_t code, const unsigned char* win,
+                                                             const unsigned char* comp, const unsigned char* zero) {
+  const unsigned char* b = (code & 1u) ? comp : win;
+  return (code & 2u) ? zero : b;
+}
+
 __device__ __forceinline__ uint32_t xcc_id() {
   uint32_t v;
   asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(v));
@@ -152,11 +168,12 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
   const int hg = wave & 1, dh = wave >> 1;
   const int head = 32 * hg + c;
   // the whole index row, once: phase A gathers its part, phase B every slot
+  const int win_n = (int)a.win_n;
   int iv_reg[C::MAX_L / 256];
 #pragma unroll
   for (int k = 0; k < C::MAX_L / 256; ++k) {
     const int i = tid + 256 * k;
-    iv_reg[k] = i < L ? irow[i] : -1;
+    iv_reg[k] = (int)dec_slot_code(i < L ? irow[i] : -1, win_n, (uint32_t)a.win_rs, (uint32_t)a.comp_rs);
   }
   bf16x8 qreg[kDD / 32];
   {
@@ -169,18 +186,23 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
     if (tid + 256 * k < L) idx_lds[tid + 256 * k] = iv_reg[k];
   __syncthreads();
   // valid rows of this split as two 64-bit masks (rows 0..63, 64..95 of the split)
-  const uint64_t vm0 = __builtin_amdgcn_ballot_w64(lane < nr && idx_lds[a0 + lane] >= 0);
-  const uint64_t vm1 = __builtin_amdgcn_ballot_w64(64 + lane < nr && idx_lds[a0 + 64 + lane] >= 0);
-  for (int r = wave; r < C::TA * 32; r += 4) {
-    unsigned char* dst = rows + r * (kDD * 2);
-    const int iv = __builtin_amdgcn_readfirstlane(r < nr ? idx_lds[a0 + r] : -1);
-    const int lch = lane ^ row_swz<64>(r);
-    if (iv < 0) {
-      *reinterpret_cast<u32x4*>(dst + lane * 16) = u32x4{0u, 0u, 0u, 0u};
-    } else if (iv < a.win_n) {
-      global_to_lds16(win_b + (int64_t)iv * a.win_rs + lch * 16, (DSA_LDS void*)dst);
-    } else {
-      global_to_lds16(comp_b + (int64_t)(iv - a.win_n) * a.comp_rs + lch * 16, (DSA_LDS void*)dst);
+  const uint64_t vm0 = __builtin_amdgcn_ballot_w64(lane < nr && !(idx_lds[a0 + lane] & 2));
+  const uint64_t vm1 = __builtin_amdgcn_ballot_w64(64 + lane < nr && !(idx_lds[a0 + 64 + lane] & 2));
+  {
+    // rows wave, wave+4, ...: this wave's codes in lanes 0..(TA*8-1), one copy per row from the row's
+    // scalar base (a row past the split copies the zero row)
+    const void* win_u = uniform_ptr(win_b);
+    const void* comp_u = uniform_ptr(comp_b);
+    const void* zero_u = uniform_ptr(g_dec_zero_row);
+    const int rl = wave + 4 * lane;
+    const int mycode = rl < nr ? idx_lds[a0 + rl] : 2;
+#pragma unroll
+    for (int k = 0; k < C::TA * 8; ++k) {
+      const int r = wave + 4 * k;
+      const uint32_t x = (uint32_t)__builtin_amdgcn_readlane(mycode, k);
+      const int lch = lane ^ row_swz<64>(r);
+      dma16_s(slot_base(x, win_u, comp_u, zero_u), (uint32_t)lch * 16u + (x & ~15u),
+              (DSA_LDS void*)(rows + r * (kDD * 2)));
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
@@ -243,7 +265,7 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
       float p[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        p[i] = exp2f(sv[ti][4 * g + i] - mref);
+        p[i] = __builtin_amdgcn_exp2f(sv[ti][4 * g + i] - mref);
         lsum += rb < a.RPS ? p[i] : 0.f;
       }
       // each half of the pair writes half of the rows; rows past nr carry P = 0
@@ -270,40 +292,40 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
   }
   if (tid == 0 && !a.local) __hip_atomic_store(a.xcc + (int64_t)q * NS + s, my_xcc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
+  // =============================== arrival at the query's rendezvous
+  // P, the stats and the XCD ids were stored write-through at device scope; each wave waits for
+  // them to complete before the barrier, so they are visible to every reader once the count
+  // reaches NS.  No cache-wide write-back or invalidate.  Nothing else is in flight here.
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();  // also: every wave is done with phase A's rows
+  uint32_t* arrive = &g_dec_sync[2 * q];
+  uint32_t* depart = &g_dec_sync[2 * q + 1];
+  if (tid == 0) __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
   // =============================== phase B gather, independent of the other workgroups
-  // Columns [d0, d0 + DS) of every row of the query go into the LDS the split's rows used; this
-  // is issued before the rendezvous so its latency hides the wait.
+  // Columns [d0, d0 + DS) of every row of the query go into the LDS the split's rows used,
+  // issued before the wait for the siblings so its latency hides in it.
   const int d0 = s * C::DS;
   const int Lk = (L + 15) & ~15;  // rows the MFMA k-steps touch
-  __syncthreads();  // every wave is done with phase A's rows
   {
+    // one copy per group of RPIB slices; each lane picks its row's base (the zero row past L)
     const int ngrp = Lk / C::RPIB;
+    const unsigned char* win_d = win_b + d0 * 2;
+    const unsigned char* comp_d = comp_b + d0 * 2;
+#pragma unroll 4
     for (int g = wave; g < ngrp; g += 4) {
       const int r = g * C::RPIB + lane / C::LPRB;
       const int p = lane % C::LPRB;
       const int lch = p ^ slice_swz<NS>(r);
-      unsigned char* grp = rows + g * C::RPIB * C::SLICEB;
-      const int iv = r < L ? idx_lds[r] : -1;
-      if (iv < 0) {
-        *reinterpret_cast<u32x4*>(grp + lane * 16) = u32x4{0u, 0u, 0u, 0u};
-      } else if (iv < a.win_n) {
-        global_to_lds16(win_b + (int64_t)iv * a.win_rs + d0 * 2 + lch * 16, (DSA_LDS void*)grp);
-      } else {
-        global_to_lds16(comp_b + (int64_t)(iv - a.win_n) * a.comp_rs + d0 * 2 + lch * 16, (DSA_LDS void*)grp);
-      }
+      const uint32_t x = r < L ? (uint32_t)idx_lds[r] : 2u;
+      const unsigned char* src = (x & 2u) ? g_dec_zero_row + lch * 16
+                                          : dec_lane_base(x, win_d, comp_d, g_dec_zero_row) + (x & ~15u) + lch * 16;
+      dma16_v(src, (DSA_LDS void*)(rows + g * C::RPIB * C::SLICEB));
     }
   }
 
-  // =============================== rendezvous of the query's NS workgroups
-  // P, the stats and the XCD ids were stored write-through at device scope; each wave waits for
-  // its stores (and its slice gathers) to complete before the barrier, so they are visible to
-  // every reader once the count reaches NS.  No cache-wide write-back or invalidate.
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
+  // =============================== wait for the query's NS workgroups (bounded)
   if (tid == 0) {
-    uint32_t* arrive = &g_dec_sync[2 * q];
-    uint32_t* depart = &g_dec_sync[2 * q + 1];
-    __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint64_t t0 = wall_clock64();
     int to = 0;
     for (uint32_t it = 1; poll_load(arrive) < (uint32_t)NS; ++it) {
@@ -313,13 +335,9 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
         break;
       }
     }
-    if (__hip_atomic_fetch_add(depart, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(NS - 1)) {
-      // last one out clears the pair for the next call
-      __hip_atomic_exchange(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_exchange(depart, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
     flags[0] = to;
   }
+  __builtin_amdgcn_s_waitcnt(0);  // the slices have landed
   __syncthreads();
   // a writer on another XCD means P must be read past this XCD's L2
   bool remote = false;
@@ -419,6 +437,13 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
         *reinterpret_cast<bf16x4*>(op + 32 * mb + 8 * g) = ov;
       }
   }
+  // departure, off the critical path: every sibling is past its wait by the time the last one
+  // leaves, and that one clears the pair for the next call
+  if (tid == 0 &&
+      __hip_atomic_fetch_add(depart, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(NS - 1)) {
+    __hip_atomic_exchange(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_exchange(depart, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // One-time check of how workgroups land on XCDs: the XCD-local rendezvous needs every
@@ -488,11 +513,15 @@ size_t sparse_attn_decode_workspace(int B, int S, int H, int D, int L, bool fp4)
 // Returns 1 and launches when the two-phase decode path applies, 0 when the caller should use
 // the general kernel, or a negative error.
 int sparse_attn_decode_launch(const __bf16* q, const unsigned char* win, int64_t win_n, int64_t win_bs,
-                              int64_t win_rs, const unsigned char* comp, int64_t comp_bs, int64_t comp_rs,
-                              const float* sink, const int32_t* idx, int L, float scale_log2, __bf16* o, int B,
-                              int S, int H, int D, bool fp4, void* workspace, hipStream_t st) {
+                              int64_t win_rs, const unsigned char* comp, int64_t comp_n, int64_t comp_bs,
+                              int64_t comp_rs, const float* sink, const int32_t* idx, int L, float scale_log2,
+                              __bf16* o, int B, int S, int H, int D, bool fp4, void* workspace, hipStream_t st) {
   const DecPlan p = plan_decode(B * S, H, D, L, fp4);
   if (!p.ok) return 0;
+  // slot codes hold row byte offsets in 32 bits; the copies move 16-byte pieces of rows
+  if ((uint64_t)win_n * (uint64_t)win_rs >= (1ull << 31) || (uint64_t)comp_n * (uint64_t)comp_rs >= (1ull << 31))
+    return 0;
+  if ((((uintptr_t)win | (uintptr_t)comp) & 15) || ((win_rs | win_bs | comp_rs | comp_bs) & 15)) return 0;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   int& resident = g_resident_blocks[dev][p.ns == 8 ? 0 : 1];

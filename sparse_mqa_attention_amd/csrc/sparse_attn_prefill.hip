@@ -91,18 +91,6 @@ __device__ __forceinline__ float p_e4m3(uint32_t sc) {
   return (sc & 0x80u) ? -v : v;
 }
 
-// Base of a slot's row from its code: the zero row (bit 1), the compressed rows (bit 0) or the
-// window rows.  Written as scalar selects: as C++ the compiler turns the choice into a table in
-// private memory.
-__device__ __forceinline__ const void* slot_base(uint32_t code, const void* win, const void* comp, const void* zero) {
-  const void* r;
-  asm("s_bitcmp1_b32 %1, 0\n\ts_cselect_b64 %0, %3, %2\n\ts_bitcmp1_b32 %1, 1\n\ts_cselect_b64 %0, %4, %0"
-      : "=&s"(r)
-      : "s"(code), "s"(win), "s"(comp), "s"(zero)
-      : "scc");
-  return r;
-}
-
 // x *= f in the register x already holds: a plain multiply inside the rare rescale branch makes
 // the register allocator shuffle the whole accumulator set at the branch's merge.
 __device__ __forceinline__ void scale_in_place(f32x16& v, float f) {
