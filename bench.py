@@ -1,7 +1,8 @@
 """Benchmark of the sparse MQA attention step on one MI355X.
 
-A step is one pass of the whole path over one batch of synthetic input: window index rows,
-index scores, top-k selection and sparse attention (every stage a libdsa kernel).  Inputs are
+A step is one pass of the whole path over one batch of synthetic input: index scores, then the
+index rows (window rows and top-k selection, one launch) and sparse attention (every stage a
+libdsa kernel).  Inputs are
 resident in HBM before timing starts; several input sets are rotated so that the 256 MB
 Infinity Cache cannot serve one step from the previous one.
 
@@ -159,9 +160,8 @@ def main():
 
     def stage_select(i):
         s, bf = sets[i % n_sets], bufs[i % n_sets]
-        dsa.dsa_window_idx(bf["idx"], w.start_pos, w.W)
         dsa.dsa_index_scores(s["qI"], s["kI"], s["w"], w_scale, w.start_pos, w.ratio, out=bf["scores"])
-        dsa.dsa_topk(bf["scores"], w.index_topk, w.start_pos, w.ratio, w.n_win, out=bf["idx"], col=Wc)
+        dsa.dsa_select(bf["scores"], w.index_topk, w.start_pos, w.ratio, w.W, w.n_win, out=bf["idx"])
 
     def stage_attn(i):
         s, bf = sets[i % n_sets], bufs[i % n_sets]

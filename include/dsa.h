@@ -7,6 +7,7 @@
  *   dsa_index_scores  score every compressed KV row for every query
  *   dsa_topk          keep the index_topk best visible rows per query
  *   dsa_window_idx    the sliding-window part of each query's index row
+ *   dsa_select        window part and top-k part of the index rows in one launch
  *   dsa_sparse_attn   attend all heads over the rows an index row names
  *
  * Citations refer to the DeepSeek V4.1 model pages ("attention/attend/selected",
@@ -107,7 +108,7 @@ int dsa_index_scores(const void* q_idx, const void* k_idx, int64_t k_batch_strid
  *   idx    int32, row (b,t) starts at idx + (b*S + t) * ld_idx; K entries are written,
  *          so a [B, S, Wc + K] buffer is filled at its tail by passing idx + Wc, ld_idx = Wc + K.
  *
- * Supported: T <= 65536.  NaN scores are outside the contract.
+ * Supported: T <= 32768.  NaN scores are outside the contract.
  */
 int dsa_topk(const float* scores, int B, int S, int T, int index_topk, int start_pos, int ratio,
              int offset, int32_t* idx, int64_t ld_idx, dsa_stream_t stream);
@@ -128,6 +129,22 @@ int dsa_window_idx(int B, int S, int start_pos, int W, int32_t* idx, int64_t ld_
 
 /* Window columns dsa_window_idx writes (min(S, W) in prefill, W in decode), or a negative error. */
 int dsa_window_cols(int S, int start_pos, int W);
+
+/*
+ * A whole index row in one launch (`Indexer.forward` and `get_window_topk_idxs` as the attention
+ * layer joins them): row (b,t) of idx gets its Wc = dsa_window_cols(S, start_pos, W) window
+ * entries at columns [0, Wc), exactly as dsa_window_idx writes them, and its K = min(index_topk, T)
+ * top-k entries at columns [Wc, Wc + K), exactly as dsa_topk writes them with the given offset
+ * (the window-KV row count: S in prefill, W in decode).  Same as the two calls in sequence,
+ * with one kernel instead of two.
+ *
+ *   scores [B, S, T] float32 (may be NULL when T == 0)
+ *   idx    int32, row (b,t) starts at idx + (b*S + t) * ld_idx, ld_idx >= Wc + K.
+ *
+ * Errors: those of dsa_window_idx and dsa_topk.
+ */
+int dsa_select(const float* scores, int B, int S, int T, int index_topk, int start_pos, int ratio, int W,
+               int offset, int32_t* idx, int64_t ld_idx, dsa_stream_t stream);
 
 /*
  * One KV source of sparse attention.  Rows are D elements of the call's dtype

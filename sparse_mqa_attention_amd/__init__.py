@@ -56,6 +56,8 @@ def _load():
     lib.dsa_index_scores.restype = i32
     lib.dsa_topk.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, i64, vp]
     lib.dsa_topk.restype = i32
+    lib.dsa_select.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, i64, vp]
+    lib.dsa_select.restype = i32
     lib.dsa_window_idx.argtypes = [i32, i32, i32, i32, vp, i64, vp]
     lib.dsa_window_idx.restype = i32
     lib.dsa_window_cols.argtypes = [i32, i32, i32]
@@ -172,6 +174,23 @@ def dsa_window_idx(out, start_pos: int, W: int, stream=None):
     return out
 
 
+def dsa_select(scores, index_topk: int, start_pos: int, ratio: int, W: int, offset: int, out=None, stream=None):
+    """Whole index rows [B, S, Wc + K]: window columns, then the top-k columns (one launch)."""
+    B, S, T = scores.shape
+    dev = _dev(scores)
+    _need_contig("scores", scores)
+    Wc = dsa_window_cols(S, start_pos, W)
+    K = min(int(index_topk), T)
+    if out is None:
+        out = torch.empty(B, S, Wc + K, dtype=torch.int32, device=dev)
+    _need_contig("idx", out)
+    if out.dtype != torch.int32 or out.shape[-1] < Wc + K:
+        raise DsaError(-2, "idx must be int32 with room for the window and top-k columns")
+    _check(lib.dsa_select(_ptr(scores), B, S, T, int(index_topk), int(start_pos), int(ratio), int(W), int(offset),
+                          _ptr(out), out.shape[-1], _stream(dev, stream)))
+    return out
+
+
 def kv_src(rows, scales=None, fmt: int = DSA_KV_DENSE) -> DsaKvSrc:
     """Describe one KV source: rows [B, n, D] (dense) or [B, n, D/2] uint8 with scales [B, n, D/16] (fp4)."""
     src = DsaKvSrc()
@@ -239,11 +258,12 @@ def sparse_attention_step(q, kv_win, kv_comp, qI, kI, w, sink, *, start_pos: int
     idx = bufs.get("idx")
     if idx is None:
         idx = torch.empty(B, S, Wc + K, dtype=torch.int32, device=q.device)
-    dsa_window_idx(idx, start_pos, W, stream=stream)
     scores = bufs.get("scores")
     if T > 0:
         scores = dsa_index_scores(qI, kI, w, w_scale, start_pos, ratio, out=scores, stream=stream)
-        dsa_topk(scores, index_topk, start_pos, ratio, kv_win.shape[1], out=idx, col=Wc, stream=stream)
+        dsa_select(scores, index_topk, start_pos, ratio, W, kv_win.shape[1], out=idx, stream=stream)
+    else:
+        dsa_window_idx(idx, start_pos, W, stream=stream)
     o = dsa_sparse_attn(q, kv_win, kv_comp if T > 0 else None, sink, idx, scale, comp_scales=comp_scales,
                         out=bufs.get("o"), workspace=bufs.get("workspace"), stream=stream)
     return o, idx, scores
@@ -254,6 +274,7 @@ __all__ = [
     "DsaKvSrc",
     "dsa_index_scores",
     "dsa_topk",
+    "dsa_select",
     "dsa_window_cols",
     "dsa_window_idx",
     "dsa_sparse_attn",

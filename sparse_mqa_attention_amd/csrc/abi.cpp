@@ -27,7 +27,7 @@ int check_launch(const char* what) {
 
 int index_scores_launch(const void*, const void*, int64_t, const void*, float, int, int, int, int, int, int, int, int,
                         float*, hipStream_t);
-int topk_launch(const float*, int, int, int, int, int, int, int, int32_t*, int64_t, hipStream_t);
+int topk_launch(const float*, int, int, int, int, int, int, int, int32_t*, int64_t, int, int, hipStream_t);
 int window_idx_launch(int, int, int, int, int, int32_t*, int64_t, hipStream_t);
 int sparse_attn_bf16_launch(const void*, const dsa_kv_src*, const dsa_kv_src*, const float*, const int32_t*, int,
                             float, void*, int, int, int, int, void*, hipStream_t);
@@ -79,7 +79,7 @@ int dsa_topk(const float* scores, int B, int S, int T, int index_topk, int start
   if (ld_idx < K) return fail(DSA_ERR_SHAPE, "dsa_topk: ld_idx %lld < K=%d", (long long)ld_idx, K);
   if (B == 0 || S == 0 || K == 0) return DSA_OK;
   if (!scores || !idx) return fail(DSA_ERR_NULL, "dsa_topk: NULL pointer");
-  return dsa::topk_launch(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, (hipStream_t)stream);
+  return dsa::topk_launch(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, 0, 0, (hipStream_t)stream);
 }
 
 int dsa_window_cols(int S, int start_pos, int W) {
@@ -98,6 +98,24 @@ int dsa_window_idx(int B, int S, int start_pos, int W, int32_t* idx, int64_t ld_
   if (B == 0 || S == 0 || Wc == 0) return DSA_OK;
   if (!idx) return fail(DSA_ERR_NULL, "dsa_window_idx: NULL idx");
   return dsa::window_idx_launch(B, S, start_pos, W, Wc, idx, ld_idx, (hipStream_t)stream);
+}
+
+int dsa_select(const float* scores, int B, int S, int T, int index_topk, int start_pos, int ratio, int W,
+               int offset, int32_t* idx, int64_t ld_idx, dsa_stream_t stream) {
+  dsa::g_err[0] = 0;
+  if (B < 0 || S < 0 || T < 0 || index_topk < 0 || start_pos < 0 || ratio <= 0 || offset < 0)
+    return fail(DSA_ERR_SHAPE, "dsa_select: bad sizes B=%d S=%d T=%d index_topk=%d start_pos=%d ratio=%d offset=%d",
+                B, S, T, index_topk, start_pos, ratio, offset);
+  const int Wc = dsa_window_cols(S, start_pos, W);
+  if (Wc < 0) return Wc;
+  dsa::g_err[0] = 0;
+  const int K = index_topk < T ? index_topk : T;
+  if (ld_idx < (int64_t)Wc + K)
+    return fail(DSA_ERR_SHAPE, "dsa_select: ld_idx %lld < Wc + K = %d", (long long)ld_idx, Wc + K);
+  if (B == 0 || S == 0 || Wc + K == 0) return DSA_OK;
+  if (!idx || (K > 0 && !scores)) return fail(DSA_ERR_NULL, "dsa_select: NULL pointer");
+  if (K == 0) return dsa::window_idx_launch(B, S, start_pos, W, Wc, idx, ld_idx, (hipStream_t)stream);
+  return dsa::topk_launch(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, (hipStream_t)stream);
 }
 
 size_t dsa_sparse_attn_workspace_size(int dtype, int B, int S, int H, int D, int L) {

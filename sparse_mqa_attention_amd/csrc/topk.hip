@@ -76,10 +76,23 @@ __device__ __forceinline__ uint32_t block_reduce_and_or(uint32_t a, uint32_t o, 
   return ra;
 }
 
+// Entry s of query t's window row (`get_window_topk_idxs`): chunk positions in prefill
+// (start_pos == 0), ring slots oldest first in decode; -1 past the query / for an unfilled slot.
+__device__ __forceinline__ int window_entry(int t, int s, int start_pos, int W) {
+  if (start_pos == 0) {
+    const int first = t - W + 1 > 0 ? t - W + 1 : 0;
+    const int pos = first + s;
+    return pos <= t ? pos : -1;
+  }
+  const int oldest = start_pos % W + 1;
+  const int slot = oldest + s < W ? oldest + s : oldest + s - W;
+  return slot <= start_pos ? slot : -1;
+}
+
 template <int NT, int KPT>
 __global__ void __launch_bounds__(NT)
 topk_kernel(const float* __restrict__ scores, int S, int T, int K, int start_pos, int ratio, int offset,
-            int32_t* __restrict__ idx, int64_t ld_idx, int row0) {
+            int32_t* __restrict__ idx, int64_t ld_idx, int row0, int W, int Wc) {
   __shared__ int hist[256];
   __shared__ int scan_scratch[NT / 64 + 2];
   __shared__ uint32_t red_scratch[2 * (NT / 64)];
@@ -89,7 +102,8 @@ topk_kernel(const float* __restrict__ scores, int S, int T, int K, int start_pos
   const int t = row % S;
   const int tid = threadIdx.x;
   const int c = min(T, visible_rows(start_pos, t, ratio));
-  int32_t* out = idx + (int64_t)row * ld_idx;
+  for (int s = tid; s < Wc; s += NT) idx[(int64_t)row * ld_idx + s] = window_entry(t, s, start_pos, W);
+  int32_t* out = idx + (int64_t)row * ld_idx + Wc;
 
   if (c <= K) {  // every visible position is kept
     for (int s = tid; s < K; s += NT) out[s] = s < c ? s + offset : -1;
@@ -189,7 +203,7 @@ topk_kernel(const float* __restrict__ scores, int S, int T, int K, int start_pos
 template <int KPL>
 __global__ void __launch_bounds__(256)
 topk_wave_kernel(const float* __restrict__ scores, int rows, int S, int T, int K, int start_pos, int ratio,
-                 int offset, int32_t* __restrict__ idx, int64_t ld_idx) {
+                 int offset, int32_t* __restrict__ idx, int64_t ld_idx, int W, int Wc) {
   __shared__ __attribute__((aligned(16))) int whist[4][256];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -198,7 +212,8 @@ topk_wave_kernel(const float* __restrict__ scores, int rows, int S, int T, int K
   int* hist = whist[wave];
   const int t = row % S;
   const int c = min(T, visible_rows(start_pos, t, ratio));
-  int32_t* out = idx + (int64_t)row * ld_idx;
+  for (int s = lane; s < Wc; s += 64) idx[(int64_t)row * ld_idx + s] = window_entry(t, s, start_pos, W);
+  int32_t* out = idx + (int64_t)row * ld_idx + Wc;
 
   if (c <= K) {  // every visible position is kept
     for (int s = lane; s < K; s += 64) out[s] = s < c ? s + offset : -1;
@@ -307,24 +322,14 @@ __global__ void window_idx_kernel(int S, int start_pos, int W, int Wc, int32_t* 
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
   const int row = blockIdx.y;  // b*S + t
   if (s >= Wc) return;
-  const int t = row % S;
-  int v;
-  if (start_pos == 0) {
-    const int first = t - W + 1 > 0 ? t - W + 1 : 0;
-    const int pos = first + s;
-    v = pos <= t ? pos : -1;
-  } else {
-    const int oldest = start_pos % W + 1;
-    const int slot = oldest + s < W ? oldest + s : oldest + s - W;
-    v = slot <= start_pos ? slot : -1;
-  }
-  idx[(int64_t)row * ld_idx + s] = v;
+  idx[(int64_t)row * ld_idx + s] = window_entry(row % S, s, start_pos, W);
 }
 
 template <int NT, int KPT>
 int launch_topk(const float* scores, int B, int S, int T, int K, int sp, int r, int off, int32_t* idx,
-                int64_t ld, hipStream_t st) {
-  hipLaunchKernelGGL((topk_kernel<NT, KPT>), dim3(B * S), dim3(NT), 0, st, scores, S, T, K, sp, r, off, idx, ld, 0);
+                int64_t ld, int W, int Wc, hipStream_t st) {
+  hipLaunchKernelGGL((topk_kernel<NT, KPT>), dim3(B * S), dim3(NT), 0, st, scores, S, T, K, sp, r, off, idx, ld, 0, W,
+                     Wc);
   return check_launch("topk");
 }
 
@@ -334,36 +339,37 @@ int launch_topk(const float* scores, int B, int S, int T, int K, int sp, int r, 
 // the buffer; the last `tail` rows on the per-row workgroup kernel (NT threads x KPT keys).
 template <int KPL, int NT, int KPT>
 int launch_topk_wave(const float* scores, int B, int S, int T, int K, int sp, int r, int off, int32_t* idx,
-                     int64_t ld, hipStream_t st) {
+                     int64_t ld, int W, int Wc, hipStream_t st) {
   const int rows = B * S;
   const int tail = (64 * KPL - T + T - 1) / T;  // rows whose read span would pass the end
   const int head = rows - tail;
   hipLaunchKernelGGL((topk_wave_kernel<KPL>), dim3((head + 3) / 4), dim3(256), 0, st, scores, head, S, T, K, sp, r,
-                     off, idx, ld);
+                     off, idx, ld, W, Wc);
   int rc = check_launch("topk_wave");
   if (rc || tail == 0) return rc;
   hipLaunchKernelGGL((topk_kernel<NT, KPT>), dim3(tail), dim3(NT), 0, st, scores, S, T, K, sp, r, off, idx, ld,
-                     head);
+                     head, W, Wc);
   return check_launch("topk");
 }
 
+// idx points at the row base; a row gets Wc window entries (W the window) then its K top-k entries.
 int topk_launch(const float* scores, int B, int S, int T, int K, int start_pos, int ratio, int offset,
-                int32_t* idx, int64_t ld_idx, hipStream_t st) {
+                int32_t* idx, int64_t ld_idx, int W, int Wc, hipStream_t st) {
   // many rows: one wave per row
   if ((int64_t)B * S >= 1024) {
-    if (T <= 2048) return launch_topk_wave<32, 256, 8>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, st);
-    if (T <= 4096) return launch_topk_wave<64, 512, 8>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, st);
-    if (T <= 8192) return launch_topk_wave<128, 1024, 8>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, st);
+    if (T <= 2048) return launch_topk_wave<32, 256, 8>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, st);
+    if (T <= 4096) return launch_topk_wave<64, 512, 8>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, st);
+    if (T <= 8192) return launch_topk_wave<128, 1024, 8>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, st);
   }
   // T <= 256*KPT with KPT <= 32, or 1024 threads x 64 keys for the longest rows
-  if (T <= 256) return launch_topk<256, 1>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, st);
-  if (T <= 512) return launch_topk<256, 2>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, st);
-  if (T <= 1024) return launch_topk<256, 4>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, st);
-  if (T <= 2048) return launch_topk<256, 8>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, st);
-  if (T <= 4096) return launch_topk<512, 8>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, st);
-  if (T <= 8192) return launch_topk<1024, 8>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, st);
-  if (T <= 16384) return launch_topk<1024, 16>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, st);
-  if (T <= 32768) return launch_topk<1024, 32>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, st);
+  if (T <= 256) return launch_topk<256, 1>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, st);
+  if (T <= 512) return launch_topk<256, 2>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, st);
+  if (T <= 1024) return launch_topk<256, 4>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, st);
+  if (T <= 2048) return launch_topk<256, 8>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, st);
+  if (T <= 4096) return launch_topk<512, 8>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, st);
+  if (T <= 8192) return launch_topk<1024, 8>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, st);
+  if (T <= 16384) return launch_topk<1024, 16>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, st);
+  if (T <= 32768) return launch_topk<1024, 32>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, st);
   return fail(DSA_ERR_UNSUPPORTED, "dsa_topk: T=%d exceeds the supported 32768 rows", T);
 }
 

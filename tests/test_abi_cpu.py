@@ -24,7 +24,7 @@ def dsa():
 
 def test_header_declares_the_step():
     names = _declared()
-    for n in ["dsa_index_scores", "dsa_topk", "dsa_window_idx", "dsa_sparse_attn", "dsa_last_error",
+    for n in ["dsa_index_scores", "dsa_topk", "dsa_window_idx", "dsa_select", "dsa_sparse_attn", "dsa_last_error",
               "dsa_abi_version", "dsa_sparse_attn_workspace_size", "dsa_window_cols"]:
         assert n in names
 
@@ -66,6 +66,11 @@ def test_argument_errors_without_launch(dsa):
     assert lib.dsa_topk(nul, 1, 1, 10, 8, 0, 4, 0, nul, 8, nul) == -1
     assert lib.dsa_window_idx(1, 2, 5, 4, nul, 4, nul) == -4
     assert lib.dsa_window_idx(1, 2, 0, 4, nul, 1, nul) == -2
+    # whole index rows: ld_idx must hold the window and the top-k columns (2 + 8 here)
+    assert lib.dsa_select(nul, 1, 2, 10, 8, 0, 4, 4, 2, nul, 9, nul) == -2
+    assert lib.dsa_select(nul, 1, 2, 10, 8, 5, 4, 4, 2, nul, 10, nul) == -4  # chunked decode
+    assert lib.dsa_select(nul, 1, 2, 10, 8, 0, 4, 4, 2, nul, 10, nul) == -1
+    assert lib.dsa_select(nul, 0, 2, 10, 8, 0, 4, 4, 2, nul, 10, nul) == 0
     # sparse attention: unsupported head_dim, missing window source, bad format, workspace
     src = dsa.DsaKvSrc()
     src.rows = 16

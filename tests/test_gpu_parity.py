@@ -102,6 +102,34 @@ def test_topk_bit_exact(B, S, T, K, sp, ratio, kind):
     np.testing.assert_array_equal(got[..., 2:], exp)
 
 
+@pytest.mark.parametrize("B,S,T,K,sp,ratio,W", [
+    (1, 64, 16, 8, 0, 4, 16),        # prefill, window narrower than the chunk
+    (2, 37, 100, 8, 0, 2, 128),      # prefill, window wider than the chunk
+    (4, 1, 2048, 512, 8191, 4, 128),  # decode
+    (2, 1, 300, 512, 1199, 4, 128),  # decode, fewer rows than index_topk
+    (1, 1100, 4000, 512, 0, 1, 128),  # one wave per row, tail rows on the per-row kernel
+    (3, 1, 0, 512, 2, 4, 4),         # nothing compressed yet: window part only
+])
+def test_select_whole_rows(B, S, T, K, sp, ratio, W):
+    """One call writes each index row: the window part, then the top-k part, exactly as the oracle."""
+    dsa = _dsa()
+    _log(f"select case B={B} S={S} T={T} K={K} sp={sp} r={ratio} W={W}")
+    rng = np.random.default_rng(7 * T + K + S)
+    s = rng.standard_normal((B, S, max(T, 1))).astype(np.float32)[..., :T]
+    c = oracle.visible_count(np.arange(S), sp, ratio)
+    s[:, np.arange(T)[None, :] >= np.minimum(c, T)[:, None]] = -np.inf
+    scores = torch.from_numpy(np.ascontiguousarray(s)).to(DEV)
+    Wc = dsa.dsa_window_cols(S, sp, W)
+    Kk = min(K, T)
+    out = torch.full((B, S, Wc + Kk + 1), -7, dtype=torch.int32, device=DEV)
+    dsa.dsa_select(scores, K, sp, ratio, W, W, out=out)
+    got = out.cpu().numpy()
+    np.testing.assert_array_equal(got[..., :Wc], oracle.window_rows(W, B, S, sp))
+    if Kk:
+        np.testing.assert_array_equal(got[..., Wc:Wc + Kk], oracle.topk_select(s.astype(np.float64), K, sp, ratio, W))
+    assert np.all(got[..., Wc + Kk:] == -7)  # columns past the row untouched
+
+
 # ------------------------------------------------------------------------ index scores
 def _check_scores(got, qI, kI, w, w_scale, sp, ratio, rows=None, ctx=""):
     q64 = qI.float().numpy().astype(np.float64)
