@@ -1,0 +1,375 @@
+// Sparse MQA attention for prefill (many queries) at head_dim 512 and up to 64 heads
+// (DeepSeek V4.1 page, `sparse_attn_kernel`: gather the indexed rows of the one shared KV tensor,
+// softmax with the per-head sink in the denominator, -1 slots ignored).
+//
+// One workgroup per query, 4 waves; wave w owns heads 16w..16w+15 over the whole head_dim, so a
+// wave's logits are complete without any exchange between waves and the only workgroup barrier
+// per tile is the one that hands a ring slot over.  Each query gathers ~600 KiB of rows, and every
+// row is read by all four waves, twice (as K and as V), so the layout is built for LDS bandwidth:
+//  * rows are gathered with 16-byte direct global->LDS copies into a ring of NST 32-row tiles,
+//    NST-2 tiles ahead of the tile being multiplied; each wave copies 8 rows per tile, one wave
+//    instruction per row, with the row address formed in scalar registers from the index row;
+//  * tile rows are 1056 bytes apart: of the pitches measured, that one serves both the K operand
+//    reads (16 rows x 16 bytes per 16 lanes) and the transposing V reads at ~150 B/clk per CU;
+//  * S^T = K . Q^T on v_mfma_f32_16x16x32_bf16 (rows x 16 heads, K = 32 dims, 4 independent
+//    chains); the accumulator of lane (g, c) holds rows 4g..4g+3 and 16+4g..16+4g+3 of head c,
+//    which is exactly the B operand of O^T = V^T . P^T when the 32 tile rows are taken in the
+//    order (4g+0..3, 16+4g+0..3) for k-group g, so the probabilities never leave their lane;
+//  * V^T comes from two ds_read_b64_tr_b16 per operand (rows 4g.. and 16+4g.., one column per
+//    lane); O^T is 32 accumulators of 16 dims x 16 heads;
+//  * the QK of tile k+1 is issued before the softmax of tile k, so the matrix cores run while the
+//    VALU computes the probabilities; online softmax in base 2 with a lazily raised running max
+//    (the accumulators are rescaled only when a tile raises a head's max by more than 8).
+#include "dsa_internal.h"
+
+namespace dsa {
+
+namespace {
+
+constexpr int kHD = 512;
+constexpr int kHTile = 32;
+constexpr int kHPitch = 1056;
+constexpr int kHTileB = kHTile * kHPitch;
+constexpr int kHNST = 4;
+constexpr int kHMaxSlots = 1024;
+constexpr float kHLog2e = 1.4426950408889634f;
+constexpr float kHRescale = 8.0f;
+constexpr float kHMinit = -1.0e30f;
+
+constexpr int kHRing = kHNST * kHTileB;
+constexpr int kHMasks = kHNST * 4 + 4;  // per slot: valid rows (a byte per wave); tile set
+constexpr int kHLds = kHRing + kHMasks + 12 + kHMaxSlots * 4;
+static_assert(kHLds <= 160 * 1024, "LDS budget");
+
+__device__ __forceinline__ int h_row(int r) { return kHPitch * r; }
+
+struct H16Args {
+  const __bf16* q;
+  const unsigned char* win;
+  int64_t win_n, win_rs;  // rows, bytes
+  int64_t win_bs;         // bytes
+  const unsigned char* comp;
+  int64_t comp_bs, comp_rs;  // bytes
+  const float* sink;
+  const int32_t* idx;
+  int L;
+  float scale_log2;
+  __bf16* o;
+  int S, H;
+};
+
+// Source of the copies for -1 slots: a zero row, so every slot costs exactly one copy.
+__device__ __attribute__((aligned(1024))) unsigned char g_h16_zero_row[kHD * 2];
+
+// 16-byte global->LDS copy of one row piece per lane.  No memory clobber: the copies only ever
+// target a ring slot that no wave reads until after the next wait and barrier (both of which are
+// ordered against this statement), so LDS reads of the other slots may be scheduled across it.
+__device__ __forceinline__ void h_dma16(const void* sbase, uint32_t voff, const DSA_LDS void* lds_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "{m0}"((uint32_t)(uintptr_t)lds_base));
+}
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// x *= f in the registers x already holds (a plain multiply inside the rare rescale branch makes
+// the register allocator shuffle the accumulator set at the branch's merge)
+__device__ __forceinline__ void h_scale(f32x4& v, float f) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    float x = v[e];
+    asm volatile("v_mul_f32 %0, %0, %1" : "+v"(x) : "v"(f));
+    v[e] = x;
+  }
+}
+
+__global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a) {
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[kHLds];
+  unsigned char* ring = smem;
+  unsigned char* masks = smem + kHRing;                                   // [NST][4] bytes
+  uint32_t* tset = reinterpret_cast<uint32_t*>(masks + kHNST * 4);       // tiles with a valid slot
+  int* idx_lds = reinterpret_cast<int*>(smem + kHRing + kHMasks + 12);  // 16-byte aligned
+
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int c = lane & 15;
+  const int head = 16 * wave + c;
+
+  const int qi = blockIdx.x;
+  const int b = qi / a.S;
+  const int L = a.L;
+  const int ntiles = (L + kHTile - 1) / kHTile;
+
+  const unsigned char* win_b = a.win + (int64_t)b * a.win_bs;
+  const unsigned char* comp_b = a.comp + (int64_t)b * a.comp_bs;
+  const int* irow = a.idx + (int64_t)qi * L;
+  const int win_n = (int)a.win_n;
+  const void* win_u = uniform_ptr(win_b);
+  const void* comp_u = uniform_ptr(comp_b);
+  const void* zero_u = uniform_ptr(g_h16_zero_row);
+
+  // ---- prologue: the index row into LDS (copies, -1 past L), this wave's query heads, the sink ----
+  for (int i0 = 64 * wave; i0 < L; i0 += 256) {
+    if (i0 + lane < L) dma4_s(irow + i0, (uint32_t)lane * 4u, (DSA_LDS void*)(idx_lds + i0));
+  }
+  for (int i = L + tid; i < ntiles * kHTile; i += 256) idx_lds[i] = -1;
+  if (tid == 0) *tset = 0u;
+  // B operand of QK: lane (g, c) holds dims 32s + 8g .. 32s + 8g + 7 of head c
+  bf16x8 qreg[16];
+  {
+    const __bf16* qp = a.q + ((int64_t)qi * a.H + min(head, a.H - 1)) * kHD + 8 * g;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) qreg[s] = head < a.H ? *reinterpret_cast<const bf16x8*>(qp + 32 * s) : bf16x8{};
+  }
+#pragma unroll
+  for (int s = 0; s < 16; ++s) asm volatile("" : "+a"(qreg[s]));
+  const float sink2 = head < a.H ? a.sink[head] * kHLog2e : 0.f;
+  wait_vmcnt<0>();
+  __syncthreads();
+  // index -> slot code: byte offset from the window or compressed base (bit 0 set for the
+  // latter), or 2 for an empty slot; row offsets fit 32 bits (checked at launch)
+  for (int i = tid; i < ntiles * kHTile; i += 256) {
+    const int iv = idx_lds[i];
+    uint32_t code;
+    if (iv < 0)
+      code = 2u;
+    else if (iv < win_n)
+      code = (uint32_t)iv * (uint32_t)a.win_rs;
+    else
+      code = (uint32_t)(iv - win_n) * (uint32_t)a.comp_rs | 1u;
+    idx_lds[i] = (int)code;
+  }
+  __syncthreads();
+  for (int i0 = 64 * wave; i0 < ntiles * kHTile; i0 += 256) {
+    const uint64_t v = __builtin_amdgcn_ballot_w64(i0 + lane < ntiles * kHTile && !(idx_lds[i0 + lane] & 2));
+    const uint32_t bits = (v & 0xFFFFFFFFull ? 1u : 0u) | (v >> 32 ? 2u : 0u);
+    if (lane == 0 && bits) atomicOr(tset, bits << (i0 / kHTile));
+  }
+  __syncthreads();
+  // The loop runs over the tiles that hold at least one valid slot, in order (a tile of -1 slots
+  // adds nothing); position k of that list lives in ring slot k % NST.
+  uint32_t pend = __builtin_amdgcn_readfirstlane(*tset);
+  const int nt = __builtin_popcount(pend);
+
+  // copies of this wave's 8 rows of position k (one wave instruction per row; an empty slot
+  // copies the zero row) and the tile's valid-row byte
+  auto issue = [&](int k) {
+    const int tile = __builtin_ctz(pend);
+    pend &= pend - 1u;
+    const int myidx = idx_lds[tile * kHTile + 8 * wave + (lane & 7)];
+    const int slot = k % kHNST;
+    const uint32_t vbits = (uint32_t)__builtin_amdgcn_ballot_w64(lane < 8 && !(myidx & 2));
+    if (lane == 0) masks[slot * 4 + wave] = (unsigned char)vbits;
+    unsigned char* tb = ring + slot * kHTileB;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const uint32_t x = (uint32_t)__builtin_amdgcn_readlane(myidx, r);
+      h_dma16(slot_base(x, win_u, comp_u, zero_u), (uint32_t)lane * 16u + (x & ~15u),
+              (DSA_LDS void*)(tb + h_row(8 * wave + r)));
+    }
+  };
+#pragma unroll
+  for (int j = 0; j < kHNST - 1; ++j)
+    if (j < nt) issue(j);
+
+  // lane bases: K operand (row c, 16-byte chunk 4s + g) and transposed V operand (rows 4g + c/4,
+  // 32-byte column block, 8 bytes per lane)
+  const int k_base = h_row(c) + 16 * g;
+  const int k_hi = h_row(c + 16) - h_row(c);
+  const int v_base = h_row(4 * g + (c >> 2)) + 8 * (c & 3);
+  const int v_hi = h_row(16 + 4 * g + (c >> 2)) - h_row(4 * g + (c >> 2));
+
+  // QK of position k: operand i (k-step i/2 of row block i%2) feeds chain 2(i%2) + (i/2)%2, so each
+  // chain's MFMAs are four apart; the K reads run eight operands ahead of the MFMAs.
+  auto kread = [&](const unsigned char* kp, int i) {
+    return *reinterpret_cast<const bf16x8*>(kp + (i & 1) * k_hi + 64 * (i >> 1));
+  };
+  auto vread = [&](const unsigned char* vp, int d) {
+    const bf16x4 lo = lds_read_tr16((const DSA_LDS __bf16*)(vp + 32 * d));
+    const bf16x4 hi = lds_read_tr16((const DSA_LDS __bf16*)(vp + v_hi + 32 * d));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  };
+
+  f32x4 acc[32];
+#pragma unroll
+  for (int d = 0; d < 32; ++d) acc[d] = f32x4{};
+  float m_run = kHMinit;
+  float l_run = 0.f;
+  auto tile_vmask = [&](int k) { return *reinterpret_cast<const uint32_t*>(masks + (k % kHNST) * 4); };
+
+  // logits of the current position as four chains (summed when first used)
+  f32x4 ch[4] = {};
+  uint32_t vm = 0u;
+  if (nt > 0) {
+    const int later0 = min(kHNST - 2, nt - 1);
+    if (later0 >= 2)
+      wait_vmcnt<16>();
+    else if (later0 == 1)
+      wait_vmcnt<8>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
+    const unsigned char* kp = ring + k_base;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) ch[2 * (i & 1) + ((i >> 1) & 1)] = mfma16(kread(kp, i), qreg[i >> 1], ch[2 * (i & 1) + ((i >> 1) & 1)]);
+    vm = tile_vmask(0);
+  }
+
+  for (int k = 0; k < nt; ++k) {
+    // tile k+1 has landed once at most the copies of tile k+2 are out; the barrier also means every
+    // wave is done with tile k-1, whose slot is refilled below
+    if (k + 2 < nt)
+      wait_vmcnt<8>();
+    else
+      wait_vmcnt<0>();
+    __syncthreads();
+    if (k + kHNST - 1 < nt) issue(k + kHNST - 1);
+    const uint32_t vm_next = tile_vmask(k + 1);
+    const unsigned char* kp = ring + ((k + 1) % kHNST) * kHTileB + k_base;
+    const unsigned char* vp = ring + (k % kHNST) * kHTileB + v_base;
+
+    // ---- one scheduling region: QK of tile k+1 on the matrix cores (a stale slot past the last
+    // tile; never used), the softmax of tile k on the VALU against the running max as it stands,
+    // and the first V operands of tile k ----
+    const f32x4 sc0 = ch[0] + ch[1], sc1 = ch[2] + ch[3];
+    f32x4 cn[4] = {};
+    {
+      bf16x8 kr[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) kr[i] = kread(kp, i);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const int sk = i >> 1, rb = i & 1;
+        cn[2 * rb + (sk & 1)] = mfma16(kr[i & 7], qreg[sk], cn[2 * rb + (sk & 1)]);
+        if (i + 8 < 32) kr[i & 7] = kread(kp, i + 8);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+      for (int i = 0; i < 24; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+    }
+    // lane (g, c) holds rows 4g+v and 16+4g+v of head c
+    float sv[8];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      sv[v] = (vm >> (4 * g + v)) & 1u ? sc0[v] : -__builtin_inff();
+      sv[4 + v] = (vm >> (16 + 4 * g + v)) & 1u ? sc1[v] : -__builtin_inff();
+    }
+    float mloc = sv[0];
+#pragma unroll
+    for (int j = 1; j < 8; ++j) mloc = fmaxf(mloc, sv[j]);
+    mloc = fmaxf(mloc, shfl_xor(mloc, 16));
+    mloc = fmaxf(mloc, shfl_xor(mloc, 32)) * a.scale_log2;  // scale > 0
+    float p[8];
+    float lsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[j], a.scale_log2, -m_run));
+      lsum += p[j];
+    }
+    constexpr int kVPre = 4;
+    bf16x8 vpre[kVPre];
+#pragma unroll
+    for (int d = 0; d < kVPre; ++d) vpre[d] = vread(vp, d);
+
+    // rare: a tile raised some head's max by more than 8; rescale and redo the probabilities
+    if (__builtin_amdgcn_ballot_w64(mloc > m_run + kHRescale) != 0ull) {
+      const float m_new = fmaxf(m_run, mloc);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < 32; ++d) h_scale(acc[d], alpha);
+      lsum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        p[j] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[j], a.scale_log2, -m_run));
+        lsum += p[j];
+      }
+    }
+    l_run += lsum;
+    bf16x8 pb;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) pb[j] = (__bf16)p[j];
+
+    // ---- matrix cores: O^T += V^T . P^T over the whole head_dim (32 independent chains), the
+    // V reads eight operands ahead ----
+#pragma unroll
+    for (int d = 0; d < 32; ++d) acc[d] = mfma16(d < kVPre ? vpre[d] : vread(vp, d), pb, acc[d]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 24; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ch[j] = cn[j];
+    vm = vm_next;
+  }
+  wait_vmcnt<0>();
+
+  if (head >= a.H) return;
+  float l_tot = l_run + shfl_xor(l_run, 16);
+  l_tot += shfl_xor(l_tot, 32);
+  const float mf = fmaxf(m_run, sink2);
+  const float f = exp2f(m_run - mf);
+  const float rn = f / (l_tot * f + exp2f(sink2 - mf));
+  // lane (g, c) holds dims 16d + 4g .. 16d + 4g + 3 of head c
+  __bf16* op = a.o + ((int64_t)qi * a.H + head) * kHD + 4 * g;
+#pragma unroll
+  for (int d = 0; d < 32; ++d) {
+    const bf16x4 v = {(__bf16)(acc[d][0] * rn), (__bf16)(acc[d][1] * rn), (__bf16)(acc[d][2] * rn),
+                      (__bf16)(acc[d][3] * rn)};
+    *reinterpret_cast<bf16x4*>(op + 16 * d) = v;
+  }
+}
+
+}  // namespace
+
+// Launches the kernel when it applies (bf16 rows, head_dim 512, at most 64 heads, index rows of
+// at most 1024 slots, enough queries to fill the GPU, 16-byte aligned rows, row offsets within
+// 32 bits, positive scale); returns 1 if launched, 0 if not, <0 on error.
+int sparse_attn_prefill_h16_launch(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
+                                   const int32_t* idx, int L, float scale, void* o, int B, int S, int H, int D,
+                                   hipStream_t st) {
+  const int Q = B * S;
+  if (D != kHD || H > 64 || L > kHMaxSlots || Q < 256) return 0;
+  if (comp && comp->rows && comp->format != DSA_KV_DENSE) return 0;
+  H16Args a{};
+  a.q = (const __bf16*)q;
+  a.win = (const unsigned char*)win->rows;
+  a.win_n = win->n_rows;
+  a.win_bs = win->batch_stride * 2;
+  a.win_rs = win->row_stride * 2;
+  if (comp && comp->rows) {
+    a.comp = (const unsigned char*)comp->rows;
+    a.comp_bs = comp->batch_stride * 2;
+    a.comp_rs = comp->row_stride * 2;
+  }
+  auto misaligned = [](const void* p, int64_t rs, int64_t bs) {
+    return (((uintptr_t)p) & 15) != 0 || (rs & 15) != 0 || (bs & 15) != 0;
+  };
+  if (misaligned(a.win, a.win_rs, a.win_bs)) return 0;
+  if (a.comp && misaligned(a.comp, a.comp_rs, a.comp_bs)) return 0;
+  if (!(scale > 0.f) || (uint64_t)a.win_n * (uint64_t)a.win_rs >= (1ull << 31)) return 0;
+  if (a.comp && (uint64_t)comp->n_rows * (uint64_t)a.comp_rs >= (1ull << 31)) return 0;
+  a.sink = sink;
+  a.idx = idx;
+  a.L = L;
+  a.scale_log2 = scale * kHLog2e;
+  a.o = (__bf16*)o;
+  a.S = S;
+  a.H = H;
+  hipLaunchKernelGGL(sparse_attn_prefill_h16_kernel, dim3(Q), dim3(256), 0, st, a);
+  const int rc = check_launch("sparse_attn_prefill_h16");
+  return rc ? rc : 1;
+}
+
+}  // namespace dsa

@@ -208,6 +208,7 @@ def _rand_idx(rng, B, S, L, n, frac_invalid=0.15):
     (1, 256, 40, 512, 256, 100, 77, "bf16", True),
     (1, 264, 16, 512, 264, 50, 33, "bf16", False),
     (1, 256, 64, 512, 256, 1000, 1025, "bf16", False),
+    (1, 288, 40, 512, 288, 90, 70, "bf16", False),  # a wave with half of its 16 heads
 ])
 def test_sparse_attn(B, S, H, D, nw, nc, L, dtype, fp4):
     dsa = _dsa()
