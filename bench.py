@@ -28,7 +28,7 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 ROTATE_BYTES = 768 << 20  # rotate input sets until they span more than the Infinity Cache (256 MB)
 KERNEL_SOURCES = ["sparse_mqa_attention_amd/csrc/sparse_attn.hip", "sparse_mqa_attention_amd/csrc/sparse_attn_decode.hip",
-                  "sparse_mqa_attention_amd/csrc/sparse_attn_prefill.hip", "sparse_mqa_attention_amd/csrc/dsa_internal.h"]
+                  "sparse_mqa_attention_amd/csrc/sparse_attn_prefill_h16.hip", "sparse_mqa_attention_amd/csrc/dsa_internal.h"]
 
 
 def _args():

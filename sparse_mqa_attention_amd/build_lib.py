@@ -10,7 +10,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = ["abi.cpp", "index_scores.hip", "index_scores_prefill.hip", "topk.hip", "sparse_attn.hip", "sparse_attn_decode.hip", "sparse_attn_prefill.hip",
+SOURCES = ["abi.cpp", "index_scores.hip", "index_scores_prefill.hip", "topk.hip", "sparse_attn.hip", "sparse_attn_decode.hip",
            "sparse_attn_prefill_h16.hip", "sparse_attn_f32.hip"]
 ARCH = "gfx950"
 # packed fp32 VALU forms are kept out of the generated code
@@ -18,8 +18,7 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", 
              "-packed-fp32-ops", "-Wall", "-Wno-unused-result"]
 # per-source additions: the prefill attention kernel keeps its MFMA accumulators in VGPRs (its
 # softmax rescales them with VALU ops, and AGPR accumulators would be copied out every tile)
-EXTRA_FLAGS = {"sparse_attn_prefill.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
-               "sparse_attn_prefill_h16.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+EXTRA_FLAGS = {"sparse_attn_prefill_h16.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:

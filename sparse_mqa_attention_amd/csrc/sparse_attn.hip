@@ -436,9 +436,6 @@ int sparse_attn_decode_launch(const __bf16* q, const unsigned char* win, int64_t
                               int64_t comp_rs, const float* sink, const int32_t* idx, int L, float scale_log2,
                               __bf16* o, int B, int S, int H, int D, bool fp4, void* workspace, hipStream_t st);
 
-int sparse_attn_prefill_launch(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
-                               const int32_t* idx, int L, float scale, void* o, int B, int S, int H, int D,
-                               hipStream_t st);
 int sparse_attn_prefill_h16_launch(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
                                    const int32_t* idx, int L, float scale, void* o, int B, int S, int H, int D,
                                    hipStream_t st);
@@ -474,11 +471,8 @@ int sparse_attn_bf16_launch(const void* q, const dsa_kv_src* win, const dsa_kv_s
                                             comp && comp->rows ? comp->n_rows : 0, a.comp_bs, a.comp_rs, sink, idx,
                                             L, a.scale_log2, a.o, B, S, H, D, fp4, workspace, st);
   if (drc != 0) return drc < 0 ? drc : 0;
-  // prefill batches at head_dim 512, one workgroup per query: bf16 rows on the 16-heads-per-wave
-  // kernel, fp4 compressed rows on the deep-ring kernel that decodes them in LDS
-  const int hrc = sparse_attn_prefill_h16_launch(q, win, comp, sink, idx, L, scale, o, B, S, H, D, st);
-  if (hrc != 0) return hrc < 0 ? hrc : 0;
-  const int prc = sparse_attn_prefill_launch(q, win, comp, sink, idx, L, scale, o, B, S, H, D, st);
+  // prefill batches at head_dim 512 (bf16 or fp4 compressed rows): one workgroup per query
+  const int prc = sparse_attn_prefill_h16_launch(q, win, comp, sink, idx, L, scale, o, B, S, H, D, st);
   if (prc != 0) return prc < 0 ? prc : 0;
   sparse_attn_split(B, S, L, &a.nsplit, &a.split_slots);
   switch (D) {

@@ -37,11 +37,14 @@ constexpr float kHRescale = 8.0f;
 constexpr float kHMinit = -1.0e30f;
 
 constexpr int kHRing = kHNST * kHTileB;
-constexpr int kHMasks = kHNST * 4 + 4;  // per slot: valid rows (a byte per wave); tile set
+constexpr int kHMasks = kHNST * 8 + 4;  // per slot: valid rows, fp4 rows (a byte per wave each); tile set
+constexpr int kHRaw = kHPitch - 288;    // an fp4 row lands raw in the last 288 bytes of its pitch
 constexpr int kHLds = kHRing + kHMasks + 12 + kHMaxSlots * 4;
 static_assert(kHLds <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ int h_row(int r) { return kHPitch * r; }
+
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
 
 struct H16Args {
   const __bf16* q;
@@ -50,6 +53,8 @@ struct H16Args {
   int64_t win_bs;         // bytes
   const unsigned char* comp;
   int64_t comp_bs, comp_rs;  // bytes
+  const unsigned char* csc;  // fp4 rows: E4M3 scales, one per 16 elements
+  int64_t csc_bs, csc_rs;
   const float* sink;
   const int32_t* idx;
   int L;
@@ -69,6 +74,10 @@ __device__ __forceinline__ void h_dma16(const void* sbase, uint32_t voff, const 
                "{m0}"((uint32_t)(uintptr_t)lds_base));
 }
 
+__device__ __forceinline__ void h_dma16_v(const void* gptr, const DSA_LDS void* lds_base) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"((uint32_t)(uintptr_t)lds_base));
+}
+
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -84,11 +93,12 @@ __device__ __forceinline__ void h_scale(f32x4& v, float f) {
   }
 }
 
+template <bool FP4>
 __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a) {
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kHLds];
   unsigned char* ring = smem;
-  unsigned char* masks = smem + kHRing;                                   // [NST][4] bytes
-  uint32_t* tset = reinterpret_cast<uint32_t*>(masks + kHNST * 4);       // tiles with a valid slot
+  unsigned char* masks = smem + kHRing;                                   // [NST][2][4] bytes
+  uint32_t* tset = reinterpret_cast<uint32_t*>(masks + kHNST * 8);       // tiles with a valid slot
   int* idx_lds = reinterpret_cast<int*>(smem + kHRing + kHMasks + 12);  // 16-byte aligned
 
   const int tid = threadIdx.x;
@@ -105,6 +115,7 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
 
   const unsigned char* win_b = a.win + (int64_t)b * a.win_bs;
   const unsigned char* comp_b = a.comp + (int64_t)b * a.comp_bs;
+  const unsigned char* csc_b = FP4 ? a.csc + (int64_t)b * a.csc_bs : nullptr;
   const int* irow = a.idx + (int64_t)qi * L;
   const int win_n = (int)a.win_n;
   const void* win_u = uniform_ptr(win_b);
@@ -139,7 +150,7 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
     else if (iv < win_n)
       code = (uint32_t)iv * (uint32_t)a.win_rs;
     else
-      code = (uint32_t)(iv - win_n) * (uint32_t)a.comp_rs | 1u;
+      code = FP4 ? ((uint32_t)(iv - win_n) << 4) | 1u : (uint32_t)(iv - win_n) * (uint32_t)a.comp_rs | 1u;
     idx_lds[i] = (int)code;
   }
   __syncthreads();
@@ -155,20 +166,61 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
   const int nt = __builtin_popcount(pend);
 
   // copies of this wave's 8 rows of position k (one wave instruction per row; an empty slot
-  // copies the zero row) and the tile's valid-row byte
+  // copies the zero row; an fp4 row copies its 256 nibble bytes and 32 scale bytes into the tail
+  // of its pitch) and the tile's valid-row and fp4-row bytes
+  // slot codes: byte offset of the row from its base, bit 0 = compressed row, bit 1 = empty slot
+  // (the zero row); for an fp4 compressed row the offset field holds the row number
   auto issue = [&](int k) {
     const int tile = __builtin_ctz(pend);
     pend &= pend - 1u;
     const int myidx = idx_lds[tile * kHTile + 8 * wave + (lane & 7)];
     const int slot = k % kHNST;
     const uint32_t vbits = (uint32_t)__builtin_amdgcn_ballot_w64(lane < 8 && !(myidx & 2));
-    if (lane == 0) masks[slot * 4 + wave] = (unsigned char)vbits;
+    const uint32_t fbits = FP4 ? (uint32_t)__builtin_amdgcn_ballot_w64(lane < 8 && (myidx & 1)) : 0u;
+    if (lane == 0) {
+      masks[slot * 8 + wave] = (unsigned char)vbits;
+      masks[slot * 8 + 4 + wave] = (unsigned char)fbits;
+    }
     unsigned char* tb = ring + slot * kHTileB;
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const uint32_t x = (uint32_t)__builtin_amdgcn_readlane(myidx, r);
-      h_dma16(slot_base(x, win_u, comp_u, zero_u), (uint32_t)lane * 16u + (x & ~15u),
-              (DSA_LDS void*)(tb + h_row(8 * wave + r)));
+      if (FP4 && (x & 1u)) {
+        const int64_t cr = x >> 4;
+        const unsigned char* src =
+            lane < 16 ? comp_b + cr * a.comp_rs + lane * 16 : csc_b + cr * a.csc_rs + (lane - 16) * 16;
+        if (lane < 18) h_dma16_v(src, (DSA_LDS void*)(tb + h_row(8 * wave + r) + kHRaw));
+      } else {
+        h_dma16(slot_base(x, win_u, comp_u, zero_u), (uint32_t)lane * 16u + (x & ~15u),
+                (DSA_LDS void*)(tb + h_row(8 * wave + r)));
+      }
+    }
+  };
+  // fp4 rows of position k that this wave copied, decoded in place (it has waited for its own
+  // copies; the next barrier publishes them): lane l writes elements 8l..8l+7 from nibble bytes
+  // 4l..4l+3 and scale byte l/2; a row's reads all complete before its write (one wave, in order)
+  auto decode = [&](int k) {
+    if constexpr (FP4) {
+      const int slot = k % kHNST;
+      const uint32_t fb = __builtin_amdgcn_readfirstlane(masks[slot * 8 + 4 + wave]);
+      unsigned char* tb = ring + slot * kHTileB;
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        if ((fb >> r) & 1u) {
+          unsigned char* row = tb + h_row(8 * wave + r);
+          const uint32_t word = *reinterpret_cast<const uint32_t*>(row + kHRaw + 4 * lane);
+          const uint32_t scb = row[kHRaw + 256 + (lane >> 1)];
+          const float sc = __builtin_amdgcn_cvt_f32_fp8((int)scb, 0);
+          // e2m1 pairs at unit scale (exact), times the E4M3 scale: exact in f32 and in bf16
+          const f32x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0);
+          const f32x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1);
+          const f32x2 e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2);
+          const f32x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3);
+          auto pk = [&](f32x2 e) { return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)(e[0] * sc), (__bf16)(e[1] * sc)}); };
+          const u32x4 v = {pk(e0), pk(e1), pk(e2), pk(e3)};
+          *reinterpret_cast<u32x4*>(row + 16 * lane) = v;
+        }
+      }
     }
   };
 #pragma unroll
@@ -198,19 +250,29 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
   for (int d = 0; d < 32; ++d) acc[d] = f32x4{};
   float m_run = kHMinit;
   float l_run = 0.f;
-  auto tile_vmask = [&](int k) { return *reinterpret_cast<const uint32_t*>(masks + (k % kHNST) * 4); };
+  auto tile_vmask = [&](int k) { return *reinterpret_cast<const uint32_t*>(masks + (k % kHNST) * 8); };
 
   // logits of the current position as four chains (summed when first used)
   f32x4 ch[4] = {};
   uint32_t vm = 0u;
   if (nt > 0) {
-    const int later0 = min(kHNST - 2, nt - 1);
-    if (later0 >= 2)
-      wait_vmcnt<16>();
-    else if (later0 == 1)
-      wait_vmcnt<8>();
-    else
-      wait_vmcnt<0>();
+    if constexpr (FP4) {
+      // positions 0 and 1 landed (own copies) and decoded before the first QK
+      if (nt > 2)
+        wait_vmcnt<8>();
+      else
+        wait_vmcnt<0>();
+      decode(0);
+      if (nt > 1) decode(1);
+    } else {
+      const int later0 = min(kHNST - 2, nt - 1);
+      if (later0 >= 2)
+        wait_vmcnt<16>();
+      else if (later0 == 1)
+        wait_vmcnt<8>();
+      else
+        wait_vmcnt<0>();
+    }
     __syncthreads();
     const unsigned char* kp = ring + k_base;
 #pragma unroll
@@ -312,6 +374,17 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
 #pragma unroll
     for (int j = 0; j < 4; ++j) ch[j] = cn[j];
     vm = vm_next;
+    if constexpr (FP4) {
+      // position k+2: its copies (own) landed once at most those of k+3 are out; decoded here so
+      // the next iteration's barrier publishes it before its QK
+      if (k + 2 < nt) {
+        if (k + 3 < nt)
+          wait_vmcnt<8>();
+        else
+          wait_vmcnt<0>();
+        decode(k + 2);
+      }
+    }
   }
   wait_vmcnt<0>();
 
@@ -333,15 +406,16 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
 
 }  // namespace
 
-// Launches the kernel when it applies (bf16 rows, head_dim 512, at most 64 heads, index rows of
-// at most 1024 slots, enough queries to fill the GPU, 16-byte aligned rows, row offsets within
-// 32 bits, positive scale); returns 1 if launched, 0 if not, <0 on error.
+// Launches the kernel when it applies (bf16 window rows, bf16 or fp4 compressed rows, head_dim 512,
+// at most 64 heads, index rows of at most 1024 slots, enough queries to fill the GPU, 16-byte
+// aligned rows and scale rows, row offsets within 32 bits, positive scale); returns 1 if
+// launched, 0 if not, <0 on error.
 int sparse_attn_prefill_h16_launch(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
                                    const int32_t* idx, int L, float scale, void* o, int B, int S, int H, int D,
                                    hipStream_t st) {
   const int Q = B * S;
   if (D != kHD || H > 64 || L > kHMaxSlots || Q < 256) return 0;
-  if (comp && comp->rows && comp->format != DSA_KV_DENSE) return 0;
+  const bool fp4 = comp && comp->rows && comp->format == DSA_KV_FP4_E4M3_G16;
   H16Args a{};
   a.q = (const __bf16*)q;
   a.win = (const unsigned char*)win->rows;
@@ -350,16 +424,23 @@ int sparse_attn_prefill_h16_launch(const void* q, const dsa_kv_src* win, const d
   a.win_rs = win->row_stride * 2;
   if (comp && comp->rows) {
     a.comp = (const unsigned char*)comp->rows;
-    a.comp_bs = comp->batch_stride * 2;
-    a.comp_rs = comp->row_stride * 2;
+    a.comp_bs = fp4 ? comp->batch_stride : comp->batch_stride * 2;
+    a.comp_rs = fp4 ? comp->row_stride : comp->row_stride * 2;
+    a.csc = comp->scales;
+    a.csc_bs = comp->scale_batch_stride;
+    a.csc_rs = comp->scale_row_stride;
   }
+  // the copies move 16-byte pieces: every row (and fp4 scale row) must start 16-byte aligned
   auto misaligned = [](const void* p, int64_t rs, int64_t bs) {
     return (((uintptr_t)p) & 15) != 0 || (rs & 15) != 0 || (bs & 15) != 0;
   };
   if (misaligned(a.win, a.win_rs, a.win_bs)) return 0;
   if (a.comp && misaligned(a.comp, a.comp_rs, a.comp_bs)) return 0;
+  if (fp4 && misaligned(a.csc, a.csc_rs, a.csc_bs)) return 0;
+  // slot codes hold row byte offsets (fp4: row numbers) in 32 bits; the softmax folds a positive
+  // scale into exp2
   if (!(scale > 0.f) || (uint64_t)a.win_n * (uint64_t)a.win_rs >= (1ull << 31)) return 0;
-  if (a.comp && (uint64_t)comp->n_rows * (uint64_t)a.comp_rs >= (1ull << 31)) return 0;
+  if (a.comp && (uint64_t)comp->n_rows * (uint64_t)(fp4 ? 16 : a.comp_rs) >= (1ull << 31)) return 0;
   a.sink = sink;
   a.idx = idx;
   a.L = L;
@@ -367,7 +448,10 @@ int sparse_attn_prefill_h16_launch(const void* q, const dsa_kv_src* win, const d
   a.o = (__bf16*)o;
   a.S = S;
   a.H = H;
-  hipLaunchKernelGGL(sparse_attn_prefill_h16_kernel, dim3(Q), dim3(256), 0, st, a);
+  if (fp4)
+    hipLaunchKernelGGL(sparse_attn_prefill_h16_kernel<true>, dim3(Q), dim3(256), 0, st, a);
+  else
+    hipLaunchKernelGGL(sparse_attn_prefill_h16_kernel<false>, dim3(Q), dim3(256), 0, st, a);
   const int rc = check_launch("sparse_attn_prefill_h16");
   return rc ? rc : 1;
 }
