@@ -256,10 +256,16 @@ topk_wave_kernel(const float* __restrict__ scores, int rows, int S, int T, int K
       *reinterpret_cast<int4*>(hist + 4 * lane) = int4{0, 0, 0, 0};
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
+      // constant trip counts (an early exit would stop the full unroll and push key[] out to
+      // scratch memory); invisible keys are 0, which no score maps to; one wave-uniform check per
+      // 16 groups skips the groups past the last visible position
 #pragma unroll
-      for (int g = 0; g < KPL; ++g) {
-        if (g >= ng) break;  // wave-uniform
-        if (64 * g + lane < c && (key[g] & mask) == prefix) atomicAdd(&hist[(key[g] & dmask) >> lo], 1);
+      for (int g0 = 0; g0 < KPL; g0 += 16) {
+        if (g0 < ng) {
+#pragma unroll
+          for (int g = g0; g < g0 + 16 && g < KPL; ++g)
+            if (key[g] != 0u && (key[g] & mask) == prefix) atomicAdd(&hist[(key[g] & dmask) >> lo], 1);
+        }
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       __builtin_amdgcn_wave_barrier();
@@ -306,7 +312,6 @@ topk_wave_kernel(const float* __restrict__ scores, int rows, int S, int T, int K
   int base = 0, eq_seen = 0;
 #pragma unroll
   for (int g = 0; g < KPL; ++g) {
-    if (g >= ng) break;  // wave-uniform
     const uint64_t eqb = __builtin_amdgcn_ballot_w64(key[g] == tau);
     const int rank = eq_seen + __builtin_amdgcn_mbcnt_hi((uint32_t)(eqb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)eqb, 0));
     eq_seen += __builtin_popcountll(eqb);
