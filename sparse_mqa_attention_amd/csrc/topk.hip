@@ -222,12 +222,23 @@ topk_wave_kernel(const float* __restrict__ scores, int rows, int S, int T, int K
   const float* srow = scores + (int64_t)row * T;
   uint32_t key[KPL];
   // all loads first, then branch-free keys (a branch per element would make the compiler wait
-  // for each load before issuing the next).  Positions past c are read but never used; the
-  // launcher keeps every read inside the scores buffer (rows whose 64*KPL positions would run
-  // past its end go to the per-row workgroup kernel).
+  // for each load before issuing the next).  The launcher keeps every read inside the scores
+  // buffer (rows whose 64*KPL positions would run past its end go to the per-row workgroup
+  // kernel).
   const float* lrow = srow + lane;
+  const int ng = (c + 63) / 64;  // groups holding a visible position
+  // groups past the last visible position are not read (one wave-uniform check per 16 groups;
+  // their keys are masked to 0 below either way)
 #pragma unroll
-  for (int g = 0; g < KPL; ++g) key[g] = __float_as_uint(lrow[64 * g]);
+  for (int g0 = 0; g0 < KPL; g0 += 16) {
+    if (g0 < ng) {
+#pragma unroll
+      for (int g = g0; g < g0 + 16 && g < KPL; ++g) key[g] = __float_as_uint(lrow[64 * g]);
+    } else {
+#pragma unroll
+      for (int g = g0; g < g0 + 16 && g < KPL; ++g) key[g] = 0u;
+    }
+  }
   uint32_t kand = 0xFFFFFFFFu, kor = 0u;
 #pragma unroll
   for (int g = 0; g < KPL; ++g) {
@@ -246,7 +257,6 @@ topk_wave_kernel(const float* __restrict__ scores, int rows, int S, int T, int K
   uint32_t prefix = kand & ~diff;
   uint32_t mask = ~diff;
   int remaining = K;
-  const int ng = (c + 63) / 64;  // groups holding a visible position
   if (diff != 0u) {
     int hb = 31 - __builtin_clz(diff);
     while (true) {
