@@ -39,7 +39,8 @@ constexpr float kHMinit = -1.0e30f;
 constexpr int kHRing = kHNST * kHTileB;
 constexpr int kHMasks = kHNST * 8 + 4;  // per slot: valid rows, fp4 rows (a byte per wave each); tile set
 constexpr int kHRaw = kHPitch - 288;    // an fp4 row lands raw in the last 288 bytes of its pitch
-constexpr int kHLds = kHRing + kHMasks + 12 + kHMaxSlots * 4;
+constexpr int kHDummy = 1024;  // write target of the decode for rows that are not fp4
+constexpr int kHLds = kHRing + kHMasks + 12 + kHMaxSlots * 4 + kHDummy;
 static_assert(kHLds <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ int h_row(int r) { return kHPitch * r; }
@@ -100,6 +101,7 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
   unsigned char* masks = smem + kHRing;                                   // [NST][2][4] bytes
   uint32_t* tset = reinterpret_cast<uint32_t*>(masks + kHNST * 8);       // tiles with a valid slot
   int* idx_lds = reinterpret_cast<int*>(smem + kHRing + kHMasks + 12);  // 16-byte aligned
+  unsigned char* dummy = smem + kHRing + kHMasks + 12 + kHMaxSlots * 4;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -198,27 +200,33 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
   };
   // fp4 rows of position k that this wave copied, decoded in place (it has waited for its own
   // copies; the next barrier publishes them): lane l writes elements 8l..8l+7 from nibble bytes
-  // 4l..4l+3 and scale byte l/2; a row's reads all complete before its write (one wave, in order)
+  // 4l..4l+3 and scale byte l/2; a row's reads all complete before its write (one wave, in order).
+  // All 8 rows go through the same instructions (a row that is not fp4 writes to a dummy area), so
+  // the reads of every row are issued before the first conversion.
   auto decode = [&](int k) {
     if constexpr (FP4) {
       const int slot = k % kHNST;
       const uint32_t fb = __builtin_amdgcn_readfirstlane(masks[slot * 8 + 4 + wave]);
-      unsigned char* tb = ring + slot * kHTileB;
+      if (fb != 0u) {
+        unsigned char* tb = ring + slot * kHTileB + h_row(8 * wave);
+        uint32_t word[8], scb[8];
 #pragma unroll
-      for (int r = 0; r < 8; ++r) {
-        if ((fb >> r) & 1u) {
-          unsigned char* row = tb + h_row(8 * wave + r);
-          const uint32_t word = *reinterpret_cast<const uint32_t*>(row + kHRaw + 4 * lane);
-          const uint32_t scb = row[kHRaw + 256 + (lane >> 1)];
-          const float sc = __builtin_amdgcn_cvt_f32_fp8((int)scb, 0);
+        for (int r = 0; r < 8; ++r) {
+          word[r] = *reinterpret_cast<const uint32_t*>(tb + h_row(r) + kHRaw + 4 * lane);
+          scb[r] = tb[h_row(r) + kHRaw + 256 + (lane >> 1)];
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+          const float sc = __builtin_amdgcn_cvt_f32_fp8((int)scb[r], 0);
           // e2m1 pairs at unit scale (exact), times the E4M3 scale: exact in f32 and in bf16
-          const f32x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0);
-          const f32x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1);
-          const f32x2 e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2);
-          const f32x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3);
+          const f32x2 e0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word[r], 1.0f, 0);
+          const f32x2 e1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word[r], 1.0f, 1);
+          const f32x2 e2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word[r], 1.0f, 2);
+          const f32x2 e3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word[r], 1.0f, 3);
           auto pk = [&](f32x2 e) { return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)(e[0] * sc), (__bf16)(e[1] * sc)}); };
           const u32x4 v = {pk(e0), pk(e1), pk(e2), pk(e3)};
-          *reinterpret_cast<u32x4*>(row + 16 * lane) = v;
+          unsigned char* dst = ((fb >> r) & 1u) ? tb + h_row(r) : dummy;
+          *reinterpret_cast<u32x4*>(dst + 16 * lane) = v;
         }
       }
     }
