@@ -118,22 +118,25 @@ index_scores_prefill_kernel(const __bf16* __restrict__ q_idx, const __bf16* __re
     for (int s = 0; s < kXKS; ++s)
       kop[s] = *reinterpret_cast<const bf16x8*>(tile + kop_row + (((2 * s + hf) ^ kop_swz) << 4));
     const int j = i * kXKT + c;
+    // both queries in four independent chains (even and odd k-steps of each), so the matrix core
+    // never waits on a dependent accumulator; a query that sees nothing of the tile (at most its
+    // last one) is still multiplied and only its stores differ
+    f32x16 acc[2][2] = {};
+#pragma unroll
+    for (int s = 0; s < kXKS; s += 2) {
+#pragma unroll
+      for (int m = 0; m < 2; ++m) acc[m][0] = mfma32(qa[m][s], kop[s], acc[m][0]);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) acc[m][1] = mfma32(qa[m][s + 1], kop[s + 1], acc[m][1]);
+    }
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      if (!live[m]) continue;
-      float* out_row = scores + ((int64_t)b * S + t0 + 2 * wave + m) * T;
-      if (i * kXKT >= ct[m]) {  // nothing visible to this query in the tile
-        if (hf == 0 && j < T) out_row[j] = ninf;
-        continue;
-      }
-      f32x16 acc = {};
-#pragma unroll
-      for (int s = 0; s < kXKS; ++s) acc = mfma32(qa[m][s], kop[s], acc);
       float sum = 0.f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sum += fmaxf(acc[e], 0.f) * wv[m][e];
+      for (int e = 0; e < 16; ++e) sum += fmaxf(acc[m][0][e] + acc[m][1][e], 0.f) * wv[m][e];
       sum += shfl_xor(sum, 32);
-      if (hf == 0 && j < T) out_row[j] = j < ct[m] ? w_scale * sum : ninf;
+      float* out_row = scores + ((int64_t)b * S + t0 + 2 * wave + m) * T;
+      if (live[m] && hf == 0 && j < T) out_row[j] = j < ct[m] ? w_scale * sum : ninf;
     }
   }
 
