@@ -7,8 +7,8 @@
 // must be reused across many tiles of the other operand, so:
 //  * one workgroup owns 8 queries (2 per wave); their index heads stay in AGPRs as the MFMA A
 //    operand for the whole kernel (32 heads x 128 dims per query = 8 k-steps of 16);
-//  * the visible keys of the block stream through an LDS ring of 32-key tiles filled by direct
-//    global->LDS copies (keys are contiguous rows, so a tile is one 8 KiB coalesced read); the
+//  * the visible keys of the block stream through an LDS ring of 64-key tiles filled by direct
+//    global->LDS copies (keys are contiguous rows, so a tile is one 16 KiB coalesced read); the
 //    16-byte chunks of key row r are XOR-swizzled by r, so the B-operand reads (16 rows at one
 //    chunk) touch every bank group once;
 //  * v_mfma_f32_32x32x16_bf16 with heads as M and keys as N: the accumulator of lane (hf, c)
@@ -25,9 +25,9 @@ namespace {
 constexpr int kXDI = 128;                // index head dim of this kernel
 constexpr int kXKS = kXDI / 16;          // MFMA k-steps
 constexpr int kXQ = 8;                   // queries per workgroup
-constexpr int kXKT = 32;                 // keys per tile
+constexpr int kXKT = 64;                 // keys per tile (two MFMA key blocks)
 constexpr int kXRowB = kXDI * 2;         // bytes of one key row
-constexpr int kXTileB = kXKT * kXRowB;   // 8 KiB
+constexpr int kXTileB = kXKT * kXRowB;   // 16 KiB
 constexpr int kXNST = 4;                 // ring stages
 
 __global__ void __launch_bounds__(256, 2)
@@ -52,14 +52,14 @@ index_scores_prefill_kernel(const __bf16* __restrict__ q_idx, const __bf16* __re
 
   const __bf16* kb = k_idx + (int64_t)b * k_bstride;
 
-  // Copies of key tile i into ring slot i % NST: two wave instructions of 4 key rows each; lane l
-  // fills physical chunk l & 15 of row 4u + l/16, which holds logical chunk (l & 15) ^ (row & 15).
+  // Copies of key tile i into ring slot i % NST: four wave instructions of 4 key rows each; lane l
+  // fills physical chunk l & 15 of row 4 blk + l/16, which holds logical chunk (l & 15) ^ (row & 15).
   // Rows past T re-read row T-1 (in bounds; never scored).
   auto issue = [&](int i) {
     unsigned char* tile = ring + (i % kXNST) * kXTileB;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int blk = 2 * wave + u;
+    for (int u = 0; u < 4; ++u) {
+      const int blk = 4 * wave + u;
       const int r = 4 * blk + (lane >> 4);
       const int j = min(i * kXKT + r, T - 1);
       const int chunk = (lane & 15) ^ (r & 15);
@@ -104,43 +104,46 @@ index_scores_prefill_kernel(const __bf16* __restrict__ q_idx, const __bf16* __re
   for (int i = 0; i < ntl; ++i) {
     const int later = min(kXNST - 2, ntl - 1 - i);
     if (later >= 2)
-      wait_vmcnt<4>();
+      wait_vmcnt<8>();
     else if (later == 1)
-      wait_vmcnt<2>();
+      wait_vmcnt<4>();
     else
       wait_vmcnt<0>();
     __syncthreads();  // tile i is complete; every wave is past tile i-1, whose slot is refilled
     if (i + kXNST - 1 < ntl) issue(i + kXNST - 1);
 
     const unsigned char* tile = ring + (i % kXNST) * kXTileB;
-    bf16x8 kop[kXKS];
 #pragma unroll
-    for (int s = 0; s < kXKS; ++s)
-      kop[s] = *reinterpret_cast<const bf16x8*>(tile + kop_row + (((2 * s + hf) ^ kop_swz) << 4));
-    const int j = i * kXKT + c;
-    // both queries in four independent chains (even and odd k-steps of each), so the matrix core
-    // never waits on a dependent accumulator; a query that sees nothing of the tile (at most its
-    // last one) is still multiplied and only its stores differ
-    f32x16 acc[2][2] = {};
+    for (int kb = 0; kb < kXKT / 32; ++kb) {
+      bf16x8 kop[kXKS];
 #pragma unroll
-    for (int s = 0; s < kXKS; s += 2) {
+      for (int s = 0; s < kXKS; ++s)
+        kop[s] = *reinterpret_cast<const bf16x8*>(tile + kb * 32 * kXRowB + kop_row + (((2 * s + hf) ^ kop_swz) << 4));
+      const int j = i * kXKT + 32 * kb + c;
+      // both queries in four independent chains (even and odd k-steps of each), so the matrix
+      // core never waits on a dependent accumulator; a query that sees nothing of the block (at
+      // most its last ones) is still multiplied and only its stores differ
+      f32x16 acc[2][2] = {};
 #pragma unroll
-      for (int m = 0; m < 2; ++m) acc[m][0] = mfma32(qa[m][s], kop[s], acc[m][0]);
+      for (int s = 0; s < kXKS; s += 2) {
 #pragma unroll
-      for (int m = 0; m < 2; ++m) acc[m][1] = mfma32(qa[m][s + 1], kop[s + 1], acc[m][1]);
-    }
+        for (int m = 0; m < 2; ++m) acc[m][0] = mfma32(qa[m][s], kop[s], acc[m][0]);
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      float sum = 0.f;
+        for (int m = 0; m < 2; ++m) acc[m][1] = mfma32(qa[m][s + 1], kop[s + 1], acc[m][1]);
+      }
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sum += fmaxf(acc[m][0][e] + acc[m][1][e], 0.f) * wv[m][e];
-      sum += shfl_xor(sum, 32);
-      float* out_row = scores + ((int64_t)b * S + t0 + 2 * wave + m) * T;
-      if (live[m] && hf == 0 && j < T) out_row[j] = j < ct[m] ? w_scale * sum : ninf;
+      for (int m = 0; m < 2; ++m) {
+        float sum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) sum += fmaxf(acc[m][0][e] + acc[m][1][e], 0.f) * wv[m][e];
+        sum += shfl_xor(sum, 32);
+        float* out_row = scores + ((int64_t)b * S + t0 + 2 * wave + m) * T;
+        if (live[m] && hf == 0 && j < T) out_row[j] = j < ct[m] ? w_scale * sum : ninf;
+      }
     }
   }
 
-  // invisible tail of each score row: [ntl * 32, T)
+  // invisible tail of each score row: [ntl * 64, T)
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     if (!live[m]) continue;
