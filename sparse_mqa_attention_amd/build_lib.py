@@ -16,9 +16,11 @@ ARCH = "gfx950"
 # packed fp32 VALU forms are kept out of the generated code
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
              "-packed-fp32-ops", "-Wall", "-Wno-unused-result"]
-# per-source additions: the prefill attention kernel keeps its MFMA accumulators in VGPRs (its
-# softmax rescales them with VALU ops, and AGPR accumulators would be copied out every tile)
-EXTRA_FLAGS = {"sparse_attn_prefill_h16.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+# per-source additions: kernels whose MFMA accumulators feed VALU work every tile keep them in
+# VGPRs (the prefill attention rescales them; the prefill index epilogue rectifies and weights
+# them), since AGPR accumulators would be copied out first
+EXTRA_FLAGS = {"sparse_attn_prefill_h16.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
+               "index_scores_prefill.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:
