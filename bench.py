@@ -1,14 +1,14 @@
 """Benchmark of the sparse MQA attention step on one MI355X.
 
 A step is one pass of the whole path over one batch of synthetic input: index scores, then the
-index rows (window rows and top-k selection, one launch) and sparse attention (every stage a
-libdsa kernel).  Inputs are
-resident in HBM before timing starts; several input sets are rotated so that the 256 MB
+index rows (window rows and top-k selection) and sparse attention through dsa_sparse_attn_select,
+which is one kernel for decode batches and two otherwise (every stage a libdsa kernel).  Inputs
+are resident in HBM before timing starts; several input sets are rotated so that the 256 MB
 Infinity Cache cannot serve one step from the previous one.
 
-Prints one JSON line (see `--help`).  The roofline object covers the dominant kernel, the sparse
-attention call, timed with HIP events on the stream it runs on; the CPU baseline is the oracle
-timed on a bounded sample on the host.
+Prints one JSON line (see `--help`).  The roofline object covers the dominant kernel (the decode
+kernel that selects and attends, or the sparse attention kernel), timed with HIP events on the
+stream it runs on; the CPU baseline is the oracle timed on a bounded sample on the host.
 """
 from __future__ import annotations
 
@@ -28,7 +28,8 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 ROTATE_BYTES = 768 << 20  # rotate input sets until they span more than the Infinity Cache (256 MB)
 KERNEL_SOURCES = ["sparse_mqa_attention_amd/csrc/sparse_attn.hip", "sparse_mqa_attention_amd/csrc/sparse_attn_decode.hip",
-                  "sparse_mqa_attention_amd/csrc/sparse_attn_prefill_h16.hip", "sparse_mqa_attention_amd/csrc/dsa_internal.h"]
+                  "sparse_mqa_attention_amd/csrc/sparse_attn_prefill_h16.hip", "sparse_mqa_attention_amd/csrc/dsa_internal.h",
+                  "sparse_mqa_attention_amd/csrc/topk_block.h"]
 
 
 def _args():
@@ -158,9 +159,25 @@ def main():
     stream = torch.cuda.current_stream(dev)
     comp_key = "kv_comp_fp4" if w.comp_fmt == "fp4" else "kv_comp"
 
-    def stage_select(i):
+    # Decode batches the two-phase decode kernel takes select their index rows inside it (one
+    # launch for top-k, window rows and attention); elsewhere the select and the attention are
+    # two launches.  The step calls the same entry point either way.
+    fused = (w.mode == "decode" and w.dtype == "bf16" and w.comp_fmt != "fp4" and w.T <= 2048 and w.D == 512
+             and w.H == 64 and w.B * w.S < 256)
+
+    def stage_index(i):
         s, bf = sets[i % n_sets], bufs[i % n_sets]
         dsa.dsa_index_scores(s["qI"], s["kI"], s["w"], w_scale, w.start_pos, w.ratio, out=bf["scores"])
+
+    def stage_select_attn(i):
+        s, bf = sets[i % n_sets], bufs[i % n_sets]
+        dsa.dsa_sparse_attn_select(bf["scores"], s["q"], s["kv_win"], s[comp_key], s["sink"],
+                                   index_topk=w.index_topk, start_pos=w.start_pos, ratio=w.ratio, W=w.W,
+                                   scale=scale, comp_scales=s.get("kv_comp_scale"), out=bf["o"], idx=bf["idx"],
+                                   workspace=bf["workspace"])
+
+    def stage_select(i):
+        s, bf = sets[i % n_sets], bufs[i % n_sets]
         dsa.dsa_select(bf["scores"], w.index_topk, w.start_pos, w.ratio, w.W, w.n_win, out=bf["idx"])
 
     def stage_attn(i):
@@ -169,8 +186,18 @@ def main():
                             comp_scales=s.get("kv_comp_scale"), out=bf["o"], workspace=bf["workspace"])
 
     def step(i):
-        stage_select(i)
-        stage_attn(i)
+        stage_index(i)
+        stage_select_attn(i)
+
+    # the dominant kernel and the rest of the step, timed apart
+    if fused:
+        dominant, rest = stage_select_attn, stage_index
+    else:
+        dominant = stage_attn
+
+        def rest(i):
+            stage_index(i)
+            stage_select(i)
 
     # Steps are captured into HIP graphs of G consecutive steps (rotating input sets), so the
     # timed region measures the GPU, not the host's launch rate.
@@ -209,8 +236,8 @@ def main():
 
     # the dominant kernel alone: R launches back to back in one graph, bracketed by HIP events
     R = 20
-    attn_graph = capture(stage_attn, 0, R)
-    sel_graph = capture(stage_select, 0, R)
+    attn_graph = capture(dominant, 0, R)
+    sel_graph = capture(rest, 0, R)
     attn_graph.replay()
     torch.cuda.synchronize()
     e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
@@ -222,8 +249,13 @@ def main():
     torch.cuda.synchronize()
     attn_avg_ms = e0.elapsed_time(e1) / R
     sel_avg_ms = e1.elapsed_time(e2) / R
-    print(f"[bench] {w.name}: step {ms_per_step * 1e3:.2f} us (wall {wall / a.steps * 1e6:.2f} us), "
-          f"attention {attn_avg_ms * 1e3:.2f} us, window+index+top-k {sel_avg_ms * 1e3:.2f} us", file=sys.stderr)
+    if fused:
+        parts = (f"window+top-k+attention (one kernel) {attn_avg_ms * 1e3:.2f} us, "
+                 f"index scores {sel_avg_ms * 1e3:.2f} us")
+    else:
+        parts = f"attention {attn_avg_ms * 1e3:.2f} us, window+index+top-k {sel_avg_ms * 1e3:.2f} us"
+    print(f"[bench] {w.name}: step {ms_per_step * 1e3:.2f} us (wall {wall / a.steps * 1e6:.2f} us), {parts}",
+          file=sys.stderr)
 
     # algorithmic work of one sparse-attention launch: every valid slot's row once, q, o, idx, sink
     idx_all = torch.stack([bufs[i % n_sets]["idx"] for i in range(n_sets)])
@@ -238,6 +270,8 @@ def main():
     else:
         row_bytes = valid_per_set * w.D * esz
     alg_bytes = 2 * q_bytes + w.B * w.S * w.L * 4 + w.H * 4 + row_bytes
+    if fused:
+        alg_bytes += w.B * w.S * w.T * 4  # the kernel also reads each query's scores once
     alg_flops = 4.0 * w.H * w.D * valid_per_set
     if w.mode == "decode":
         achieved = alg_bytes / (attn_avg_ms * 1e-3) / 1e9
@@ -251,8 +285,11 @@ def main():
         per_launch = alg_flops
     sha = kernel_src_sha()
     roof["traffic"] = _traffic(w.name, sha)
-    roof["kernel"] = "dsa_sparse_attn" + (" (gather-attention + split combine)" if
-                                          dsa.dsa_sparse_attn_workspace_size(1, w.B, w.S, w.H, w.D, w.L) else "")
+    if fused:
+        roof["kernel"] = "dsa_sparse_attn_select (index rows + gather-attention + split combine, one kernel)"
+    else:
+        roof["kernel"] = "dsa_sparse_attn" + (" (gather-attention + split combine)" if
+                                              dsa.dsa_sparse_attn_workspace_size(1, w.B, w.S, w.H, w.D, w.L) else "")
     roof["avg_launch_us"] = round(attn_avg_ms * 1e3, 2)
     roof["algorithmic_per_launch"] = per_launch
 

@@ -9,6 +9,8 @@
  *   dsa_window_idx    the sliding-window part of each query's index row
  *   dsa_select        window part and top-k part of the index rows in one launch
  *   dsa_sparse_attn   attend all heads over the rows an index row names
+ *   dsa_sparse_attn_select  dsa_select then dsa_sparse_attn, one launch where the decode
+ *                     attention kernel can select its own index rows
  *
  * Citations refer to the DeepSeek V4.1 model pages ("attention/attend/selected",
  * "reindex-layer/read-weights") by the class or function that holds the step.
@@ -195,6 +197,30 @@ int dsa_sparse_attn(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp
 
 /* Bytes of workspace dsa_sparse_attn needs for this shape (0 when none). */
 size_t dsa_sparse_attn_workspace_size(int dtype, int B, int S, int H, int D, int L);
+
+/*
+ * The index rows and the attention over them (`Indexer.forward`, `get_window_topk_idxs` and
+ * `sparse_attn` as `Attention.forward` chains them): the same results as
+ *
+ *   dsa_select(scores, B, S, T, index_topk, start_pos, ratio, W, win->n_rows, idx, L, stream)
+ *   dsa_sparse_attn(q, win, comp, sink, idx, L, scale, o, dtype, B, S, H, D, workspace, ...)
+ *
+ * with L = dsa_window_cols(S, start_pos, W) + min(index_topk, T).  For decode batches that the
+ * two-phase decode attention kernel takes (bf16, D = 512, H = 64, dense rows, fewer than 256
+ * queries, T <= 2048) it is one launch: every workgroup of a query selects that query's index row
+ * from its scores in the kernel's prologue.  Otherwise it makes the two calls above.
+ *
+ *   scores [B, S, T] float32; q, win, comp, sink, o, workspace as for dsa_sparse_attn, with the
+ *   workspace sized by dsa_sparse_attn_workspace_size(dtype, B, S, H, D, L).
+ *   idx    [B, S, L] int32, contiguous: receives the index rows.  It may be NULL when the one-launch
+ *          path applies (the rows are then not written out); DSA_ERR_NULL when it does not.
+ *
+ * Errors: those of dsa_select and dsa_sparse_attn.
+ */
+int dsa_sparse_attn_select(const float* scores, int T, int index_topk, int start_pos, int ratio, int W,
+                           const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
+                           float scale, void* o, int dtype, int B, int S, int H, int D, int32_t* idx,
+                           void* workspace, size_t workspace_bytes, dsa_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -10,6 +10,7 @@ Calls (same names as the C entry points):
     dsa_topk          the index_topk best visible rows per query
     dsa_window_idx    sliding-window part of each index row
     dsa_sparse_attn   attention with a per-head sink over the indexed rows
+    dsa_sparse_attn_select  the index rows and the attention (one launch for decode batches)
 """
 from __future__ import annotations
 
@@ -65,6 +66,10 @@ def _load():
     lib.dsa_sparse_attn.argtypes = [vp, ctypes.POINTER(DsaKvSrc), ctypes.POINTER(DsaKvSrc), vp, vp, i32, f32, vp,
                                     i32, i32, i32, i32, i32, vp, ctypes.c_size_t, vp]
     lib.dsa_sparse_attn.restype = i32
+    lib.dsa_sparse_attn_select.argtypes = [vp, i32, i32, i32, i32, i32, vp, ctypes.POINTER(DsaKvSrc),
+                                           ctypes.POINTER(DsaKvSrc), vp, f32, vp, i32, i32, i32, i32, i32, vp, vp,
+                                           ctypes.c_size_t, vp]
+    lib.dsa_sparse_attn_select.restype = i32
     lib.dsa_sparse_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.dsa_sparse_attn_workspace_size.restype = ctypes.c_size_t
     return lib
@@ -243,6 +248,40 @@ def dsa_sparse_attn(q, kv_win, kv_comp, sink, idx, scale: float, comp_scales=Non
     return out
 
 
+def dsa_sparse_attn_select(scores, q, kv_win, kv_comp, sink, *, index_topk: int, start_pos: int, ratio: int,
+                           W: int, scale: float, comp_scales=None, out=None, idx=None, workspace=None, stream=None):
+    """Index rows (window + top-k, as dsa_select with offset kv_win.shape[1]) and the sparse attention
+    over them; one launch for decode batches the two-phase decode kernel takes.  Returns (o, idx);
+    idx [B, S, L] int32 receives the rows (allocated when not given)."""
+    dev = _dev(q, kv_win, kv_comp, sink, scores)
+    _need_contig("q", q)
+    _need_contig("scores", scores)
+    B, S, H, D = q.shape
+    T = scores.shape[-1]
+    Wc = dsa_window_cols(S, start_pos, W)
+    L = Wc + min(int(index_topk), T)
+    dt = _dtype_code(q)
+    win = kv_src(kv_win)
+    fp4 = kv_comp is not None and kv_comp.dtype == torch.uint8
+    comp = kv_src(kv_comp, comp_scales, DSA_KV_FP4_E4M3_G16 if fp4 else DSA_KV_DENSE)
+    if out is None:
+        out = torch.empty_like(q)
+    _need_contig("o", out)
+    if idx is None:
+        idx = torch.empty(B, S, L, dtype=torch.int32, device=dev)
+    _need_contig("idx", idx)
+    if idx.dtype != torch.int32 or idx.shape[-1] != L:
+        raise DsaError(-2, "idx must be int32 [B, S, L] with L = window columns + top-k columns")
+    need = dsa_sparse_attn_workspace_size(dt, B, S, H, D, L)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.dsa_sparse_attn_select(_ptr(scores), T, int(index_topk), int(start_pos), int(ratio), int(W), _ptr(q),
+                                      ctypes.byref(win), ctypes.byref(comp), _ptr(sink), float(scale), _ptr(out), dt,
+                                      B, S, H, D, _ptr(idx), _ptr(workspace), wbytes, _stream(dev, stream)))
+    return out, idx
+
+
 def sparse_attention_step(q, kv_win, kv_comp, qI, kI, w, sink, *, start_pos: int, ratio: int, W: int,
                           index_topk: int, scale: float, w_scale: float, comp_scales=None, bufs=None,
                           stream=None):
@@ -261,11 +300,14 @@ def sparse_attention_step(q, kv_win, kv_comp, qI, kI, w, sink, *, start_pos: int
     scores = bufs.get("scores")
     if T > 0:
         scores = dsa_index_scores(qI, kI, w, w_scale, start_pos, ratio, out=scores, stream=stream)
-        dsa_select(scores, index_topk, start_pos, ratio, W, kv_win.shape[1], out=idx, stream=stream)
-    else:
-        dsa_window_idx(idx, start_pos, W, stream=stream)
-    o = dsa_sparse_attn(q, kv_win, kv_comp if T > 0 else None, sink, idx, scale, comp_scales=comp_scales,
-                        out=bufs.get("o"), workspace=bufs.get("workspace"), stream=stream)
+        o, idx = dsa_sparse_attn_select(scores, q, kv_win, kv_comp, sink, index_topk=index_topk,
+                                        start_pos=start_pos, ratio=ratio, W=W, scale=scale,
+                                        comp_scales=comp_scales, out=bufs.get("o"), idx=idx,
+                                        workspace=bufs.get("workspace"), stream=stream)
+        return o, idx, scores
+    dsa_window_idx(idx, start_pos, W, stream=stream)
+    o = dsa_sparse_attn(q, kv_win, None, sink, idx, scale, out=bufs.get("o"), workspace=bufs.get("workspace"),
+                        stream=stream)
     return o, idx, scores
 
 
@@ -278,6 +320,7 @@ __all__ = [
     "dsa_window_cols",
     "dsa_window_idx",
     "dsa_sparse_attn",
+    "dsa_sparse_attn_select",
     "dsa_sparse_attn_workspace_size",
     "kv_src",
     "sparse_attention_step",

@@ -6,6 +6,7 @@
 #include <cstdio>
 
 #include "../../include/dsa.h"
+#include "dsa_internal.h"
 
 namespace dsa {
 
@@ -34,6 +35,8 @@ int sparse_attn_bf16_launch(const void*, const dsa_kv_src*, const dsa_kv_src*, c
 int sparse_attn_f32_launch(const void*, const dsa_kv_src*, const dsa_kv_src*, const float*, const int32_t*, int,
                            float, void*, int, int, int, int, hipStream_t);
 size_t sparse_attn_bf16_workspace(int, int, int, int, int, bool);
+int sparse_attn_bf16_select_launch(const void*, const dsa_kv_src*, const dsa_kv_src*, const float*, const DecSelect*,
+                                   int, float, void*, int, int, int, int, void*, hipStream_t);
 
 }  // namespace dsa
 
@@ -184,6 +187,49 @@ int dsa_sparse_attn(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp
     return dsa::sparse_attn_bf16_launch(q, win, cs, sink, idx, L, scale, o, B, S, H, D, workspace,
                                         (hipStream_t)stream);
   return dsa::sparse_attn_f32_launch(q, win, cs, sink, idx, L, scale, o, B, S, H, D, (hipStream_t)stream);
+}
+
+int dsa_sparse_attn_select(const float* scores, int T, int index_topk, int start_pos, int ratio, int W,
+                           const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
+                           float scale, void* o, int dtype, int B, int S, int H, int D, int32_t* idx,
+                           void* workspace, size_t workspace_bytes, dsa_stream_t stream) {
+  dsa::g_err[0] = 0;
+  if (B < 0 || S < 0 || T < 0 || index_topk < 0 || start_pos < 0 || ratio <= 0)
+    return fail(DSA_ERR_SHAPE, "dsa_sparse_attn_select: bad sizes B=%d S=%d T=%d index_topk=%d start_pos=%d ratio=%d",
+                B, S, T, index_topk, start_pos, ratio);
+  if (!win) return fail(DSA_ERR_NULL, "dsa_sparse_attn_select: window source missing");
+  const int Wc = dsa_window_cols(S, start_pos, W);
+  if (Wc < 0) return Wc;
+  dsa::g_err[0] = 0;
+  const int K = index_topk < T ? index_topk : T;
+  const int L = Wc + K;
+  if (B == 0 || S == 0) return DSA_OK;
+  if (win->n_rows > 0x7FFFFFFF) return fail(DSA_ERR_SHAPE, "dsa_sparse_attn_select: window rows beyond 32-bit indices");
+  const int offset = (int)win->n_rows;
+  if (K > 0 && !scores) return fail(DSA_ERR_NULL, "dsa_sparse_attn_select: NULL scores");
+  // one launch when the decode attention kernel can select the rows itself
+  if (dtype == DSA_BF16 && K > 0 && T <= 2048 && q && sink && o && (((uintptr_t)q | (uintptr_t)o) & 15) == 0 &&
+      win->rows && win->format == DSA_KV_DENSE) {
+    int rc = check_src(win, "window", dtype, D, B, true);
+    if (rc) return rc;
+    rc = check_src(comp, "compressed", dtype, D, B, false);
+    if (rc) return rc;
+    const size_t need = dsa_sparse_attn_workspace_size(dtype, B, S, H, D, L);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+      return fail(DSA_ERR_WORKSPACE, "dsa_sparse_attn_select: workspace of %zu bytes needed, %zu given", need,
+                  workspace_bytes);
+    dsa::DecSelect sel{scores, T, K, start_pos, ratio, W, Wc, offset, idx, (int64_t)L};
+    dsa_kv_src empty{};
+    const dsa_kv_src* cs = (comp && comp->n_rows > 0) ? comp : &empty;
+    rc = dsa::sparse_attn_bf16_select_launch(q, win, cs, sink, &sel, L, scale, o, B, S, H, D, workspace,
+                                             (hipStream_t)stream);
+    if (rc != 0) return rc < 0 ? rc : DSA_OK;
+  }
+  // otherwise: the index rows into idx, then the attention over them
+  if (!idx) return fail(DSA_ERR_NULL, "dsa_sparse_attn_select: idx needed for this shape");
+  int rc = dsa_select(scores, B, S, T, index_topk, start_pos, ratio, W, offset, idx, L, stream);
+  if (rc) return rc;
+  return dsa_sparse_attn(q, win, comp, sink, idx, L, scale, o, dtype, B, S, H, D, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -103,6 +103,16 @@ __device__ __forceinline__ T shfl_xor(T v, int mask) {
   return __shfl_xor(v, mask, 64);
 }
 
+// Index rows selected inside the decode attention kernel: the queries' scores [Q][T], top-k size
+// K, visibility (start_pos, ratio), window W with Wc columns and the top-k offset; idx_out (may
+// be null) receives the rows, ld_out apart.
+struct DecSelect {
+  const float* scores;
+  int T, K, start_pos, ratio, W, Wc, offset;
+  int32_t* idx_out;
+  int64_t ld_out;
+};
+
 __device__ __forceinline__ int visible_rows(int start_pos, int t, int ratio) {
   return (start_pos + t + 1) / ratio;
 }

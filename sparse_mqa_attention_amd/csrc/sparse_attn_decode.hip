@@ -22,7 +22,7 @@
 // Blocks are numbered so that all NS workgroups of a query land on one XCD (dispatch assigns
 // consecutive workgroups to the 8 XCDs round-robin), keeping the rendezvous and the re-gather in
 // one L2.  What crosses HBM is each valid row once, q, o, and the small P (Q x 64 x L bf16).
-#include "dsa_internal.h"
+#include "topk_block.h"
 
 namespace dsa {
 
@@ -56,6 +56,13 @@ struct DecArgs {
   uint32_t* xcc;  // [Q][NS] XCD of each phase-A workgroup
   int S, Q, RPS, Lp, xcd_map;
   int local;  // all workgroups of a query share one XCD (calibrated): P and stats go through its L2
+  // index rows selected in the kernel (instead of read from idx): the query's scores [T], the
+  // top-k size K, visibility (start_pos, ratio), window W with Wc columns, top-k offset; s == 0
+  // writes the row to idx_out when that is set
+  const float* scores;
+  int T, K, start_pos, ratio, W, Wc, offset;
+  int32_t* idx_out;
+  int64_t ld_out;
 };
 
 template <int NS>
@@ -126,7 +133,10 @@ __device__ __forceinline__ uint32_t xcc_id() {
   return v & 0xFu;
 }
 
-template <int NS>
+// SKPT = 0: the index rows come from idx; SKPT > 0: each workgroup selects its query's index row
+// from the scores (window part, then the top-k part, exactly as the top-k kernels do), SKPT scores
+// per thread.
+template <int NS, int SKPT>
 __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
   using C = DecCfg<NS>;
   constexpr int XBUF_FLOATS = 4 * C::TA * 16 * 64;  // per wave, per tile: one partial S^T tile
@@ -135,6 +145,7 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
   __shared__ int idx_lds[C::MAX_L];
   __shared__ float stats_lds[NS * kDH * 2];
   __shared__ int flags[1];  // the rendezvous timed out
+  __shared__ topk_dev::TopkSmem<256> tsm;
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -169,22 +180,51 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
   const int head = 32 * hg + c;
   // the whole index row, once: phase A gathers its part, phase B every slot
   const int win_n = (int)a.win_n;
-  int iv_reg[C::MAX_L / 256];
-#pragma unroll
-  for (int k = 0; k < C::MAX_L / 256; ++k) {
-    const int i = tid + 256 * k;
-    iv_reg[k] = (int)dec_slot_code(i < L ? irow[i] : -1, win_n, (uint32_t)a.win_rs, (uint32_t)a.comp_rs);
-  }
   bf16x8 qreg[kDD / 32];
-  {
-    const __bf16* qp = a.q + ((int64_t)q * kDH + head) * kDD + (kDD / 2) * dh + hf * 8;
+  if constexpr (SKPT == 0) {
+    int iv_reg[C::MAX_L / 256];
 #pragma unroll
-    for (int k = 0; k < kDD / 32; ++k) qreg[k] = *reinterpret_cast<const bf16x8*>(qp + 16 * k);
+    for (int k = 0; k < C::MAX_L / 256; ++k) {
+      const int i = tid + 256 * k;
+      iv_reg[k] = (int)dec_slot_code(i < L ? irow[i] : -1, win_n, (uint32_t)a.win_rs, (uint32_t)a.comp_rs);
+    }
+    {
+      const __bf16* qp = a.q + ((int64_t)q * kDH + head) * kDD + (kDD / 2) * dh + hf * 8;
+#pragma unroll
+      for (int k = 0; k < kDD / 32; ++k) qreg[k] = *reinterpret_cast<const bf16x8*>(qp + 16 * k);
+    }
+#pragma unroll
+    for (int k = 0; k < C::MAX_L / 256; ++k)
+      if (tid + 256 * k < L) idx_lds[tid + 256 * k] = iv_reg[k];
+    __syncthreads();
+  } else {
+    {
+      const __bf16* qp = a.q + ((int64_t)q * kDH + head) * kDD + (kDD / 2) * dh + hf * 8;
+#pragma unroll
+      for (int k = 0; k < kDD / 32; ++k) qreg[k] = *reinterpret_cast<const bf16x8*>(qp + 16 * k);
+    }
+    // this query's index row from its scores: Wc window entries, then the K top-k entries
+    const int t = q % a.S;
+    const int cvis = min(a.T, visible_rows(a.start_pos, t, a.ratio));
+    for (int i = tid; i < a.Wc; i += 256) idx_lds[i] = topk_dev::window_entry(t, i, a.start_pos, a.W);
+    if (cvis <= a.K) {  // every visible position is kept
+      for (int i = tid; i < a.K; i += 256) idx_lds[a.Wc + i] = i < cvis ? i + a.offset : -1;
+    } else {
+      int* top = idx_lds + a.Wc;
+      topk_dev::block_topk<256, SKPT>(a.scores + (int64_t)q * a.T, cvis, a.K, a.offset, tsm,
+                                      [&](int slot, int v) { top[slot] = v; });
+    }
+    __syncthreads();
+    // the row as selected (one workgroup of the query), then its slot codes in place (each entry
+    // by the thread that wrote it out)
+    const bool wr = a.idx_out != nullptr && s == 0;
+    for (int i = tid; i < L; i += 256) {
+      const int iv = idx_lds[i];
+      if (wr) a.idx_out[(int64_t)q * a.ld_out + i] = iv;
+      idx_lds[i] = (int)dec_slot_code(iv, win_n, (uint32_t)a.win_rs, (uint32_t)a.comp_rs);
+    }
+    __syncthreads();
   }
-#pragma unroll
-  for (int k = 0; k < C::MAX_L / 256; ++k)
-    if (tid + 256 * k < L) idx_lds[tid + 256 * k] = iv_reg[k];
-  __syncthreads();
   // valid rows of this split as two 64-bit masks (rows 0..63, 64..95 of the split)
   const uint64_t vm0 = __builtin_amdgcn_ballot_w64(lane < nr && !(idx_lds[a0 + lane] & 2));
   const uint64_t vm1 = __builtin_amdgcn_ballot_w64(64 + lane < nr && !(idx_lds[a0 + 64 + lane] & 2));
@@ -458,7 +498,7 @@ struct DecPlan {
   int ns, rps, lp, ok;
 };
 
-int g_resident_blocks[64][2] = {};  // per device and split count: workgroups resident at once
+int g_resident_blocks[64][4] = {};  // per device, split count and selection: workgroups resident at once
 int g_xcd_local[64] = {};           // per device: 0 unknown, 1 XCD-local rendezvous valid, -1 not
 
 int xcd_local_mode(int dev, hipStream_t st) {
@@ -478,10 +518,10 @@ int xcd_local_mode(int dev, hipStream_t st) {
   return ok;
 }
 
-template <int NS>
+template <int NS, int SKPT>
 int resident_blocks(int dev) {
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sparse_attn_decode_kernel<NS>, 256, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sparse_attn_decode_kernel<NS, SKPT>, 256, 0) != hipSuccess)
     return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   return per_cu * cus;
@@ -511,21 +551,29 @@ size_t sparse_attn_decode_workspace(int B, int S, int H, int D, int L, bool fp4)
 }
 
 // Returns 1 and launches when the two-phase decode path applies, 0 when the caller should use
-// the general kernel, or a negative error.
+// the general kernel, or a negative error.  With sel set, the kernel selects the index rows itself
+// (idx is not read); that needs at most 2048 scores per row.
 int sparse_attn_decode_launch(const __bf16* q, const unsigned char* win, int64_t win_n, int64_t win_bs,
                               int64_t win_rs, const unsigned char* comp, int64_t comp_n, int64_t comp_bs,
                               int64_t comp_rs, const float* sink, const int32_t* idx, int L, float scale_log2,
-                              __bf16* o, int B, int S, int H, int D, bool fp4, void* workspace, hipStream_t st) {
+                              __bf16* o, int B, int S, int H, int D, bool fp4, void* workspace,
+                              const DecSelect* sel, hipStream_t st) {
   const DecPlan p = plan_decode(B * S, H, D, L, fp4);
   if (!p.ok) return 0;
+  if (sel && (sel->T > 2048 || sel->T < 1 || sel->Wc + sel->K != L)) return 0;
   // slot codes hold row byte offsets in 32 bits; the copies move 16-byte pieces of rows
   if ((uint64_t)win_n * (uint64_t)win_rs >= (1ull << 31) || (uint64_t)comp_n * (uint64_t)comp_rs >= (1ull << 31))
     return 0;
   if ((((uintptr_t)win | (uintptr_t)comp) & 15) || ((win_rs | win_bs | comp_rs | comp_bs) & 15)) return 0;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int& resident = g_resident_blocks[dev][p.ns == 8 ? 0 : 1];
-  if (resident == 0) resident = p.ns == 8 ? resident_blocks<8>(dev) : resident_blocks<16>(dev);
+  const int vi = (p.ns == 8 ? 0 : 1) + (sel ? 2 : 0);
+  int& resident = g_resident_blocks[dev][vi];
+  if (resident == 0)
+    resident = vi == 0 ? resident_blocks<8, 0>(dev)
+             : vi == 1 ? resident_blocks<16, 0>(dev)
+             : vi == 2 ? resident_blocks<8, 8>(dev)
+                       : resident_blocks<16, 8>(dev);
   const int Q = B * S;
   if (Q * p.ns > resident) return 0;  // the rendezvous needs every workgroup resident at once
   DecArgs a{};
@@ -551,11 +599,25 @@ int sparse_attn_decode_launch(const __bf16* q, const unsigned char* win, int64_t
   a.Lp = p.lp;
   a.xcd_map = (Q % 8 == 0) ? 1 : 0;
   a.local = a.xcd_map && xcd_local_mode(dev, st);
+  if (sel) {
+    a.scores = sel->scores;
+    a.T = sel->T;
+    a.K = sel->K;
+    a.start_pos = sel->start_pos;
+    a.ratio = sel->ratio;
+    a.W = sel->W;
+    a.Wc = sel->Wc;
+    a.offset = sel->offset;
+    a.idx_out = sel->idx_out;
+    a.ld_out = sel->ld_out;
+  }
   dim3 grid(Q * p.ns);
-  if (p.ns == 8)
-    hipLaunchKernelGGL(sparse_attn_decode_kernel<8>, grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(sparse_attn_decode_kernel<16>, grid, dim3(256), 0, st, a);
+  switch (vi) {
+    case 0: hipLaunchKernelGGL((sparse_attn_decode_kernel<8, 0>), grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((sparse_attn_decode_kernel<16, 0>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((sparse_attn_decode_kernel<8, 8>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((sparse_attn_decode_kernel<16, 8>), grid, dim3(256), 0, st, a); break;
+  }
   const int rc = check_launch("sparse_attn_decode");
   return rc ? rc : 1;
 }

@@ -12,91 +12,19 @@
 // at most K positions need no scores at all: they are 0..c-1 followed by -1.
 //
 // Window rows (`get_window_topk_idxs`): a direct formula per entry.
-#include "dsa_internal.h"
+#include "topk_block.h"
 
 namespace dsa {
 
 namespace {
 
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (u == 0x80000000u) u = 0u;  // -0.0 == +0.0
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
-// Exclusive prefix sum over the block (blockDim.x threads, multiple of 64); returns the
-// exclusive prefix of `v` and writes the block total to *total.
-template <int NT>
-__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch /* NT/64 + 1 ints */, int* total) {
-  constexpr int NW = NT / 64;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int u = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += u;
-  }
-  if (lane == 63) scratch[wave] = incl;
-  __syncthreads();
-  int wbase = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    const int s = scratch[i];
-    wbase += (i < wave) ? s : 0;
-    tot += s;
-  }
-  __syncthreads();
-  *total = tot;
-  return wbase + incl - v;
-}
-
-template <int NT>
-__device__ __forceinline__ uint32_t block_reduce_and_or(uint32_t a, uint32_t o, uint32_t* scratch, uint32_t* out_or) {
-  constexpr int NW = NT / 64;
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    a &= __shfl_xor(a, m, 64);
-    o |= __shfl_xor(o, m, 64);
-  }
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (lane == 0) {
-    scratch[2 * wave] = a;
-    scratch[2 * wave + 1] = o;
-  }
-  __syncthreads();
-  uint32_t ra = 0xFFFFFFFFu, ro = 0u;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) {
-    ra &= scratch[2 * i];
-    ro |= scratch[2 * i + 1];
-  }
-  __syncthreads();
-  *out_or = ro;
-  return ra;
-}
-
-// Entry s of query t's window row (`get_window_topk_idxs`): chunk positions in prefill
-// (start_pos == 0), ring slots oldest first in decode; -1 past the query / for an unfilled slot.
-__device__ __forceinline__ int window_entry(int t, int s, int start_pos, int W) {
-  if (start_pos == 0) {
-    const int first = t - W + 1 > 0 ? t - W + 1 : 0;
-    const int pos = first + s;
-    return pos <= t ? pos : -1;
-  }
-  const int oldest = start_pos % W + 1;
-  const int slot = oldest + s < W ? oldest + s : oldest + s - W;
-  return slot <= start_pos ? slot : -1;
-}
+using namespace topk_dev;
 
 template <int NT, int KPT>
 __global__ void __launch_bounds__(NT)
 topk_kernel(const float* __restrict__ scores, int S, int T, int K, int start_pos, int ratio, int offset,
             int32_t* __restrict__ idx, int64_t ld_idx, int row0, int W, int Wc) {
-  __shared__ int hist[256];
-  __shared__ int scan_scratch[NT / 64 + 2];
-  __shared__ uint32_t red_scratch[2 * (NT / 64)];
-  __shared__ int sel_info[2];
+  __shared__ TopkSmem<NT> sm;
 
   const int row = row0 + blockIdx.x;  // b*S + t
   const int t = row % S;
@@ -110,88 +38,7 @@ topk_kernel(const float* __restrict__ scores, int S, int T, int K, int start_pos
     return;
   }
   // n = K here: exactly K positions are kept and no -1 is written
-  const float* srow = scores + (int64_t)row * T;
-  const int jbase = tid * KPT;
-  uint32_t key[KPT];
-  // loads first (clamped, always in bounds), then branch-free keys, so the loads overlap
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) key[i] = __float_as_uint(srow[min(jbase + i, c - 1)]);
-  uint32_t kand = 0xFFFFFFFFu, kor = 0u;
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const bool vis = jbase + i < c;
-    const uint32_t k = order_key(__uint_as_float(key[i]));
-    key[i] = vis ? k : 0u;  // invisible: below every real key
-    kand &= vis ? k : 0xFFFFFFFFu;
-    kor |= vis ? k : 0u;
-  }
-  uint32_t all_or;
-  const uint32_t all_and = block_reduce_and_or<NT>(kand, kor, red_scratch, &all_or);
-  const uint32_t diff = all_and ^ all_or;  // bits that differ among the visible keys
-
-  uint32_t prefix = all_and & ~diff;  // bits shared by every visible key
-  uint32_t mask = ~diff;              // bits already fixed
-  int remaining = K;                  // how many of the keys matching `prefix` are still to be taken
-  if (diff != 0u) {
-    int hb = 31 - __builtin_clz(diff);  // highest differing bit
-    while (true) {
-      const int lo = hb >= 7 ? hb - 7 : 0;
-      const int width = hb - lo + 1;
-      const uint32_t dmask = ((width == 32) ? 0xFFFFFFFFu : ((1u << width) - 1u)) << lo;
-      for (int i = tid; i < 256; i += NT) hist[i] = 0;
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        if (jbase + i < c && (key[i] & mask) == prefix) atomicAdd(&hist[(key[i] & dmask) >> lo], 1);
-      }
-      __syncthreads();
-      // suffix counts over the bins (largest digit first): thread i takes bin 255 - i
-      const int bin = 255 - (tid & 255);
-      const int cnt = tid < 256 ? hist[bin] : 0;
-      int tot;
-      const int excl = block_exclusive_scan<NT>(cnt, scan_scratch, &tot);  // keys in bins above `bin`
-      if (tid < 256 && excl < remaining && excl + cnt >= remaining) {
-        sel_info[0] = bin;
-        sel_info[1] = excl;
-      }
-      __syncthreads();
-      const int sbin = sel_info[0];
-      remaining -= sel_info[1];
-      prefix |= ((uint32_t)sbin << lo);
-      mask |= dmask;
-      __syncthreads();
-      if (lo == 0) break;
-      hb = lo - 1;
-    }
-  }
-  const uint32_t tau = prefix;  // key of the K-th best visible score
-  // keep keys > tau, and the first `remaining` keys == tau in position order
-  int n_eq = 0;
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) n_eq += (jbase + i < c && key[i] == tau) ? 1 : 0;
-  int tot_eq;
-  int eq_before = block_exclusive_scan<NT>(n_eq, scan_scratch, &tot_eq);
-  int n_keep = 0;
-  uint32_t keep_bits = 0u;  // KPT <= 32
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const bool vis = jbase + i < c;
-    bool k = vis && key[i] > tau;
-    if (vis && key[i] == tau) {
-      k = eq_before < remaining;
-      ++eq_before;
-    }
-    if (k) {
-      keep_bits |= 1u << i;
-      ++n_keep;
-    }
-  }
-  int tot_keep;
-  int pos = block_exclusive_scan<NT>(n_keep, scan_scratch, &tot_keep);
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    if ((keep_bits & (1u << i)) && pos < K) out[pos++] = jbase + i + offset;
-  }
+  block_topk<NT, KPT>(scores + (int64_t)row * T, c, K, offset, sm, [&](int slot, int v) { out[slot] = v; });
 }
 
 // Many rows (prefill): one wave per row and no workgroup barriers.  Lane l holds the keys of

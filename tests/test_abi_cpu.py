@@ -24,7 +24,8 @@ def dsa():
 
 def test_header_declares_the_step():
     names = _declared()
-    for n in ["dsa_index_scores", "dsa_topk", "dsa_window_idx", "dsa_select", "dsa_sparse_attn", "dsa_last_error",
+    for n in ["dsa_index_scores", "dsa_topk", "dsa_window_idx", "dsa_select", "dsa_sparse_attn",
+              "dsa_sparse_attn_select", "dsa_last_error",
               "dsa_abi_version", "dsa_sparse_attn_workspace_size", "dsa_window_cols"]:
         assert n in names
 
@@ -71,6 +72,24 @@ def test_argument_errors_without_launch(dsa):
     assert lib.dsa_select(nul, 1, 2, 10, 8, 5, 4, 4, 2, nul, 10, nul) == -4  # chunked decode
     assert lib.dsa_select(nul, 1, 2, 10, 8, 0, 4, 4, 2, nul, 10, nul) == -1
     assert lib.dsa_select(nul, 0, 2, 10, 8, 0, 4, 4, 2, nul, 10, nul) == 0
+    # index rows + attention: sizes, missing window source, chunked decode, empty batch, a shape
+    # that needs idx (the fp32 path always runs the two calls)
+    src0 = dsa.DsaKvSrc()
+    src0.rows = 16
+    src0.n_rows = 4
+    src0.batch_stride = 4 * 64
+    src0.row_stride = 64
+    sel = lib.dsa_sparse_attn_select
+    assert sel(vp(16), 10, 8, 0, 0, 4, vp(16), ctypes.byref(src0), None, vp(16), 1.0, vp(16), 1, 1, 1, 1, 64, nul,
+               nul, 0, nul) == -2  # ratio 0
+    assert sel(vp(16), 10, 8, 0, 4, 4, vp(16), None, None, vp(16), 1.0, vp(16), 1, 1, 1, 1, 64, nul, nul, 0,
+               nul) == -1
+    assert sel(vp(16), 10, 8, 10, 4, 4, vp(16), ctypes.byref(src0), None, vp(16), 1.0, vp(16), 1, 1, 4, 1, 64, nul,
+               nul, 0, nul) == -4  # chunked decode
+    assert sel(vp(16), 10, 8, 0, 4, 4, vp(16), ctypes.byref(src0), None, vp(16), 1.0, vp(16), 1, 0, 1, 1, 64, nul,
+               nul, 0, nul) == 0
+    assert sel(vp(16), 10, 8, 0, 4, 4, vp(16), ctypes.byref(src0), None, vp(16), 1.0, vp(16), 0, 1, 1, 1, 64, nul,
+               nul, 0, nul) == -1
     # sparse attention: unsupported head_dim, missing window source, bad format, workspace
     src = dsa.DsaKvSrc()
     src.rows = 16

@@ -339,6 +339,45 @@ def test_step_full_size_sampled(name):
         assert np.all(idx_cpu[t, w.Wc + n:] == -1)
 
 
+# ------------------------------------------------------------------------ index rows + attention in one call
+@pytest.mark.parametrize("B,T,ctx,kind", [
+    (32, 2048, 8192, "normal"),  # decode, one launch: every workgroup selects its query's row
+    (5, 1999, 7996, "ties"),     # 16 splits, ties at the threshold go to the lower rows
+    (3, 300, 1200, "normal"),    # fewer visible rows than index_topk: all kept, -1 tail
+    (4, 4000, 16000, "normal"),  # more than 2048 scores per row: the select and attention calls
+])
+def test_sparse_attn_select(B, T, ctx, kind):
+    """The index rows written out equal the oracle's window + top-k rows exactly, and the output
+    matches the oracle's attention over those rows; two calls in a row."""
+    dsa = _dsa()
+    _log(f"select+attn case B={B} T={T} ctx={ctx} {kind}")
+    H, D, nw, K, ratio, S = 64, 512, 128, 512, 4, 1
+    sp = ctx - 1
+    g = torch.Generator().manual_seed(B * 7 + T)
+    q = torch.randn(B, S, H, D, generator=g).to(torch.bfloat16)
+    kv_win = torch.randn(B, nw, D, generator=g).to(torch.bfloat16)
+    kv_comp = torch.randn(B, T, D, generator=g).to(torch.bfloat16)
+    sink = torch.randn(H, generator=g)
+    rng = np.random.default_rng(T + B)
+    if kind == "ties":
+        sc = rng.integers(-4, 5, size=(B, S, T)).astype(np.float32)
+    else:
+        sc = rng.standard_normal((B, S, T)).astype(np.float32)
+    c = oracle.visible_count(np.arange(S), sp, ratio)
+    sc[:, np.arange(T)[None, :] >= np.minimum(c, T)[:, None]] = -np.inf
+    exp_idx = np.concatenate([oracle.window_rows(nw, B, S, sp), oracle.topk_select(sc.astype(np.float64), K, sp,
+                                                                                   ratio, nw)], axis=-1)
+    scale = D ** -0.5
+    exp_o = oracle.sparse_attn(q, oracle.kv_concat(kv_win, kv_comp), sink, exp_idx, scale)
+    args = (torch.from_numpy(sc).to(DEV), q.to(DEV), kv_win.to(DEV), kv_comp.to(DEV), sink.to(DEV))
+    for call in range(2):
+        o, idx = dsa.dsa_sparse_attn_select(*args, index_topk=K, start_pos=sp, ratio=ratio, W=nw, scale=scale)
+        np.testing.assert_array_equal(idx.cpu().numpy(), exp_idx)
+        err = max_abs_err(o.float().cpu().numpy(), exp_o)
+        _log(f"  call {call}: max abs err {err:.3e}")
+        assert err <= ATTN_TOL["bf16"], err
+
+
 # ------------------------------------------------------------------------ two-phase decode path
 @pytest.mark.parametrize("B,S,L,nc,inval", [
     (32, 1, 640, 2048, 0.0),   # 8 splits, XCD-grouped blocks
