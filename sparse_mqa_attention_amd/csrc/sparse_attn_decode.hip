@@ -145,7 +145,9 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
   __shared__ int idx_lds[C::MAX_L];
   __shared__ float stats_lds[NS * kDH * 2];
   __shared__ int flags[1];  // the rendezvous timed out
-  __shared__ topk_dev::TopkSmem<256> tsm;
+  // the in-kernel top-k works in the row buffer, which phase A fills only after it
+  static_assert(sizeof(topk_dev::TopkSmem<256>) <= C::ROWS_BYTES, "top-k scratch fits the row buffer");
+  topk_dev::TopkSmem<256>& tsm = *reinterpret_cast<topk_dev::TopkSmem<256>*>(rows);
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -211,7 +213,7 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
       for (int i = tid; i < a.K; i += 256) idx_lds[a.Wc + i] = i < cvis ? i + a.offset : -1;
     } else {
       int* top = idx_lds + a.Wc;
-      topk_dev::block_topk<256, SKPT>(a.scores + (int64_t)q * a.T, cvis, a.K, a.offset, tsm,
+      topk_dev::block_topk<256, SKPT>(a.scores + (int64_t)q * a.T, a.T, cvis, a.K, a.offset, tsm,
                                       [&](int slot, int v) { top[slot] = v; });
     }
     __syncthreads();

@@ -38,7 +38,7 @@ topk_kernel(const float* __restrict__ scores, int S, int T, int K, int start_pos
     return;
   }
   // n = K here: exactly K positions are kept and no -1 is written
-  block_topk<NT, KPT>(scores + (int64_t)row * T, c, K, offset, sm, [&](int slot, int v) { out[slot] = v; });
+  block_topk<NT, KPT>(scores + (int64_t)row * T, T, c, K, offset, sm, [&](int slot, int v) { out[slot] = v; });
 }
 
 // Many rows (prefill): one wave per row and no workgroup barriers.  Lane l holds the keys of
