@@ -16,21 +16,46 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Block scan of a 64-bit word that packs four 16-bit counters (no carries cross
-// a field as long as every field's block total stays below 65536).  Returns the exclusive prefix of
-// `v` and writes the block total to *total.  `scratch` (NT/64 words) is written once and read after
-// the one barrier; the caller gives every scan of a kernel its own scratch.
+// Inclusive prefix over the 64 lanes of a wave: DPP shifts within each row of 16 lanes, then the
+// row broadcasts of lanes 15 and 31 carry the row totals up (rows the mask leaves out keep x).
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t x) {
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+// AND and OR of the wave's values (lane 63 of the inclusive prefix), uniform
+__device__ __forceinline__ void wave_and_or(uint32_t& a, uint32_t& o) {
+  a &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)a, 0x111, 0xf, 0xf, false);
+  o |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o, 0x111, 0xf, 0xf, false);
+  a &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)a, 0x112, 0xf, 0xf, false);
+  o |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o, 0x112, 0xf, 0xf, false);
+  a &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)a, 0x114, 0xf, 0xf, false);
+  o |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o, 0x114, 0xf, 0xf, false);
+  a &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)a, 0x118, 0xf, 0xf, false);
+  o |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o, 0x118, 0xf, 0xf, false);
+  a &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)a, 0x142, 0xa, 0xf, false);
+  o |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o, 0x142, 0xa, 0xf, false);
+  a &= (uint32_t)__builtin_amdgcn_update_dpp(-1, (int)a, 0x143, 0xc, 0xf, false);
+  o |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)o, 0x143, 0xc, 0xf, false);
+  a = (uint32_t)__builtin_amdgcn_readlane((int)a, 63);
+  o = (uint32_t)__builtin_amdgcn_readlane((int)o, 63);
+}
+
+// Block scan of a 64-bit word that packs four 16-bit counters (no carry crosses a field as long as
+// every field's block total stays below 65536, so the two 32-bit halves scan apart).  Returns the
+// exclusive prefix of `v` and writes the block total to *total.  `scratch` (NT/64 words) is
+// written once and read after the one barrier; each scan of a kernel gets its own scratch.
 template <int NT>
 __device__ __forceinline__ uint64_t block_scan_packed(uint64_t v, uint64_t* scratch, uint64_t* total) {
   constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  uint64_t incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint64_t u = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += u;
-  }
+  const uint64_t incl = ((uint64_t)wave_incl_sum((uint32_t)(v >> 32)) << 32) | wave_incl_sum((uint32_t)v);
   if (lane == 63) scratch[wave] = incl;
   __syncthreads();
   uint64_t wbase = 0, tot = 0;
@@ -72,7 +97,7 @@ struct TopkSmem {
   static constexpr int NW = NT / 64;
   static constexpr int R = NW;     // histogram copies: lane l counts into copy l % R
   static constexpr int RP = 257;   // copy stride in ints: the copies of one bin sit in different banks
-  int hist[2][R * RP];             // two sets, used on alternate passes
+  alignas(16) int hist[2][R * RP]; // two sets, used on alternate passes
   alignas(16) int cnt[2][256];     // per-pass bin totals
   uint32_t red[2 * NW];
   uint64_t scan[2][NW];
@@ -139,7 +164,7 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ srow, int T
       for (int e = 0; e < E; ++e) key[j * E + e] = __float_as_uint(srow[min(E * (NT * j + tid) + e, c - 1)]);
   }
   // this pass's histogram set starts at zero (the other set is cleared during the first pass)
-  for (int i = tid; i < R * RP; i += NT) sm.hist[0][i] = 0;
+  for (int i = tid; i < R * RP / 4; i += NT) reinterpret_cast<int4*>(sm.hist[0])[i] = int4{0, 0, 0, 0};
   uint32_t kand = 0xFFFFFFFFu, kor = 0u;
 #pragma unroll
   for (int i = 0; i < KPT; ++i) {
@@ -149,11 +174,7 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ srow, int T
     kand &= vis ? k : 0xFFFFFFFFu;
     kor |= vis ? k : 0u;
   }
-#pragma unroll
-  for (int m = 1; m < 64; m <<= 1) {
-    kand &= __shfl_xor(kand, m, 64);
-    kor |= __shfl_xor(kor, m, 64);
-  }
+  wave_and_or(kand, kor);
   if (lane == 0) {
     sm.red[2 * wave] = kand;
     sm.red[2 * wave + 1] = kor;
@@ -193,43 +214,24 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ srow, int T
         for (int r = 0; r < R; ++r) s += sm.hist[set][r * RP + tid];
         sm.cnt[set][tid] = s;
       }
-      for (int i = tid; i < R * RP; i += NT) sm.hist[set ^ 1][i] = 0;
+      for (int i = tid; i < R * RP / 4; i += NT) reinterpret_cast<int4*>(sm.hist[set ^ 1])[i] = int4{0, 0, 0, 0};
       __syncthreads();
       // every wave picks the digit: lane l scans digits 255-4l .. 252-4l (largest first)
       const int4 h4 = *reinterpret_cast<const int4*>(&sm.cnt[set][252 - 4 * lane]);
       const int c0 = h4.w, c1 = h4.z, c2 = h4.y, c3 = h4.x;
       const int mine = c0 + c1 + c2 + c3;
-      int incl = mine;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int u = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += u;
-      }
+      const int incl = (int)wave_incl_sum((uint32_t)mine);
       const int excl = incl - mine;  // keys in digits above this lane's four
-      const uint64_t hit = __builtin_amdgcn_ballot_w64(excl < remaining && incl >= remaining);
-      const int src = __builtin_ctzll(hit);
-      int digit = 0, above = 0, in_digit = 0;
-      if (lane == src) {
-        int a = excl;
-        if (a + c0 >= remaining) {
-          digit = 255 - 4 * lane;
-          in_digit = c0;
-        } else if ((a += c0) + c1 >= remaining) {
-          digit = 254 - 4 * lane;
-          in_digit = c1;
-        } else if ((a += c1) + c2 >= remaining) {
-          digit = 253 - 4 * lane;
-          in_digit = c2;
-        } else {
-          a += c2;
-          digit = 252 - 4 * lane;
-          in_digit = c3;
-        }
-        above = a;
-      }
-      digit = __shfl(digit, src, 64);
-      above = __shfl(above, src, 64);
-      in_digit = __shfl(in_digit, src, 64);
+      // the one lane whose four digits hold the `remaining`-th key; every lane works out its own
+      // candidate and the answer is read from that lane
+      const int src = __builtin_ctzll(__builtin_amdgcn_ballot_w64(excl < remaining && incl >= remaining));
+      const int a1 = excl + c0, a2 = a1 + c1, a3 = a2 + c2;
+      const int sub = a1 >= remaining ? 0 : a2 >= remaining ? 1 : a3 >= remaining ? 2 : 3;
+      const int above_l = sub == 0 ? excl : sub == 1 ? a1 : sub == 2 ? a2 : a3;
+      const int in_l = sub == 0 ? c0 : sub == 1 ? c1 : sub == 2 ? c2 : c3;
+      const int digit = __builtin_amdgcn_readlane(255 - 4 * lane - sub, src);
+      const int above = __builtin_amdgcn_readlane(above_l, src);
+      const int in_digit = __builtin_amdgcn_readlane(in_l, src);
       remaining -= above;
       prefix |= ((uint32_t)digit << lo);
       mask |= dmask;
@@ -266,36 +268,44 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ srow, int T
     for (int j = 0; j < J; ++j) eq_base[j] = fields_below(eq_tot, j) + field16(eq_before, j);
   }
   Bits keep_bits = 0u;
-  uint64_t kw = 0;
+  if (exact) {  // every key at or above the threshold is taken
 #pragma unroll
-  for (int j = 0; j < J; ++j) {
-    int rank = eq_base[j], n = 0;
+    for (int i = 0; i < KPT; ++i) {
+      const bool vis = E * (NT * (i / E) + tid) + i % E < c;
+      keep_bits |= (vis && (key[i] & mask) >= tau) ? (Bits)1 << i : (Bits)0;
+    }
+  } else {
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int i = j * E + e;
-      const bool vis = E * (NT * j + tid) + e < c;
-      const uint32_t mk = key[i] & mask;
-      bool k = vis && mk > tau;
-      if (vis && mk == tau) {
-        k = exact || rank < remaining;
-        ++rank;
-      }
-      if (k) {
-        keep_bits |= (Bits)1 << i;
-        ++n;
+    for (int j = 0; j < J; ++j) {
+      int rank = eq_base[j];
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const int i = j * E + e;
+        const bool vis = E * (NT * j + tid) + e < c;
+        const uint32_t mk = key[i] & mask;
+        bool k = vis && mk > tau;
+        if (vis && mk == tau) {
+          k = rank < remaining;
+          ++rank;
+        }
+        keep_bits |= k ? (Bits)1 << i : (Bits)0;
       }
     }
-    kw |= (uint64_t)n << (16 * j);
   }
+  constexpr uint32_t CM = (1u << E) - 1u;  // one chunk's bits
+  uint64_t kw = 0;
+#pragma unroll
+  for (int j = 0; j < J; ++j) kw |= (uint64_t)__builtin_popcount((uint32_t)(keep_bits >> (j * E)) & CM) << (16 * j);
   uint64_t k_tot;
   const uint64_t k_before = block_scan_packed<NT>(kw, sm.scan[1], &k_tot);
 #pragma unroll
   for (int j = 0; j < J; ++j) {
-    int slot = fields_below(k_tot, j) + field16(k_before, j);
+    const uint32_t cb = (uint32_t)(keep_bits >> (j * E)) & CM;
+    const int base = fields_below(k_tot, j) + field16(k_before, j);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int i = j * E + e;
-      if (((keep_bits >> i) & 1u) && slot < K) put(slot++, E * (NT * j + tid) + e + offset);
+      const int slot = base + __builtin_popcount(cb & ((1u << e) - 1u));
+      if (((cb >> e) & 1u) && slot < K) put(slot, E * (NT * j + tid) + e + offset);
     }
   }
 }
