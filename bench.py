@@ -1,14 +1,15 @@
 """Benchmark of the sparse MQA attention step on one MI355X.
 
-A step is one pass of the whole path over one batch of synthetic input: index scores, then the
-index rows (window rows and top-k selection) and sparse attention through dsa_sparse_attn_select,
-which is one kernel for decode batches and two otherwise (every stage a libdsa kernel).  Inputs
-are resident in HBM before timing starts; several input sets are rotated so that the 256 MB
-Infinity Cache cannot serve one step from the previous one.
+A step is one pass of the whole path over one batch of synthetic input through
+dsa_sparse_attn_step: index scores, index rows (window rows and top-k selection) and sparse
+attention.  For decode batches that is one kernel; otherwise the index scores, the index rows and
+the attention are three launches (every stage a libdsa kernel).  Inputs are resident in HBM before
+timing starts; several input sets are rotated so that the 256 MB Infinity Cache cannot serve one
+step from the previous one.
 
 Prints one JSON line (see `--help`).  The roofline object covers the dominant kernel (the decode
-kernel that selects and attends, or the sparse attention kernel), timed with HIP events on the
-stream it runs on; the CPU baseline is the oracle timed on a bounded sample on the host.
+kernel that scores, selects and attends, or the sparse attention kernel), timed with HIP events on
+the stream it runs on; the CPU baseline is the oracle timed on a bounded sample on the host.
 """
 from __future__ import annotations
 
@@ -29,7 +30,7 @@ PEAK_BF16_TFLOPS = 2500.0
 ROTATE_BYTES = 768 << 20  # rotate input sets until they span more than the Infinity Cache (256 MB)
 KERNEL_SOURCES = ["sparse_mqa_attention_amd/csrc/sparse_attn.hip", "sparse_mqa_attention_amd/csrc/sparse_attn_decode.hip",
                   "sparse_mqa_attention_amd/csrc/sparse_attn_prefill_h16.hip", "sparse_mqa_attention_amd/csrc/dsa_internal.h",
-                  "sparse_mqa_attention_amd/csrc/topk_block.h"]
+                  "sparse_mqa_attention_amd/csrc/topk_block.h", "sparse_mqa_attention_amd/csrc/index_tile.h"]
 
 
 def _args():
@@ -159,22 +160,21 @@ def main():
     stream = torch.cuda.current_stream(dev)
     comp_key = "kv_comp_fp4" if w.comp_fmt == "fp4" else "kv_comp"
 
-    # Decode batches the two-phase decode kernel takes select their index rows inside it (one
-    # launch for top-k, window rows and attention); elsewhere the select and the attention are
-    # two launches.  The step calls the same entry point either way.
+    # Decode batches the two-phase decode kernel takes score, select and attend inside it (one
+    # launch for the whole step); elsewhere the step is index scores, index rows and attention.
     fused = (w.mode == "decode" and w.dtype == "bf16" and w.comp_fmt != "fp4" and w.T <= 2048 and w.D == 512
-             and w.H == 64 and w.B * w.S < 256)
+             and w.H == 64 and w.B * w.S < 256 and w.D_I == 128 and w.H_I <= 64)
+
+    def stage_step(i):
+        s, bf = sets[i % n_sets], bufs[i % n_sets]
+        dsa.dsa_sparse_attn_step(s["qI"], s["kI"], s["w"], s["q"], s["kv_win"], s[comp_key], s["sink"],
+                                 index_topk=w.index_topk, start_pos=w.start_pos, ratio=w.ratio, W=w.W, scale=scale,
+                                 w_scale=w_scale, comp_scales=s.get("kv_comp_scale"), out=bf["o"],
+                                 scores=bf["scores"], idx=bf["idx"], workspace=bf["workspace"])
 
     def stage_index(i):
         s, bf = sets[i % n_sets], bufs[i % n_sets]
         dsa.dsa_index_scores(s["qI"], s["kI"], s["w"], w_scale, w.start_pos, w.ratio, out=bf["scores"])
-
-    def stage_select_attn(i):
-        s, bf = sets[i % n_sets], bufs[i % n_sets]
-        dsa.dsa_sparse_attn_select(bf["scores"], s["q"], s["kv_win"], s[comp_key], s["sink"],
-                                   index_topk=w.index_topk, start_pos=w.start_pos, ratio=w.ratio, W=w.W,
-                                   scale=scale, comp_scales=s.get("kv_comp_scale"), out=bf["o"], idx=bf["idx"],
-                                   workspace=bf["workspace"])
 
     def stage_select(i):
         s, bf = sets[i % n_sets], bufs[i % n_sets]
@@ -185,13 +185,11 @@ def main():
         dsa.dsa_sparse_attn(s["q"], s["kv_win"], s[comp_key], s["sink"], bf["idx"], scale,
                             comp_scales=s.get("kv_comp_scale"), out=bf["o"], workspace=bf["workspace"])
 
-    def step(i):
-        stage_index(i)
-        stage_select_attn(i)
+    step = stage_step
 
     # the dominant kernel and the rest of the step, timed apart
     if fused:
-        dominant, rest = stage_select_attn, stage_index
+        dominant, rest = stage_step, None
     else:
         dominant = stage_attn
 
@@ -237,21 +235,21 @@ def main():
     # the dominant kernel alone: R launches back to back in one graph, bracketed by HIP events
     R = 20
     attn_graph = capture(dominant, 0, R)
-    sel_graph = capture(rest, 0, R)
+    sel_graph = capture(rest, 0, R) if rest is not None else None
     attn_graph.replay()
     torch.cuda.synchronize()
     e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
     e0.record(stream)
     attn_graph.replay()
     e1.record(stream)
-    sel_graph.replay()
+    if sel_graph is not None:
+        sel_graph.replay()
     e2.record(stream)
     torch.cuda.synchronize()
     attn_avg_ms = e0.elapsed_time(e1) / R
     sel_avg_ms = e1.elapsed_time(e2) / R
     if fused:
-        parts = (f"window+top-k+attention (one kernel) {attn_avg_ms * 1e3:.2f} us, "
-                 f"index scores {sel_avg_ms * 1e3:.2f} us")
+        parts = f"index scores+window+top-k+attention (one kernel) {attn_avg_ms * 1e3:.2f} us"
     else:
         parts = f"attention {attn_avg_ms * 1e3:.2f} us, window+index+top-k {sel_avg_ms * 1e3:.2f} us"
     print(f"[bench] {w.name}: step {ms_per_step * 1e3:.2f} us (wall {wall / a.steps * 1e6:.2f} us), {parts}",
@@ -271,7 +269,9 @@ def main():
         row_bytes = valid_per_set * w.D * esz
     alg_bytes = 2 * q_bytes + w.B * w.S * w.L * 4 + w.H * 4 + row_bytes
     if fused:
-        alg_bytes += w.B * w.S * w.T * 4  # the kernel also reads each query's scores once
+        # the kernel also reads the index keys, index queries and head weights, and writes each
+        # query's scores and reads them back once
+        alg_bytes += (w.B * w.T * w.D_I * 2 + w.B * w.S * w.H_I * (w.D_I + 1) * 2 + 2 * w.B * w.S * w.T * 4)
     alg_flops = 4.0 * w.H * w.D * valid_per_set
     if w.mode == "decode":
         achieved = alg_bytes / (attn_avg_ms * 1e-3) / 1e9
@@ -286,7 +286,8 @@ def main():
     sha = kernel_src_sha()
     roof["traffic"] = _traffic(w.name, sha)
     if fused:
-        roof["kernel"] = "dsa_sparse_attn_select (index rows + gather-attention + split combine, one kernel)"
+        roof["kernel"] = ("dsa_sparse_attn_step (index scores + index rows + gather-attention + split combine, "
+                          "one kernel)")
     else:
         roof["kernel"] = "dsa_sparse_attn" + (" (gather-attention + split combine)" if
                                               dsa.dsa_sparse_attn_workspace_size(1, w.B, w.S, w.H, w.D, w.L) else "")

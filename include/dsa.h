@@ -11,6 +11,8 @@
  *   dsa_sparse_attn   attend all heads over the rows an index row names
  *   dsa_sparse_attn_select  dsa_select then dsa_sparse_attn, one launch where the decode
  *                     attention kernel can select its own index rows
+ *   dsa_sparse_attn_step  the whole step: dsa_index_scores then dsa_sparse_attn_select, one
+ *                     launch where the decode attention kernel can also score the rows
  *
  * Citations refer to the DeepSeek V4.1 model pages ("attention/attend/selected",
  * "reindex-layer/read-weights") by the class or function that holds the step.
@@ -221,6 +223,35 @@ int dsa_sparse_attn_select(const float* scores, int T, int index_topk, int start
                            const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
                            float scale, void* o, int dtype, int B, int S, int H, int D, int32_t* idx,
                            void* workspace, size_t workspace_bytes, dsa_stream_t stream);
+
+/*
+ * The whole step (`Indexer.forward` for the scores and the index rows, `get_window_topk_idxs`,
+ * `sparse_attn` as `Attention.forward` chains them): the same results as
+ *
+ *   dsa_index_scores(q_idx, k_idx, k_batch_stride, w, w_scale, dtype, B, S, T, H_I, D_I,
+ *                    start_pos, ratio, scores, stream)
+ *   dsa_sparse_attn_select(scores, T, index_topk, start_pos, ratio, W, q, win, comp, sink,
+ *                          scale, o, dtype, B, S, H, D, idx, workspace, workspace_bytes, stream)
+ *
+ * For the decode batches whose index rows dsa_sparse_attn_select selects inside the decode
+ * attention kernel, and with D_I = 128, H_I <= 64, 16-byte aligned q_idx and k_idx and
+ * k_batch_stride a multiple of 8, it is one launch: the workgroups of a query each score a share
+ * of the compressed rows into `scores`, meet, select the query's index row from all of its scores
+ * and attend.  That needs the workgroups of a query to share one L2 (checked once per device);
+ * where they do not, or the shape does not fit, it makes the two calls above.
+ *
+ *   q_idx, k_idx, w, w_scale, H_I, D_I, T, start_pos, ratio: as for dsa_index_scores
+ *   scores [B, S, T] float32, required: always written in full (dsa_index_scores' contract)
+ *   index_topk, W, q, win, comp, sink, scale, o, dtype, B, S, H, D, idx, workspace: as for
+ *   dsa_sparse_attn_select (idx may be NULL where that call allows it)
+ *
+ * Errors: those of dsa_index_scores and dsa_sparse_attn_select.
+ */
+int dsa_sparse_attn_step(const void* q_idx, const void* k_idx, int64_t k_batch_stride, const void* w, float w_scale,
+                         int H_I, int D_I, int T, int index_topk, int start_pos, int ratio, int W, const void* q,
+                         const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink, float scale, void* o,
+                         int dtype, int B, int S, int H, int D, float* scores, int32_t* idx, void* workspace,
+                         size_t workspace_bytes, dsa_stream_t stream);
 
 #ifdef __cplusplus
 }

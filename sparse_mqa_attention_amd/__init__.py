@@ -11,6 +11,8 @@ Calls (same names as the C entry points):
     dsa_window_idx    sliding-window part of each index row
     dsa_sparse_attn   attention with a per-head sink over the indexed rows
     dsa_sparse_attn_select  the index rows and the attention (one launch for decode batches)
+    dsa_sparse_attn_step    the whole step: index scores, index rows, attention (one launch
+                            for decode batches)
 """
 from __future__ import annotations
 
@@ -70,6 +72,10 @@ def _load():
                                            ctypes.POINTER(DsaKvSrc), vp, f32, vp, i32, i32, i32, i32, i32, vp, vp,
                                            ctypes.c_size_t, vp]
     lib.dsa_sparse_attn_select.restype = i32
+    lib.dsa_sparse_attn_step.argtypes = [vp, vp, i64, vp, f32, i32, i32, i32, i32, i32, i32, i32, vp,
+                                         ctypes.POINTER(DsaKvSrc), ctypes.POINTER(DsaKvSrc), vp, f32, vp, i32, i32,
+                                         i32, i32, i32, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.dsa_sparse_attn_step.restype = i32
     lib.dsa_sparse_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.dsa_sparse_attn_workspace_size.restype = ctypes.c_size_t
     return lib
@@ -282,6 +288,51 @@ def dsa_sparse_attn_select(scores, q, kv_win, kv_comp, sink, *, index_topk: int,
     return out, idx
 
 
+def dsa_sparse_attn_step(q_idx, k_idx, w, q, kv_win, kv_comp, sink, *, index_topk: int, start_pos: int, ratio: int,
+                         W: int, scale: float, w_scale: float, comp_scales=None, out=None, scores=None, idx=None,
+                         workspace=None, stream=None):
+    """The whole step: index scores (as dsa_index_scores), index rows and the sparse attention over
+    them (as dsa_sparse_attn_select); one launch for decode batches the decode kernel takes.
+    Returns (o, idx, scores); scores [B, S, T] float32 and idx [B, S, L] int32 are allocated when not
+    given."""
+    dev = _dev(q_idx, k_idx, w, q, kv_win, kv_comp, sink)
+    _need_contig("q_idx", q_idx)
+    _need_contig("w", w)
+    _need_contig("q", q)
+    B, S, H, D = q.shape
+    H_I, D_I = q_idx.shape[2], q_idx.shape[3]
+    T = k_idx.shape[1]
+    kbs, krs = _batched_rows("k_idx", k_idx)
+    if krs != D_I:
+        raise DsaError(-2, "k_idx rows must be dense")
+    Wc = dsa_window_cols(S, start_pos, W)
+    L = Wc + min(int(index_topk), T)
+    dt = _dtype_code(q)
+    win = kv_src(kv_win)
+    fp4 = kv_comp is not None and kv_comp.dtype == torch.uint8
+    comp = kv_src(kv_comp, comp_scales, DSA_KV_FP4_E4M3_G16 if fp4 else DSA_KV_DENSE)
+    if out is None:
+        out = torch.empty_like(q)
+    _need_contig("o", out)
+    if scores is None:
+        scores = torch.empty(B, S, T, dtype=torch.float32, device=dev)
+    _need_contig("scores", scores)
+    if idx is None:
+        idx = torch.empty(B, S, L, dtype=torch.int32, device=dev)
+    _need_contig("idx", idx)
+    if idx.dtype != torch.int32 or idx.shape[-1] != L:
+        raise DsaError(-2, "idx must be int32 [B, S, L] with L = window columns + top-k columns")
+    need = dsa_sparse_attn_workspace_size(dt, B, S, H, D, L)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.dsa_sparse_attn_step(_ptr(q_idx), _ptr(k_idx), kbs, _ptr(w), float(w_scale), H_I, D_I, T,
+                                    int(index_topk), int(start_pos), int(ratio), int(W), _ptr(q), ctypes.byref(win),
+                                    ctypes.byref(comp), _ptr(sink), float(scale), _ptr(out), dt, B, S, H, D,
+                                    _ptr(scores), _ptr(idx), _ptr(workspace), wbytes, _stream(dev, stream)))
+    return out, idx, scores
+
+
 def sparse_attention_step(q, kv_win, kv_comp, qI, kI, w, sink, *, start_pos: int, ratio: int, W: int,
                           index_topk: int, scale: float, w_scale: float, comp_scales=None, bufs=None,
                           stream=None):
@@ -297,18 +348,15 @@ def sparse_attention_step(q, kv_win, kv_comp, qI, kI, w, sink, *, start_pos: int
     idx = bufs.get("idx")
     if idx is None:
         idx = torch.empty(B, S, Wc + K, dtype=torch.int32, device=q.device)
-    scores = bufs.get("scores")
     if T > 0:
-        scores = dsa_index_scores(qI, kI, w, w_scale, start_pos, ratio, out=scores, stream=stream)
-        o, idx = dsa_sparse_attn_select(scores, q, kv_win, kv_comp, sink, index_topk=index_topk,
-                                        start_pos=start_pos, ratio=ratio, W=W, scale=scale,
-                                        comp_scales=comp_scales, out=bufs.get("o"), idx=idx,
-                                        workspace=bufs.get("workspace"), stream=stream)
-        return o, idx, scores
+        return dsa_sparse_attn_step(qI, kI, w, q, kv_win, kv_comp, sink, index_topk=index_topk, start_pos=start_pos,
+                                    ratio=ratio, W=W, scale=scale, w_scale=w_scale, comp_scales=comp_scales,
+                                    out=bufs.get("o"), scores=bufs.get("scores"), idx=idx,
+                                    workspace=bufs.get("workspace"), stream=stream)
     dsa_window_idx(idx, start_pos, W, stream=stream)
     o = dsa_sparse_attn(q, kv_win, None, sink, idx, scale, out=bufs.get("o"), workspace=bufs.get("workspace"),
                         stream=stream)
-    return o, idx, scores
+    return o, idx, bufs.get("scores")
 
 
 __all__ = [
@@ -321,6 +369,7 @@ __all__ = [
     "dsa_window_idx",
     "dsa_sparse_attn",
     "dsa_sparse_attn_select",
+    "dsa_sparse_attn_step",
     "dsa_sparse_attn_workspace_size",
     "kv_src",
     "sparse_attention_step",

@@ -36,7 +36,7 @@ int sparse_attn_f32_launch(const void*, const dsa_kv_src*, const dsa_kv_src*, co
                            float, void*, int, int, int, int, hipStream_t);
 size_t sparse_attn_bf16_workspace(int, int, int, int, int, bool);
 int sparse_attn_bf16_select_launch(const void*, const dsa_kv_src*, const dsa_kv_src*, const float*, const DecSelect*,
-                                   int, float, void*, int, int, int, int, void*, hipStream_t);
+                                   const DecIndex*, int, float, void*, int, int, int, int, void*, hipStream_t);
 
 }  // namespace dsa
 
@@ -221,7 +221,7 @@ int dsa_sparse_attn_select(const float* scores, int T, int index_topk, int start
     dsa::DecSelect sel{scores, T, K, start_pos, ratio, W, Wc, offset, idx, (int64_t)L};
     dsa_kv_src empty{};
     const dsa_kv_src* cs = (comp && comp->n_rows > 0) ? comp : &empty;
-    rc = dsa::sparse_attn_bf16_select_launch(q, win, cs, sink, &sel, L, scale, o, B, S, H, D, workspace,
+    rc = dsa::sparse_attn_bf16_select_launch(q, win, cs, sink, &sel, nullptr, L, scale, o, B, S, H, D, workspace,
                                              (hipStream_t)stream);
     if (rc != 0) return rc < 0 ? rc : DSA_OK;
   }
@@ -230,6 +230,55 @@ int dsa_sparse_attn_select(const float* scores, int T, int index_topk, int start
   int rc = dsa_select(scores, B, S, T, index_topk, start_pos, ratio, W, offset, idx, L, stream);
   if (rc) return rc;
   return dsa_sparse_attn(q, win, comp, sink, idx, L, scale, o, dtype, B, S, H, D, workspace, workspace_bytes, stream);
+}
+
+int dsa_sparse_attn_step(const void* q_idx, const void* k_idx, int64_t k_batch_stride, const void* w, float w_scale,
+                         int H_I, int D_I, int T, int index_topk, int start_pos, int ratio, int W, const void* q,
+                         const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink, float scale, void* o,
+                         int dtype, int B, int S, int H, int D, float* scores, int32_t* idx, void* workspace,
+                         size_t workspace_bytes, dsa_stream_t stream) {
+  dsa::g_err[0] = 0;
+  if (dtype != DSA_F32 && dtype != DSA_BF16) return fail(DSA_ERR_DTYPE, "dsa_sparse_attn_step: dtype %d", dtype);
+  if (B < 0 || S < 0 || T < 0 || H_I <= 0 || D_I <= 0 || index_topk < 0 || start_pos < 0 || ratio <= 0)
+    return fail(DSA_ERR_SHAPE,
+                "dsa_sparse_attn_step: bad sizes B=%d S=%d T=%d H_I=%d D_I=%d index_topk=%d start_pos=%d ratio=%d", B,
+                S, T, H_I, D_I, index_topk, start_pos, ratio);
+  if (!win) return fail(DSA_ERR_NULL, "dsa_sparse_attn_step: window source missing");
+  const int Wc = dsa_window_cols(S, start_pos, W);
+  if (Wc < 0) return Wc;
+  dsa::g_err[0] = 0;
+  if (B == 0 || S == 0) return DSA_OK;
+  const int K = index_topk < T ? index_topk : T;
+  const int L = Wc + K;
+  // one launch: the decode attention kernel scores, selects and attends (index head dim 128)
+  if (dtype == DSA_BF16 && K > 0 && T <= 2048 && D_I == 128 && H_I <= 64 && q_idx && k_idx && w && scores && q &&
+      sink && o && (((uintptr_t)q | (uintptr_t)o | (uintptr_t)q_idx | (uintptr_t)k_idx) & 15) == 0 &&
+      k_batch_stride >= (int64_t)T * D_I && k_batch_stride % 8 == 0 &&
+      (int64_t)T <= ((int64_t)start_pos + S) / ratio && win->rows && win->format == DSA_KV_DENSE &&
+      win->n_rows <= 0x7FFFFFFF) {
+    int rc = check_src(win, "window", dtype, D, B, true);
+    if (rc) return rc;
+    rc = check_src(comp, "compressed", dtype, D, B, false);
+    if (rc) return rc;
+    const size_t need = dsa_sparse_attn_workspace_size(dtype, B, S, H, D, L);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+      return fail(DSA_ERR_WORKSPACE, "dsa_sparse_attn_step: workspace of %zu bytes needed, %zu given", need,
+                  workspace_bytes);
+    dsa::DecSelect sel{scores, T, K, start_pos, ratio, W, Wc, (int)win->n_rows, idx, (int64_t)L};
+    dsa::DecIndex ix{(const __bf16*)q_idx, (const __bf16*)k_idx, k_batch_stride, (const __bf16*)w, w_scale, H_I,
+                     scores};
+    dsa_kv_src empty{};
+    const dsa_kv_src* cs = (comp && comp->n_rows > 0) ? comp : &empty;
+    rc = dsa::sparse_attn_bf16_select_launch(q, win, cs, sink, &sel, &ix, L, scale, o, B, S, H, D, workspace,
+                                             (hipStream_t)stream);
+    if (rc != 0) return rc < 0 ? rc : DSA_OK;
+  }
+  // otherwise: the index scores, then the index rows and the attention
+  int rc = dsa_index_scores(q_idx, k_idx, k_batch_stride, w, w_scale, dtype, B, S, T, H_I, D_I, start_pos, ratio,
+                            scores, stream);
+  if (rc) return rc;
+  return dsa_sparse_attn_select(scores, T, index_topk, start_pos, ratio, W, q, win, comp, sink, scale, o, dtype, B, S,
+                                H, D, idx, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -113,6 +113,20 @@ struct DecSelect {
   int64_t ld_out;
 };
 
+// Index scores computed by the decode attention kernel itself (with a DecSelect): index queries
+// q_idx [Q][H_I][128], keys k_idx [B][T][128] (batch stride k_bstride elements), head weights
+// w [Q][H_I], all bf16; the scores go to scores_out [Q][T] (the DecSelect's scores), where the
+// query's workgroups exchange them.
+struct DecIndex {
+  const __bf16* q_idx;
+  const __bf16* k_idx;
+  int64_t k_bstride;
+  const __bf16* w;
+  float w_scale;
+  int H_I;
+  float* scores_out;
+};
+
 __device__ __forceinline__ int visible_rows(int start_pos, int t, int ratio) {
   return (start_pos + t + 1) / ratio;
 }

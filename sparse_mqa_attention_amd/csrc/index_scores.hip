@@ -11,7 +11,7 @@
 // 16 heads of row c, so the ReLU, the head weights and the head sum happen in registers and one
 // cross-half shuffle finishes each row.  Rows past c(t) are never multiplied: whole tiles past
 // the visibility edge only store -inf.
-#include "dsa_internal.h"
+#include "index_tile.h"
 
 namespace dsa {
 
@@ -20,13 +20,6 @@ namespace {
 constexpr int kIdxThreads = 256;  // 4 waves
 constexpr int kRowsPerWave = 64;
 constexpr int kRowsPerBlock = kIdxThreads / 64 * kRowsPerWave;  // 256
-
-// Physical 16-byte chunk of logical chunk `ch` in LDS row `r` (rows of NCH chunks).
-template <int NCH>
-__device__ __forceinline__ int qswz(int r, int ch) {
-  constexpr int M = NCH < 16 ? NCH - 1 : 15;
-  return ch ^ (r & M);
-}
 
 template <int DI, int MT, int QB>
 __global__ void __launch_bounds__(kIdxThreads)
@@ -100,24 +93,7 @@ index_scores_bf16_kernel(const __bf16* __restrict__ q_idx, const __bf16* __restr
         if (hf == 0 && j < T) out_row[j] = ninf;
         continue;
       }
-      float sum = 0.f;
-#pragma unroll
-      for (int m = 0; m < MT; ++m) {
-        f32x16 acc = {};
-        const int h = 32 * m + c;
-#pragma unroll
-        for (int s = 0; s < KS; ++s) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              &q_lds[(q * HP + h) * DI + qswz<NCH>(h, 2 * s + hf) * 8]);
-          acc = mfma32(a, kreg[n][s], acc);
-        }
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int hh = 32 * m + 8 * (e >> 2) + 4 * hf + (e & 3);
-          sum += fmaxf(acc[e], 0.f) * w_lds[q * HP + hh];
-        }
-      }
-      sum += shfl_xor(sum, 32);
+      const float sum = index_tile_sum<DI, MT>(q_lds + q * HP * DI, w_lds + q * HP, kreg[n], hf, c);
       if (hf == 0 && j < T) out_row[j] = j < ct ? w_scale * sum : ninf;
     }
   }

@@ -435,7 +435,7 @@ int sparse_attn_decode_launch(const __bf16* q, const unsigned char* win, int64_t
                               int64_t win_rs, const unsigned char* comp, int64_t comp_n, int64_t comp_bs,
                               int64_t comp_rs, const float* sink, const int32_t* idx, int L, float scale_log2,
                               __bf16* o, int B, int S, int H, int D, bool fp4, void* workspace,
-                              const DecSelect* sel, hipStream_t st);
+                              const DecSelect* sel, const DecIndex* ix, hipStream_t st);
 
 int sparse_attn_prefill_h16_launch(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
                                    const int32_t* idx, int L, float scale, void* o, int B, int S, int H, int D,
@@ -470,7 +470,8 @@ int sparse_attn_bf16_launch(const void* q, const dsa_kv_src* win, const dsa_kv_s
   // decode batches: two-phase kernel without partial outputs when its shape and residency fit
   const int drc = sparse_attn_decode_launch(a.q, a.win, a.win_n, a.win_bs, a.win_rs, a.comp,
                                             comp && comp->rows ? comp->n_rows : 0, a.comp_bs, a.comp_rs, sink, idx,
-                                            L, a.scale_log2, a.o, B, S, H, D, fp4, workspace, nullptr, st);
+                                            L, a.scale_log2, a.o, B, S, H, D, fp4, workspace, nullptr, nullptr,
+                                            st);
   if (drc != 0) return drc < 0 ? drc : 0;
   // prefill batches at head_dim 512 (bf16 or fp4 compressed rows): one workgroup per query
   const int prc = sparse_attn_prefill_h16_launch(q, win, comp, sink, idx, L, scale, o, B, S, H, D, st);
@@ -489,8 +490,8 @@ int sparse_attn_bf16_launch(const void* q, const dsa_kv_src* win, const dsa_kv_s
 // two-phase decode kernel applies, at most 2048 scores per row): one launch for top-k, window rows
 // and attention.  Returns 1 if launched, 0 if not applicable, <0 on error.
 int sparse_attn_bf16_select_launch(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
-                                   const DecSelect* sel, int L, float scale, void* o, int B, int S, int H, int D,
-                                   void* workspace, hipStream_t st) {
+                                   const DecSelect* sel, const DecIndex* ix, int L, float scale, void* o, int B, int S,
+                                   int H, int D, void* workspace, hipStream_t st) {
   const bool fp4 = comp && comp->rows && comp->format == DSA_KV_FP4_E4M3_G16;
   if (fp4) return 0;
   const unsigned char* comp_rows = comp && comp->rows ? (const unsigned char*)comp->rows : nullptr;
@@ -498,7 +499,7 @@ int sparse_attn_bf16_select_launch(const void* q, const dsa_kv_src* win, const d
                                    win->batch_stride * 2, win->row_stride * 2, comp_rows,
                                    comp_rows ? comp->n_rows : 0, comp_rows ? comp->batch_stride * 2 : 0,
                                    comp_rows ? comp->row_stride * 2 : 0, sink, nullptr, L, scale * kLog2e,
-                                   (__bf16*)o, B, S, H, D, false, workspace, sel, st);
+                                   (__bf16*)o, B, S, H, D, false, workspace, sel, ix, st);
 }
 
 size_t sparse_attn_bf16_workspace(int B, int S, int H, int D, int L, bool fp4) {

@@ -22,6 +22,7 @@
 // Blocks are numbered so that all NS workgroups of a query land on one XCD (dispatch assigns
 // consecutive workgroups to the 8 XCDs round-robin), keeping the rendezvous and the re-gather in
 // one L2.  What crosses HBM is each valid row once, q, o, and the small P (Q x 64 x L bf16).
+#include "index_tile.h"
 #include "topk_block.h"
 
 namespace dsa {
@@ -35,9 +36,10 @@ constexpr int kDecQueriesMax = 4096;
 constexpr float kLog2eD = 1.4426950408889634f;
 constexpr uint64_t kSpinTimeoutTicks = 20000000ull;  // 0.2 s of the 100 MHz constant-rate counter
 
-// Per query: arrivals and departures of its workgroups.  Zero when the code object loads; the
-// last workgroup of a query to leave resets both, so every call finds them at zero.
-__device__ uint32_t g_dec_sync[2 * kDecQueriesMax];
+// Per query: arrivals at the index-score exchange (kernels that score their own rows), arrivals
+// at the phase A/B rendezvous, and departures of its workgroups.  Zero when the code object
+// loads; the last workgroup of a query to leave resets all three, so every call finds them at 0.
+__device__ uint32_t g_dec_sync[3 * kDecQueriesMax];
 __device__ uint32_t g_dec_error;
 
 struct DecArgs {
@@ -63,6 +65,13 @@ struct DecArgs {
   int T, K, start_pos, ratio, W, Wc, offset;
   int32_t* idx_out;
   int64_t ld_out;
+  // index scores computed in the kernel (see DecIndex): scores then points at scores_out
+  const __bf16* q_idx;
+  const __bf16* k_idx;
+  int64_t k_bstride;
+  const __bf16* w_idx;
+  float w_scale;
+  int H_I;
 };
 
 template <int NS>
@@ -135,8 +144,9 @@ __device__ __forceinline__ uint32_t xcc_id() {
 
 // SKPT = 0: the index rows come from idx; SKPT > 0: each workgroup selects its query's index row
 // from the scores (window part, then the top-k part, exactly as the top-k kernels do), SKPT scores
-// per thread.
-template <int NS, int SKPT>
+// per thread.  IX = 1 (with SKPT > 0): the query's workgroups first compute those scores, each
+// for its share of the compressed rows, and exchange them through the scores buffer.
+template <int NS, int SKPT, int IX>
 __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
   using C = DecCfg<NS>;
   constexpr int XBUF_FLOATS = 4 * C::TA * 16 * 64;  // per wave, per tile: one partial S^T tile
@@ -200,14 +210,88 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
       if (tid + 256 * k < L) idx_lds[tid + 256 * k] = iv_reg[k];
     __syncthreads();
   } else {
-    {
-      const __bf16* qp = a.q + ((int64_t)q * kDH + head) * kDD + (kDD / 2) * dh + hf * 8;
+    const int t = q % a.S;
+    const int cvis = min(a.T, visible_rows(a.start_pos, t, a.ratio));
+    const __bf16* qp = a.q + ((int64_t)q * kDH + head) * kDD + (kDD / 2) * dh + hf * 8;
+    if constexpr (IX == 0) {  // the attention's query, in flight while the rows are selected
 #pragma unroll
       for (int k = 0; k < kDD / 32; ++k) qreg[k] = *reinterpret_cast<const bf16x8*>(qp + 16 * k);
     }
+    if constexpr (IX != 0) {
+      // ============================= index scores of compressed rows [j0, j1) of this query, with
+      // the index kernel's tile arithmetic; the query's workgroups exchange them through the
+      // scores buffer, in the L2 of the XCD they share
+      constexpr int DI = 128;
+      constexpr int NCH = DI / 8;
+      constexpr int KS = DI / 16;
+      const int hp = a.H_I > 32 ? 64 : 32;  // heads padded to whole MFMA tiles
+      const int tps = ((a.T + NS - 1) / NS + 31) & ~31;  // rows per workgroup, whole 32-row tiles
+      const int j0 = s * tps;
+      const int j1 = min(a.T, j0 + tps);
+      const int jw = j0 + 64 * wave;  // this wave's two tiles
+      const __bf16* kb = a.k_idx + (int64_t)bq * a.k_bstride;
+      // the keys first, then the index queries straight into LDS, so both are in flight at once
+      bf16x8 kreg[2][KS];
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const int j = jw + 32 * n + c;
+        const bool live = jw + 32 * n < min(j1, cvis) && j < j1;
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+          kreg[n][k] = live ? *reinterpret_cast<const bf16x8*>(kb + (int64_t)j * DI + hf * 8 + 16 * k) : bf16x8{};
+      }
+      // wave w copies LDS rows 4i .. 4i+3 for i = w, w+4, ...: lane l the 16 bytes that belong at
+      // physical chunk l%16 of row 4i + l/16 (the zero row past the real heads)
+      __bf16* qi_lds = reinterpret_cast<__bf16*>(rows);
+      float* wi_lds = reinterpret_cast<float*>(rows + 64 * DI * 2);
+      for (int i = wave; i < hp / 4; i += 4) {
+        const int h = 4 * i + (lane >> 4);
+        const int ch = qswz<NCH>(h, lane & 15);
+        const void* src = h < a.H_I ? (const void*)(a.q_idx + ((int64_t)q * a.H_I + h) * DI + ch * 8)
+                                    : (const void*)(g_dec_zero_row + ch * 16);
+        dma16_v(src, (DSA_LDS void*)(rows + i * 4 * DI * 2));
+      }
+      if (tid < hp) wi_lds[tid] = tid < a.H_I ? bf16_to_f32(a.w_idx[(int64_t)q * a.H_I + tid]) : 0.f;
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      float* srow = const_cast<float*>(a.scores) + (int64_t)q * a.T;
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const int jt = jw + 32 * n;
+        const int j = jt + c;
+        if (jt < j1) {
+          float v = -__builtin_inff();
+          if (jt < cvis) {  // a tile wholly past the visible rows is not multiplied
+            const float sum = hp == 32 ? index_tile_sum<DI, 1>(qi_lds, wi_lds, kreg[n], hf, c)
+                                       : index_tile_sum<DI, 2>(qi_lds, wi_lds, kreg[n], hf, c);
+            if (j < cvis) v = a.w_scale * sum;
+          }
+          if (hf == 0 && j < j1) srow[j] = v;
+        }
+      }
+      // every score of this workgroup has reached L2 before it counts itself in
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();  // also: the staged index queries are read no more
+      // the attention's query, in flight during the exchange and the selection
+#pragma unroll
+      for (int k = 0; k < kDD / 32; ++k) qreg[k] = *reinterpret_cast<const bf16x8*>(qp + 16 * k);
+      if (tid == 0) {
+        uint32_t* arrive_ix = &g_dec_sync[3 * q];
+        __hip_atomic_fetch_add(arrive_ix, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t t0 = wall_clock64();
+        int to = 0;
+        for (uint32_t it = 1; poll_load(arrive_ix) < (uint32_t)NS; ++it) {
+          if ((it & 15u) == 0u && wall_clock64() - t0 > kSpinTimeoutTicks) {
+            to = 1;
+            atomicOr(&g_dec_error, 1u);
+            break;
+          }
+        }
+        flags[0] = to;
+      }
+      __syncthreads();
+    }
     // this query's index row from its scores: Wc window entries, then the K top-k entries
-    const int t = q % a.S;
-    const int cvis = min(a.T, visible_rows(a.start_pos, t, a.ratio));
     for (int i = tid; i < a.Wc; i += 256) idx_lds[i] = topk_dev::window_entry(t, i, a.start_pos, a.W);
     if (cvis <= a.K) {  // every visible position is kept
       for (int i = tid; i < a.K; i += 256) idx_lds[a.Wc + i] = i < cvis ? i + a.offset : -1;
@@ -340,8 +424,8 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
   // reaches NS.  No cache-wide write-back or invalidate.  Nothing else is in flight here.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();  // also: every wave is done with phase A's rows
-  uint32_t* arrive = &g_dec_sync[2 * q];
-  uint32_t* depart = &g_dec_sync[2 * q + 1];
+  uint32_t* arrive = &g_dec_sync[3 * q + 1];
+  uint32_t* depart = &g_dec_sync[3 * q + 2];
   if (tid == 0) __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // =============================== phase B gather, independent of the other workgroups
@@ -377,7 +461,7 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
         break;
       }
     }
-    flags[0] = to;
+    flags[0] = IX != 0 ? (flags[0] | to) : to;
   }
   __builtin_amdgcn_s_waitcnt(0);  // the slices have landed
   __syncthreads();
@@ -483,6 +567,7 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
   // leaves, and that one clears the pair for the next call
   if (tid == 0 &&
       __hip_atomic_fetch_add(depart, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(NS - 1)) {
+    if (IX != 0) __hip_atomic_exchange(&g_dec_sync[3 * q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_exchange(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_exchange(depart, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -500,7 +585,7 @@ struct DecPlan {
   int ns, rps, lp, ok;
 };
 
-int g_resident_blocks[64][4] = {};  // per device, split count and selection: workgroups resident at once
+int g_resident_blocks[64][6] = {};  // per device and kernel variant: workgroups resident at once
 int g_xcd_local[64] = {};           // per device: 0 unknown, 1 XCD-local rendezvous valid, -1 not
 
 int xcd_local_mode(int dev, hipStream_t st) {
@@ -520,10 +605,11 @@ int xcd_local_mode(int dev, hipStream_t st) {
   return ok;
 }
 
-template <int NS, int SKPT>
+template <int NS, int SKPT, int IX>
 int resident_blocks(int dev) {
   int per_cu = 0, cus = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sparse_attn_decode_kernel<NS, SKPT>, 256, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, sparse_attn_decode_kernel<NS, SKPT, IX>, 256, 0) !=
+      hipSuccess)
     return 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
   return per_cu * cus;
@@ -554,28 +640,33 @@ size_t sparse_attn_decode_workspace(int B, int S, int H, int D, int L, bool fp4)
 
 // Returns 1 and launches when the two-phase decode path applies, 0 when the caller should use
 // the general kernel, or a negative error.  With sel set, the kernel selects the index rows itself
-// (idx is not read); that needs at most 2048 scores per row.
+// (idx is not read); that needs at most 2048 scores per row.  With ix set too, it also computes
+// those scores (index head dim 128, at most 64 index heads), which needs every workgroup of a
+// query on one XCD.
 int sparse_attn_decode_launch(const __bf16* q, const unsigned char* win, int64_t win_n, int64_t win_bs,
                               int64_t win_rs, const unsigned char* comp, int64_t comp_n, int64_t comp_bs,
                               int64_t comp_rs, const float* sink, const int32_t* idx, int L, float scale_log2,
                               __bf16* o, int B, int S, int H, int D, bool fp4, void* workspace,
-                              const DecSelect* sel, hipStream_t st) {
+                              const DecSelect* sel, const DecIndex* ix, hipStream_t st) {
   const DecPlan p = plan_decode(B * S, H, D, L, fp4);
   if (!p.ok) return 0;
   if (sel && (sel->T > 2048 || sel->T < 1 || sel->Wc + sel->K != L)) return 0;
+  if (ix && (!sel || ix->H_I < 1 || ix->H_I > 64 || ix->scores_out != sel->scores)) return 0;
   // slot codes hold row byte offsets in 32 bits; the copies move 16-byte pieces of rows
   if ((uint64_t)win_n * (uint64_t)win_rs >= (1ull << 31) || (uint64_t)comp_n * (uint64_t)comp_rs >= (1ull << 31))
     return 0;
   if ((((uintptr_t)win | (uintptr_t)comp) & 15) || ((win_rs | win_bs | comp_rs | comp_bs) & 15)) return 0;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  const int vi = (p.ns == 8 ? 0 : 1) + (sel ? 2 : 0);
+  const int vi = (p.ns == 8 ? 0 : 1) + (sel ? 2 : 0) + (ix ? 2 : 0);
   int& resident = g_resident_blocks[dev][vi];
   if (resident == 0)
-    resident = vi == 0 ? resident_blocks<8, 0>(dev)
-             : vi == 1 ? resident_blocks<16, 0>(dev)
-             : vi == 2 ? resident_blocks<8, 8>(dev)
-                       : resident_blocks<16, 8>(dev);
+    resident = vi == 0 ? resident_blocks<8, 0, 0>(dev)
+             : vi == 1 ? resident_blocks<16, 0, 0>(dev)
+             : vi == 2 ? resident_blocks<8, 8, 0>(dev)
+             : vi == 3 ? resident_blocks<16, 8, 0>(dev)
+             : vi == 4 ? resident_blocks<8, 8, 1>(dev)
+                       : resident_blocks<16, 8, 1>(dev);
   const int Q = B * S;
   if (Q * p.ns > resident) return 0;  // the rendezvous needs every workgroup resident at once
   DecArgs a{};
@@ -601,6 +692,7 @@ int sparse_attn_decode_launch(const __bf16* q, const unsigned char* win, int64_t
   a.Lp = p.lp;
   a.xcd_map = (Q % 8 == 0) ? 1 : 0;
   a.local = a.xcd_map && xcd_local_mode(dev, st);
+  if (ix && !a.local) return 0;  // the score exchange reads its siblings' plain stores from one L2
   if (sel) {
     a.scores = sel->scores;
     a.T = sel->T;
@@ -613,12 +705,22 @@ int sparse_attn_decode_launch(const __bf16* q, const unsigned char* win, int64_t
     a.idx_out = sel->idx_out;
     a.ld_out = sel->ld_out;
   }
+  if (ix) {
+    a.q_idx = ix->q_idx;
+    a.k_idx = ix->k_idx;
+    a.k_bstride = ix->k_bstride;
+    a.w_idx = ix->w;
+    a.w_scale = ix->w_scale;
+    a.H_I = ix->H_I;
+  }
   dim3 grid(Q * p.ns);
   switch (vi) {
-    case 0: hipLaunchKernelGGL((sparse_attn_decode_kernel<8, 0>), grid, dim3(256), 0, st, a); break;
-    case 1: hipLaunchKernelGGL((sparse_attn_decode_kernel<16, 0>), grid, dim3(256), 0, st, a); break;
-    case 2: hipLaunchKernelGGL((sparse_attn_decode_kernel<8, 8>), grid, dim3(256), 0, st, a); break;
-    default: hipLaunchKernelGGL((sparse_attn_decode_kernel<16, 8>), grid, dim3(256), 0, st, a); break;
+    case 0: hipLaunchKernelGGL((sparse_attn_decode_kernel<8, 0, 0>), grid, dim3(256), 0, st, a); break;
+    case 1: hipLaunchKernelGGL((sparse_attn_decode_kernel<16, 0, 0>), grid, dim3(256), 0, st, a); break;
+    case 2: hipLaunchKernelGGL((sparse_attn_decode_kernel<8, 8, 0>), grid, dim3(256), 0, st, a); break;
+    case 3: hipLaunchKernelGGL((sparse_attn_decode_kernel<16, 8, 0>), grid, dim3(256), 0, st, a); break;
+    case 4: hipLaunchKernelGGL((sparse_attn_decode_kernel<8, 8, 1>), grid, dim3(256), 0, st, a); break;
+    default: hipLaunchKernelGGL((sparse_attn_decode_kernel<16, 8, 1>), grid, dim3(256), 0, st, a); break;
   }
   const int rc = check_launch("sparse_attn_decode");
   return rc ? rc : 1;

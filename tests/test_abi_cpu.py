@@ -25,7 +25,7 @@ def dsa():
 def test_header_declares_the_step():
     names = _declared()
     for n in ["dsa_index_scores", "dsa_topk", "dsa_window_idx", "dsa_select", "dsa_sparse_attn",
-              "dsa_sparse_attn_select", "dsa_last_error",
+              "dsa_sparse_attn_select", "dsa_sparse_attn_step", "dsa_last_error",
               "dsa_abi_version", "dsa_sparse_attn_workspace_size", "dsa_window_cols"]:
         assert n in names
 
@@ -90,6 +90,22 @@ def test_argument_errors_without_launch(dsa):
                nul, 0, nul) == 0
     assert sel(vp(16), 10, 8, 0, 4, 4, vp(16), ctypes.byref(src0), None, vp(16), 1.0, vp(16), 0, 1, 1, 1, 64, nul,
                nul, 0, nul) == -1
+    # the whole step: dtype, sizes, missing window source, empty batch
+    step = lib.dsa_sparse_attn_step
+    common = (vp(16), vp(16), 128 * 10, vp(16), 1.0)
+    assert step(*common, 32, 128, 10, 8, 0, 4, 4, vp(16), ctypes.byref(src0), None, vp(16), 1.0, vp(16), 7, 1, 1, 1,
+                64, vp(16), nul, nul, 0, nul) == -3
+    assert step(*common, 32, 128, 10, 8, 0, 0, 4, vp(16), ctypes.byref(src0), None, vp(16), 1.0, vp(16), 1, 1, 1, 1,
+                64, vp(16), nul, nul, 0, nul) == -2  # ratio 0
+    assert step(*common, 0, 128, 10, 8, 0, 4, 4, vp(16), ctypes.byref(src0), None, vp(16), 1.0, vp(16), 1, 1, 1, 1,
+                64, vp(16), nul, nul, 0, nul) == -2  # no index heads
+    assert step(*common, 32, 128, 10, 8, 0, 4, 4, vp(16), None, None, vp(16), 1.0, vp(16), 1, 1, 1, 1, 64, vp(16),
+                nul, nul, 0, nul) == -1
+    assert step(*common, 32, 128, 10, 8, 0, 4, 4, vp(16), ctypes.byref(src0), None, vp(16), 1.0, vp(16), 1, 0, 1, 1,
+                64, vp(16), nul, nul, 0, nul) == 0
+    # T beyond what the queries can see is the index scores' shape error
+    assert step(*common, 32, 128, 10, 8, 0, 4, 4, vp(16), ctypes.byref(src0), None, vp(16), 1.0, vp(16), 1, 1, 4, 1,
+                64, vp(16), nul, nul, 0, nul) == -2
     # sparse attention: unsupported head_dim, missing window source, bad format, workspace
     src = dsa.DsaKvSrc()
     src.rows = 16

@@ -378,6 +378,56 @@ def test_sparse_attn_select(B, T, ctx, kind):
         assert err <= ATTN_TOL["bf16"], err
 
 
+# ------------------------------------------------------------------------ the whole step in one call
+@pytest.mark.parametrize("B,T,ctx,H_I", [
+    (32, 2048, 8192, 32),   # decode, one launch: 8 workgroups per query score 256 rows each
+    (5, 1999, 7996, 64),    # 16 workgroups per query, two MFMA tiles of index heads, ragged tail
+    (3, 300, 1200, 40),     # fewer visible rows than index_topk: all kept, -1 tail
+    (16, 100, 400, 8),      # most workgroups score no rows
+    (4, 4000, 16000, 32),   # more than 2048 scores per row: index scores, then the select call
+])
+def test_sparse_attn_step(B, T, ctx, H_I):
+    """dsa_sparse_attn_step gives the bits of dsa_index_scores followed by dsa_sparse_attn_select
+    (scores, index rows, output), and those match the oracle; three calls in a row."""
+    dsa = _dsa()
+    _log(f"whole step case B={B} T={T} ctx={ctx} H_I={H_I}")
+    H, D, nw, K, ratio, S, DI = 64, 512, 128, 512, 4, 1, 128
+    sp = ctx - 1
+    g = torch.Generator().manual_seed(B * 13 + T)
+    q = torch.randn(B, S, H, D, generator=g).to(torch.bfloat16)
+    kv_win = torch.randn(B, nw, D, generator=g).to(torch.bfloat16)
+    kv_comp = torch.randn(B, T, D, generator=g).to(torch.bfloat16)
+    sink = torch.randn(H, generator=g)
+    qI = torch.randn(B, S, H_I, DI, generator=g).to(torch.bfloat16)
+    kI = torch.randn(B, T + 8, DI, generator=g).to(torch.bfloat16)[:, :T]  # batch stride larger than T*DI
+    w = (torch.randn(B, S, H_I, generator=g) * 0.5).to(torch.bfloat16)
+    scale, w_scale = D ** -0.5, DI ** -0.5 * H_I ** -0.5
+    dev = [t.to(DEV) for t in (qI, kI, w, q, kv_win, kv_comp, sink)]
+    kw = dict(index_topk=K, start_pos=sp, ratio=ratio, W=nw, scale=scale)
+    # the two calls the step stands for
+    ref_scores = dsa.dsa_index_scores(dev[0], dev[1], dev[2], w_scale, sp, ratio)
+    ref_o, ref_idx = dsa.dsa_sparse_attn_select(ref_scores, *dev[3:], **kw)
+    ref_scores, ref_o, ref_idx = ref_scores.cpu().numpy(), ref_o.float().cpu().numpy(), ref_idx.cpu().numpy()
+    # against the oracle: scores within the fp32 bound, top-k by the parity rules, attention
+    _check_scores(ref_scores, qI, kI.contiguous(), w, w_scale, sp, ratio, ctx="step")
+    exp_scores = oracle.index_scores(qI.float().numpy().astype(np.float64), kI.float().numpy().astype(np.float64),
+                                     w.float().numpy().astype(np.float64), w_scale, sp, ratio)
+    c = int(min(T, oracle.visible_count(0, sp, ratio)))
+    win = oracle.window_rows(nw, B, S, sp)
+    for b in range(B):
+        np.testing.assert_array_equal(ref_idx[b, 0, :win.shape[-1]], win[b, 0])
+        check_topk_row(ref_idx[b, 0, win.shape[-1]:], exp_scores[b, 0], min(K, T), c, nw, ctx=f"step ({b},0)")
+    exp_o = oracle.sparse_attn(q, oracle.kv_concat(kv_win, kv_comp), sink, ref_idx, scale)
+    err = max_abs_err(ref_o, exp_o)
+    assert err <= ATTN_TOL["bf16"], err
+    for call in range(3):
+        o, idx, scores = dsa.dsa_sparse_attn_step(*dev, w_scale=w_scale, **kw)
+        np.testing.assert_array_equal(scores.cpu().numpy(), ref_scores)
+        np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+        np.testing.assert_array_equal(o.float().cpu().numpy(), ref_o)
+        _log(f"  call {call}: same bits as the two calls; attention max abs err {err:.3e}")
+
+
 # ------------------------------------------------------------------------ two-phase decode path
 @pytest.mark.parametrize("B,S,L,nc,inval", [
     (32, 1, 640, 2048, 0.0),   # 8 splits, XCD-grouped blocks
