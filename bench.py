@@ -41,7 +41,23 @@ def _args():
     p.add_argument("--workload", default="decode_b32_ctx8k")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device copy of MIB MiB three times (scale of the HBM byte counters)")
     return p.parse_args()
+
+
+def copy_calibration(mib: int):
+    """A plain device-to-device copy of known size, three times: reads and writes mib MiB each."""
+    import torch
+
+    n = mib << 20
+    x = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
 
 
 def kernel_src_sha() -> str:
@@ -130,6 +146,9 @@ def cpu_baseline(w, cpu_in, target_s: float):
 # ---------------------------------------------------------------------------- GPU run
 def main():
     a = _args()
+    if a.copy_calibration:
+        copy_calibration(a.copy_calibration)
+        return
     if a.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {a.gpus}); the path shards by batch/query "
               "without collectives and is measured at one GPU's share", file=sys.stderr)
