@@ -45,7 +45,11 @@ __device__ __forceinline__ void global_to_lds16(const void* gptr, DSA_LDS void* 
 // instruction per wave).  The s_nop gives the one wait state a copy needs after the M0 write that
 // sets its LDS base.  _s forms take the row base in scalar registers and a per-lane 32-bit offset.
 
-// A wave-uniform pointer, placed in scalar registers.
+// A wave-uniform pointer, placed in scalar registers.  The registers are written by a VALU
+// instruction (v_readfirstlane): a vector memory instruction that takes them as its scalar address
+// must come at least 5 wait states later, and the compiler does not count wait states for an
+// address consumed inside inline asm.  The _s copy helpers below therefore take bases formed by
+// scalar instructions (or computed well before), except dma4_s, which waits itself.
 __device__ __forceinline__ const void* uniform_ptr(const void* p) {
   const uint64_t v = (uint64_t)(uintptr_t)p;
   const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
@@ -57,9 +61,11 @@ __device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, const 
                "{m0}"((uint32_t)(uintptr_t)lds_base)
                : "memory");
 }
+// (the base comes straight from v_readfirstlane: s_nop 4 gives the 5 wait states before the
+// copy reads it, which also cover the one the M0 write needs)
 __device__ __forceinline__ void dma4_s(const void* sbase, uint32_t voff, const DSA_LDS void* lds_base) {
   sbase = uniform_ptr(sbase);
-  asm volatile("s_nop 0\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"((uint32_t)(uintptr_t)lds_base)
+  asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" ::"v"(voff), "s"(sbase), "{m0}"((uint32_t)(uintptr_t)lds_base)
                : "memory");
 }
 __device__ __forceinline__ void dma16_v(const void* gptr, const DSA_LDS void* lds_base) {
