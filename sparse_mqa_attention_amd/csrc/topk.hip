@@ -44,14 +44,20 @@ topk_kernel(const float* __restrict__ scores, int S, int T, int K, int start_pos
 // Many rows (prefill): one wave per row and no workgroup barriers.  Lane l holds the keys of
 // positions 64g + l (g < KPL) in registers (invisible positions get key 0, below every real
 // key).  The radix select takes 8-bit digits, from the highest bit where the row's keys differ,
-// through a wave-private 256-bin LDS histogram.  The kept positions leave in
+// through a wave-private 256-bin LDS histogram kept in kWR copies (lane l counts into copy
+// l % kWR, the copies kWP ints apart so one bin's copies sit in different banks: the first pass
+// sees whole exponent ranges share a bin, and atomics to one address serialise).  It stops as
+// soon as the chosen digit holds exactly the keys still to be taken.  The kept positions leave in
 // ascending order through ballot/mbcnt prefix counts per group g, which also hand the ties at the
 // threshold to the lowest positions.
+constexpr int kWR = 4;    // histogram copies per wave
+constexpr int kWP = 257;  // ints between copies
+
 template <int KPL>
 __global__ void __launch_bounds__(256)
 topk_wave_kernel(const float* __restrict__ scores, int rows, int S, int T, int K, int start_pos, int ratio,
                  int offset, int32_t* __restrict__ idx, int64_t ld_idx, int W, int Wc) {
-  __shared__ __attribute__((aligned(16))) int whist[4][256];
+  __shared__ int whist[4][kWR * kWP];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int row = blockIdx.x * 4 + wave;  // b*S + t
@@ -104,13 +110,19 @@ topk_wave_kernel(const float* __restrict__ scores, int rows, int S, int T, int K
   uint32_t prefix = kand & ~diff;
   uint32_t mask = ~diff;
   int remaining = K;
+  bool exact = false;  // exactly `remaining` visible keys match `prefix` under `mask`
   if (diff != 0u) {
     int hb = 31 - __builtin_clz(diff);
+    // lane l owns digits 252-4l .. 255-4l in every copy: it clears them here and after each pass
+#pragma unroll
+    for (int r = 0; r < kWR; ++r)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) hist[r * kWP + 252 - 4 * lane + j] = 0;
+    int* hcopy = hist + (lane % kWR) * kWP;
     while (true) {
       const int lo = hb >= 7 ? hb - 7 : 0;
       const int width = hb - lo + 1;
       const uint32_t dmask = ((width == 32) ? 0xFFFFFFFFu : ((1u << width) - 1u)) << lo;
-      *reinterpret_cast<int4*>(hist + 4 * lane) = int4{0, 0, 0, 0};
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       // constant trip counts (an early exit would stop the full unroll and push key[] out to
@@ -121,14 +133,23 @@ topk_wave_kernel(const float* __restrict__ scores, int rows, int S, int T, int K
         if (g0 < ng) {
 #pragma unroll
           for (int g = g0; g < g0 + 16 && g < KPL; ++g)
-            if (key[g] != 0u && (key[g] & mask) == prefix) atomicAdd(&hist[(key[g] & dmask) >> lo], 1);
+            if (key[g] != 0u && (key[g] & mask) == prefix) atomicAdd(&hcopy[(key[g] & dmask) >> lo], 1);
         }
       }
       __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
       __builtin_amdgcn_wave_barrier();
-      // lane l takes digits 255-4l .. 252-4l (largest first); counts of keys in larger digits
-      const int4 h4 = *reinterpret_cast<const int4*>(hist + 252 - 4 * lane);
-      const int c0 = h4.w, c1 = h4.z, c2 = h4.y, c3 = h4.x;  // digits 255-4l, 254-4l, 253-4l, 252-4l
+      // lane l takes digits 255-4l .. 252-4l (largest first), summed over the copies (and cleared
+      // for the next pass); counts of keys in larger digits
+      int hc[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (int r = 0; r < kWR; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          int* hp = hist + r * kWP + 252 - 4 * lane + j;
+          hc[j] += *hp;
+          *hp = 0;
+        }
+      const int c0 = hc[3], c1 = hc[2], c2 = hc[1], c3 = hc[0];  // digits 255-4l, 254-4l, 253-4l, 252-4l
       const int mine = c0 + c1 + c2 + c3;
       int incl = mine;
 #pragma unroll
@@ -140,29 +161,51 @@ topk_wave_kernel(const float* __restrict__ scores, int rows, int S, int T, int K
       const bool here = excl < remaining && incl >= remaining;
       const uint64_t hmask = __builtin_amdgcn_ballot_w64(here);
       const int src = __builtin_ctzll(hmask);
-      int digit = 0, above = 0;
+      int digit = 0, above = 0, in_digit = 0;
       if (lane == src) {
         int a = excl;
         if (a + c0 >= remaining) {
           digit = 255 - 4 * lane;
+          in_digit = c0;
         } else if ((a += c0) + c1 >= remaining) {
           digit = 254 - 4 * lane;
+          in_digit = c1;
         } else if ((a += c1) + c2 >= remaining) {
           digit = 253 - 4 * lane;
+          in_digit = c2;
         } else {
           a += c2;
           digit = 252 - 4 * lane;
+          in_digit = c3;
         }
         above = a;
       }
       digit = __shfl(digit, src, 64);
       above = __shfl(above, src, 64);
+      in_digit = __shfl(in_digit, src, 64);
       remaining -= above;
       prefix |= ((uint32_t)digit << lo);
       mask |= dmask;
+      if (in_digit == remaining) {
+        exact = true;  // every key of the chosen digit is taken
+        break;
+      }
       if (lo == 0) break;
       hb = lo - 1;
     }
+  }
+  if (exact) {
+    // keep every visible key at or above the chosen digit, in position order
+    int base = 0;
+#pragma unroll
+    for (int g = 0; g < KPL; ++g) {
+      const bool keep = key[g] != 0u && (key[g] & mask) >= prefix;
+      const uint64_t kb = __builtin_amdgcn_ballot_w64(keep);
+      const int pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(kb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)kb, 0));
+      if (keep) out[pos] = 64 * g + lane + offset;
+      base += __builtin_popcountll(kb);
+    }
+    return;
   }
   const uint32_t tau = prefix;  // key of the K-th best visible score (a real key, so never 0)
   // keep keys > tau and the first `remaining` keys == tau, in position order (invisible keys are 0)
