@@ -124,28 +124,33 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
   const void* comp_u = uniform_ptr(comp_b);
   const void* zero_u = uniform_ptr(g_h16_zero_row);
 
-  // ---- prologue: the index row into LDS (copies, -1 past L), this wave's query heads, the sink ----
+  // ---- prologue: the index row into LDS (copies, -1 past L), this wave's query heads and the
+  // sink, in that order, so that the index row can be used while the rest is still in flight ----
   for (int i0 = 64 * wave; i0 < L; i0 += 256) {
     if (i0 + lane < L) dma4_s(irow + i0, (uint32_t)lane * 4u, (DSA_LDS void*)(idx_lds + i0));
   }
   for (int i = L + tid; i < ntiles * kHTile; i += 256) idx_lds[i] = -1;
   if (tid == 0) *tset = 0u;
-  // B operand of QK: lane (g, c) holds dims 32s + 8g .. 32s + 8g + 7 of head c
+  // B operand of QK: lane (g, c) holds dims 32s + 8g .. 32s + 8g + 7 of head c.  Exactly 16 loads
+  // and one sink load, unconditional (lanes of heads past H read head H-1: finite values whose
+  // results are never stored), so that waiting for all but the last 17 vector memory operations
+  // waits for the index row only; the sink is scaled where it is used, at the end.
   bf16x8 qreg[16];
   {
     const __bf16* qp = a.q + ((int64_t)qi * a.H + min(head, a.H - 1)) * kHD + 8 * g;
 #pragma unroll
-    for (int s = 0; s < 16; ++s) qreg[s] = head < a.H ? *reinterpret_cast<const bf16x8*>(qp + 32 * s) : bf16x8{};
+    for (int s = 0; s < 16; ++s) qreg[s] = *reinterpret_cast<const bf16x8*>(qp + 32 * s);
   }
-#pragma unroll
-  for (int s = 0; s < 16; ++s) asm volatile("" : "+a"(qreg[s]));
-  const float sink2 = head < a.H ? a.sink[head] * kHLog2e : 0.f;
-  wait_vmcnt<0>();
+  const float sink_raw = a.sink[min(head, a.H - 1)];
+  wait_vmcnt<17>();
   __syncthreads();
   // index -> slot code: byte offset from the window or compressed base (bit 0 set for the
-  // latter), or 2 for an empty slot; row offsets fit 32 bits (checked at launch)
-  for (int i = tid; i < ntiles * kHTile; i += 256) {
-    const int iv = idx_lds[i];
+  // latter), or 2 for an empty slot; row offsets fit 32 bits (checked at launch).  Each wave
+  // converts 64 consecutive slots at a time and marks the tiles among them that hold a valid slot.
+  for (int i0 = 64 * wave; i0 < ntiles * kHTile; i0 += 256) {
+    const int i = i0 + lane;
+    const bool in = i < ntiles * kHTile;
+    const int iv = in ? idx_lds[i] : -1;
     uint32_t code;
     if (iv < 0)
       code = 2u;
@@ -153,11 +158,8 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
       code = (uint32_t)iv * (uint32_t)a.win_rs;
     else
       code = FP4 ? ((uint32_t)(iv - win_n) << 4) | 1u : (uint32_t)(iv - win_n) * (uint32_t)a.comp_rs | 1u;
-    idx_lds[i] = (int)code;
-  }
-  __syncthreads();
-  for (int i0 = 64 * wave; i0 < ntiles * kHTile; i0 += 256) {
-    const uint64_t v = __builtin_amdgcn_ballot_w64(i0 + lane < ntiles * kHTile && !(idx_lds[i0 + lane] & 2));
+    if (in) idx_lds[i] = (int)code;
+    const uint64_t v = __builtin_amdgcn_ballot_w64(in && iv >= 0);
     const uint32_t bits = (v & 0xFFFFFFFFull ? 1u : 0u) | (v >> 32 ? 2u : 0u);
     if (lane == 0 && bits) atomicOr(tset, bits << (i0 / kHTile));
   }
@@ -282,6 +284,8 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
         wait_vmcnt<0>();
     }
     __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 16; ++s) asm volatile("" : "+a"(qreg[s]));
     const unsigned char* kp = ring + k_base;
 #pragma unroll
     for (int i = 0; i < 32; ++i) ch[2 * (i & 1) + ((i >> 1) & 1)] = mfma16(kread(kp, i), qreg[i >> 1], ch[2 * (i & 1) + ((i >> 1) & 1)]);
@@ -397,6 +401,7 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
   wait_vmcnt<0>();
 
   if (head >= a.H) return;
+  const float sink2 = sink_raw * kHLog2e;
   float l_tot = l_run + shfl_xor(l_run, 16);
   l_tot += shfl_xor(l_tot, 32);
   const float mf = fmaxf(m_run, sink2);
