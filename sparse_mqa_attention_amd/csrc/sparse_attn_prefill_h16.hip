@@ -38,9 +38,12 @@ constexpr float kHMinit = -1.0e30f;
 
 constexpr int kHRing = kHNST * kHTileB;
 constexpr int kHMasks = kHNST * 8 + 4;  // per slot: valid rows, fp4 rows (a byte per wave each); tile set
-constexpr int kHRaw = kHPitch - 288;    // an fp4 row lands raw in the last 288 bytes of its pitch
 constexpr int kHDummy = 1024;  // write target of the decode for rows that are not fp4
-constexpr int kHLds = kHRing + kHMasks + 12 + kHMaxSlots * 4 + kHDummy;
+// per ring slot and wave: the fp4 scale bytes of the wave's 8 rows (the first 256 of 1024 bytes)
+constexpr int kHStage = 1024;
+constexpr int kHStageOff = kHRing + kHMasks + 12 + kHMaxSlots * 4 + kHDummy;
+constexpr int kHLds = kHStageOff + kHNST * 4 * kHStage;
+static_assert(kHStageOff % 16 == 0, "stage alignment");
 static_assert(kHLds <= 160 * 1024, "LDS budget");
 
 __device__ __forceinline__ int h_row(int r) { return kHPitch * r; }
@@ -75,9 +78,6 @@ __device__ __forceinline__ void h_dma16(const void* sbase, uint32_t voff, const 
                "{m0}"((uint32_t)(uintptr_t)lds_base));
 }
 
-__device__ __forceinline__ void h_dma16_v(const void* gptr, const DSA_LDS void* lds_base) {
-  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "{m0}"((uint32_t)(uintptr_t)lds_base));
-}
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -96,6 +96,7 @@ __device__ __forceinline__ void h_scale(f32x4& v, float f) {
 
 template <bool FP4>
 __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a) {
+  constexpr int kHCopies = FP4 ? 9 : 8;  // copy instructions per wave and tile
   __shared__ __attribute__((aligned(1024))) unsigned char smem[kHLds];
   unsigned char* ring = smem;
   unsigned char* masks = smem + kHRing;                                   // [NST][2][4] bytes
@@ -123,6 +124,7 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
   const void* win_u = uniform_ptr(win_b);
   const void* comp_u = uniform_ptr(comp_b);
   const void* zero_u = uniform_ptr(g_h16_zero_row);
+  const void* csc_u = FP4 ? uniform_ptr(csc_b) : zero_u;
 
   // ---- prologue: the index row into LDS (copies, -1 past L), this wave's query heads and the
   // sink, in that order, so that the index row can be used while the rest is still in flight ----
@@ -157,7 +159,7 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
     else if (iv < win_n)
       code = (uint32_t)iv * (uint32_t)a.win_rs;
     else
-      code = FP4 ? ((uint32_t)(iv - win_n) << 4) | 1u : (uint32_t)(iv - win_n) * (uint32_t)a.comp_rs | 1u;
+      code = (uint32_t)(iv - win_n) * (uint32_t)a.comp_rs | 1u;
     if (in) idx_lds[i] = (int)code;
     const uint64_t v = __builtin_amdgcn_ballot_w64(in && iv >= 0);
     const uint32_t bits = (v & 0xFFFFFFFFull ? 1u : 0u) | (v >> 32 ? 2u : 0u);
@@ -169,11 +171,13 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
   uint32_t pend = __builtin_amdgcn_readfirstlane(*tset);
   const int nt = __builtin_popcount(pend);
 
-  // copies of this wave's 8 rows of position k (one wave instruction per row; an empty slot
-  // copies the zero row; an fp4 row copies its 256 nibble bytes and 32 scale bytes into the tail
-  // of its pitch) and the tile's valid-row and fp4-row bytes
-  // slot codes: byte offset of the row from its base, bit 0 = compressed row, bit 1 = empty slot
-  // (the zero row); for an fp4 compressed row the offset field holds the row number
+  // copies of this wave's 8 rows of position k and the tile's valid-row and fp4-row bytes.  Every
+  // row is one wave instruction from a scalar base (slot codes: byte offset of the row from its
+  // base, bit 0 = compressed row, bit 1 = empty slot, read from the zero row).  An fp4 row (256
+  // nibble bytes) is read by lanes l and l+16, l+32, l+48 alike, so nothing past it is read; the
+  // copies land in the first 1024 bytes of its pitch, where the decode writes the bf16 row.  One
+  // more instruction per tile fetches the 32 scale bytes of each of the 8 rows into the wave's
+  // stage of the slot (from the zero row when the tile has no fp4 row of this wave).
   auto issue = [&](int k) {
     const int tile = __builtin_ctz(pend);
     pend &= pend - 1u;
@@ -186,18 +190,21 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
       masks[slot * 8 + 4 + wave] = (unsigned char)fbits;
     }
     unsigned char* tb = ring + slot * kHTileB;
+    const uint32_t fold = (uint32_t)(lane & 48) * 16u;  // lane*16 - fold = (lane mod 16)*16
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const uint32_t x = (uint32_t)__builtin_amdgcn_readlane(myidx, r);
-      if (FP4 && (x & 1u)) {
-        const int64_t cr = x >> 4;
-        const unsigned char* src =
-            lane < 16 ? comp_b + cr * a.comp_rs + lane * 16 : csc_b + cr * a.csc_rs + (lane - 16) * 16;
-        if (lane < 18) h_dma16_v(src, (DSA_LDS void*)(tb + h_row(8 * wave + r) + kHRaw));
-      } else {
-        h_dma16(slot_base(x, win_u, comp_u, zero_u), (uint32_t)lane * 16u + (x & ~15u),
-                (DSA_LDS void*)(tb + h_row(8 * wave + r)));
-      }
+      const uint32_t voff = (uint32_t)lane * 16u - (FP4 ? (x & 1u) * fold : 0u);
+      h_dma16(slot_base(x, win_u, comp_u, zero_u), voff + (x & ~15u), (DSA_LDS void*)(tb + h_row(8 * wave + r)));
+    }
+    if constexpr (FP4) {
+      // lane l (mod 16): 16 of the 32 scale bytes of row (l mod 16)/2 (scale rows are 32 bytes for
+      // 256-byte nibble rows, so a row's byte offset / 8 is its scale row's); other rows re-read
+      // scale row 0
+      const uint32_t sc = (uint32_t)idx_lds[tile * kHTile + 8 * wave + ((lane & 15) >> 1)];
+      const uint32_t soff = ((sc & 1u) ? ((sc & ~15u) >> 3) : 0u) + (uint32_t)(lane & 1) * 16u;
+      h_dma16(fbits ? csc_u : zero_u, fbits ? soff : 0u,
+              (DSA_LDS void*)(smem + kHStageOff + (slot * 4 + wave) * kHStage));
     }
   };
   // fp4 rows of position k that this wave copied, decoded in place (it has waited for its own
@@ -211,11 +218,12 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
       const uint32_t fb = __builtin_amdgcn_readfirstlane(masks[slot * 8 + 4 + wave]);
       if (fb != 0u) {
         unsigned char* tb = ring + slot * kHTileB + h_row(8 * wave);
+        const unsigned char* stg = smem + kHStageOff + (slot * 4 + wave) * kHStage;
         uint32_t word[8], scb[8];
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-          word[r] = *reinterpret_cast<const uint32_t*>(tb + h_row(r) + kHRaw + 4 * lane);
-          scb[r] = tb[h_row(r) + kHRaw + 256 + (lane >> 1)];
+          word[r] = *reinterpret_cast<const uint32_t*>(tb + h_row(r) + 4 * lane);
+          scb[r] = stg[32 * r + (lane >> 1)];
         }
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
@@ -269,7 +277,7 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
     if constexpr (FP4) {
       // positions 0 and 1 landed (own copies) and decoded before the first QK
       if (nt > 2)
-        wait_vmcnt<8>();
+        wait_vmcnt<kHCopies>();
       else
         wait_vmcnt<0>();
       decode(0);
@@ -277,9 +285,9 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
     } else {
       const int later0 = min(kHNST - 2, nt - 1);
       if (later0 >= 2)
-        wait_vmcnt<16>();
+        wait_vmcnt<2 * kHCopies>();
       else if (later0 == 1)
-        wait_vmcnt<8>();
+        wait_vmcnt<kHCopies>();
       else
         wait_vmcnt<0>();
     }
@@ -296,7 +304,7 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
     // tile k+1 has landed once at most the copies of tile k+2 are out; the barrier also means every
     // wave is done with tile k-1, whose slot is refilled below
     if (k + 2 < nt)
-      wait_vmcnt<8>();
+      wait_vmcnt<kHCopies>();
     else
       wait_vmcnt<0>();
     __syncthreads();
@@ -391,7 +399,7 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
       // the next iteration's barrier publishes it before its QK
       if (k + 2 < nt) {
         if (k + 3 < nt)
-          wait_vmcnt<8>();
+          wait_vmcnt<kHCopies>();
         else
           wait_vmcnt<0>();
         decode(k + 2);
@@ -453,7 +461,10 @@ int sparse_attn_prefill_h16_launch(const void* q, const dsa_kv_src* win, const d
   // slot codes hold row byte offsets (fp4: row numbers) in 32 bits; the softmax folds a positive
   // scale into exp2
   if (!(scale > 0.f) || (uint64_t)a.win_n * (uint64_t)a.win_rs >= (1ull << 31)) return 0;
-  if (a.comp && (uint64_t)comp->n_rows * (uint64_t)(fp4 ? 16 : a.comp_rs) >= (1ull << 31)) return 0;
+  if (a.comp && (uint64_t)comp->n_rows * (uint64_t)a.comp_rs >= (1ull << 31)) return 0;
+  // fp4 rows: 256 nibble bytes and 32 scale bytes per row, densely strided (a row's byte offset
+  // / 8 is then its scale row's)
+  if (fp4 && (a.comp_rs != kHD / 2 || a.csc_rs != kHD / 16)) return 0;
   a.sink = sink;
   a.idx = idx;
   a.L = L;
