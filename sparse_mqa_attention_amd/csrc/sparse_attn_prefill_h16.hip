@@ -178,10 +178,14 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
   // copies land in the first 1024 bytes of its pitch, where the decode writes the bf16 row.  One
   // more instruction per tile fetches the 32 scale bytes of each of the 8 rows into the wave's
   // stage of the slot (from the zero row when the tile has no fp4 row of this wave).
+  // the slot codes of the next tile to copy (lane l: row 8*wave + l%8), read one issue ahead so
+  // the read is off the path from the barrier to the copies
+  int nidx = pend ? idx_lds[__builtin_ctz(pend) * kHTile + 8 * wave + (lane & 7)] : 0;
+  // (fp4: lane l also holds the code of row (l mod 16)/2, for the scale copy)
+  int nsc = (FP4 && pend) ? idx_lds[__builtin_ctz(pend) * kHTile + 8 * wave + ((lane & 15) >> 1)] : 0;
   auto issue = [&](int k) {
-    const int tile = __builtin_ctz(pend);
-    pend &= pend - 1u;
-    const int myidx = idx_lds[tile * kHTile + 8 * wave + (lane & 7)];
+    pend &= pend - 1u;  // the tile being copied, whose codes are already in nidx (and nsc)
+    const int myidx = nidx;
     const int slot = k % kHNST;
     const uint32_t vbits = (uint32_t)__builtin_amdgcn_ballot_w64(lane < 8 && !(myidx & 2));
     const uint32_t fbits = FP4 ? (uint32_t)__builtin_amdgcn_ballot_w64(lane < 8 && (myidx & 1)) : 0u;
@@ -201,10 +205,14 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
       // lane l (mod 16): 16 of the 32 scale bytes of row (l mod 16)/2 (scale rows are 32 bytes for
       // 256-byte nibble rows, so a row's byte offset / 8 is its scale row's); other rows re-read
       // scale row 0
-      const uint32_t sc = (uint32_t)idx_lds[tile * kHTile + 8 * wave + ((lane & 15) >> 1)];
+      const uint32_t sc = (uint32_t)nsc;
       const uint32_t soff = ((sc & 1u) ? ((sc & ~15u) >> 3) : 0u) + (uint32_t)(lane & 1) * 16u;
       h_dma16(fbits ? csc_u : zero_u, fbits ? soff : 0u,
               (DSA_LDS void*)(smem + kHStageOff + (slot * 4 + wave) * kHStage));
+    }
+    if (pend) {
+      nidx = idx_lds[__builtin_ctz(pend) * kHTile + 8 * wave + (lane & 7)];
+      if constexpr (FP4) nsc = idx_lds[__builtin_ctz(pend) * kHTile + 8 * wave + ((lane & 15) >> 1)];
     }
   };
   // fp4 rows of position k that this wave copied, decoded in place (it has waited for its own
