@@ -136,7 +136,10 @@ index_scores_prefill_kernel(const __bf16* __restrict__ q_idx, const __bf16* __re
         float sum = 0.f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) sum += fmaxf(acc[m][0][e] + acc[m][1][e], 0.f) * wv[m][e];
-        sum += shfl_xor(sum, 32);
+        // the two halves' sums, exchanged on the VALU (no LDS permute behind the operand reads):
+        // v_permlane32_swap of sum with itself leaves {lower half's, upper half's} in every lane
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(sum), false, false);
+        sum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         float* out_row = scores + ((int64_t)b * S + t0 + 2 * wave + m) * T;
         if (live[m] && hf == 0 && j < T) out_row[j] = j < ct[m] ? w_scale * sum : ninf;
       }
