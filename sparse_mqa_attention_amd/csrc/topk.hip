@@ -53,15 +53,26 @@ topk_kernel(const float* __restrict__ scores, int S, int T, int K, int start_pos
 constexpr int kWR = 4;    // histogram copies per wave
 constexpr int kWP = 257;  // ints between copies
 
+// Order-preserving key of a score for the one-wave kernel, in three VALU operations: a
+// non-negative float u maps to u + 2^31, a negative one to -u (two's complement), which sends -0.0
+// to the key of +0.0 with no compare.  Every float maps to a key >= 1, so 0 stays free to mark an
+// invisible position.
+__device__ __forceinline__ uint32_t wave_key(uint32_t u) {
+  const uint32_t s = (uint32_t)((int32_t)u >> 31);
+  return (u ^ (s | 0x80000000u)) - s;
+}
+
 template <int KPL>
 __global__ void __launch_bounds__(256)
 topk_wave_kernel(const float* __restrict__ scores, int rows, int S, int T, int K, int start_pos, int ratio,
                  int offset, int32_t* __restrict__ idx, int64_t ld_idx, int W, int Wc) {
+  static_assert(KPL % 16 == 0, "blocks of 16 groups");
   __shared__ int whist[4][kWR * kWP];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int row = blockIdx.x * 4 + wave;  // b*S + t
-  if (row >= rows) return;                // wave-uniform; no workgroup barrier below
+  // b*S + t, the last rows (most visible positions) first; wave-uniform, no workgroup barrier below
+  const int row = rows - 1 - (blockIdx.x * 4 + wave);
+  if (row < 0) return;
   int* hist = whist[wave];
   const int t = row % S;
   const int c = min(T, visible_rows(start_pos, t, ratio));
@@ -92,14 +103,29 @@ topk_wave_kernel(const float* __restrict__ scores, int rows, int S, int T, int K
       for (int g = g0; g < g0 + 16 && g < KPL; ++g) key[g] = 0u;
     }
   }
+  // keys, block by block of 16 groups: a block wholly visible needs no mask, the block holding
+  // the last visible position masks each group, blocks past it stay 0
   uint32_t kand = 0xFFFFFFFFu, kor = 0u;
 #pragma unroll
-  for (int g = 0; g < KPL; ++g) {
-    const bool vis = 64 * g + lane < c;
-    const uint32_t k = order_key(__uint_as_float(key[g]));
-    key[g] = vis ? k : 0u;
-    kand &= vis ? k : 0xFFFFFFFFu;
-    kor |= vis ? k : 0u;
+  for (int g0 = 0; g0 < KPL; g0 += 16) {
+    if (64 * (g0 + 16) <= c) {
+#pragma unroll
+      for (int g = g0; g < g0 + 16; ++g) {
+        const uint32_t k = wave_key(key[g]);
+        key[g] = k;
+        kand &= k;
+        kor |= k;
+      }
+    } else if (g0 < ng) {
+#pragma unroll
+      for (int g = g0; g < g0 + 16; ++g) {
+        const bool vis = 64 * g + lane < c;
+        const uint32_t k = wave_key(key[g]);
+        key[g] = vis ? k : 0u;
+        kand &= vis ? k : 0xFFFFFFFFu;
+        kor |= vis ? k : 0u;
+      }
+    }
   }
 #pragma unroll
   for (int m = 1; m < 64; m <<= 1) {
@@ -107,10 +133,13 @@ topk_wave_kernel(const float* __restrict__ scores, int rows, int S, int T, int K
     kor |= __shfl_xor(kor, m, 64);
   }
   const uint32_t diff = kand ^ kor;  // bits that differ among the visible keys
+  // prefix: the bits every visible key shares, then the digits chosen so far; the keys still in
+  // the running are the visible ones equal to it under mask (the shared bits and those digits)
   uint32_t prefix = kand & ~diff;
   uint32_t mask = ~diff;
   int remaining = K;
-  bool exact = false;  // exactly `remaining` visible keys match `prefix` under `mask`
+  bool exact = false;  // exactly `remaining` visible keys agree with `prefix` down to bit lo_end
+  int lo_end = 0;      // lowest bit of the last digit taken
   if (diff != 0u) {
     int hb = 31 - __builtin_clz(diff);
     // lane l owns digits 252-4l .. 255-4l in every copy: it clears them here and after each pass
@@ -132,7 +161,7 @@ topk_wave_kernel(const float* __restrict__ scores, int rows, int S, int T, int K
       for (int g0 = 0; g0 < KPL; g0 += 16) {
         if (g0 < ng) {
 #pragma unroll
-          for (int g = g0; g < g0 + 16 && g < KPL; ++g)
+          for (int g = g0; g < g0 + 16; ++g)
             if (key[g] != 0u && (key[g] & mask) == prefix) atomicAdd(&hcopy[(key[g] & dmask) >> lo], 1);
         }
       }
@@ -188,6 +217,7 @@ topk_wave_kernel(const float* __restrict__ scores, int rows, int S, int T, int K
       mask |= dmask;
       if (in_digit == remaining) {
         exact = true;  // every key of the chosen digit is taken
+        lo_end = lo;
         break;
       }
       if (lo == 0) break;
@@ -195,15 +225,24 @@ topk_wave_kernel(const float* __restrict__ scores, int rows, int S, int T, int K
     }
   }
   if (exact) {
-    // keep every visible key at or above the chosen digit, in position order
+    // keep every visible key at or above the chosen digit, in position order.  mask is every
+    // bit from lo_end up plus bits all visible keys share (where key and prefix agree), so
+    // (key & mask) >= prefix is key >= thr, thr being prefix cleared below lo_end; thr >= 1 also
+    // drops the invisible keys (0).  Exactly K keys pass: stop once they are out.
+    const uint32_t thr = max(prefix & (0xFFFFFFFFu << lo_end), 1u);
     int base = 0;
 #pragma unroll
-    for (int g = 0; g < KPL; ++g) {
-      const bool keep = key[g] != 0u && (key[g] & mask) >= prefix;
-      const uint64_t kb = __builtin_amdgcn_ballot_w64(keep);
-      const int pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(kb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)kb, 0));
-      if (keep) out[pos] = 64 * g + lane + offset;
-      base += __builtin_popcountll(kb);
+    for (int g0 = 0; g0 < KPL; g0 += 16) {
+      if (g0 < ng && base < K) {
+#pragma unroll
+        for (int g = g0; g < g0 + 16; ++g) {
+          const bool keep = key[g] >= thr;
+          const uint64_t kb = __builtin_amdgcn_ballot_w64(keep);
+          const int pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(kb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)kb, 0));
+          if (keep) *(int32_t*)((char*)out + (uint32_t)pos * 4u) = 64 * g + lane + offset;
+          base += __builtin_popcountll(kb);
+        }
+      }
     }
     return;
   }
@@ -211,15 +250,21 @@ topk_wave_kernel(const float* __restrict__ scores, int rows, int S, int T, int K
   // keep keys > tau and the first `remaining` keys == tau, in position order (invisible keys are 0)
   int base = 0, eq_seen = 0;
 #pragma unroll
-  for (int g = 0; g < KPL; ++g) {
-    const uint64_t eqb = __builtin_amdgcn_ballot_w64(key[g] == tau);
-    const int rank = eq_seen + __builtin_amdgcn_mbcnt_hi((uint32_t)(eqb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)eqb, 0));
-    eq_seen += __builtin_popcountll(eqb);
-    const bool keep = key[g] > tau || (key[g] == tau && rank < remaining);
-    const uint64_t kb = __builtin_amdgcn_ballot_w64(keep);
-    const int pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(kb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)kb, 0));
-    if (keep) out[pos] = 64 * g + lane + offset;
-    base += __builtin_popcountll(kb);
+  for (int g0 = 0; g0 < KPL; g0 += 16) {
+    if (g0 < ng) {
+#pragma unroll
+      for (int g = g0; g < g0 + 16; ++g) {
+        const uint64_t eqb = __builtin_amdgcn_ballot_w64(key[g] == tau);
+        const int rank =
+            eq_seen + __builtin_amdgcn_mbcnt_hi((uint32_t)(eqb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)eqb, 0));
+        eq_seen += __builtin_popcountll(eqb);
+        const bool keep = key[g] > tau || (key[g] == tau && rank < remaining);
+        const uint64_t kb = __builtin_amdgcn_ballot_w64(keep);
+        const int pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(kb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)kb, 0));
+        if (keep) *(int32_t*)((char*)out + (uint32_t)pos * 4u) = 64 * g + lane + offset;
+        base += __builtin_popcountll(kb);
+      }
+    }
   }
 }
 
