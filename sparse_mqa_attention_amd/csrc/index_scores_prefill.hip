@@ -30,6 +30,11 @@ constexpr int kXRowB = kXDI * 2;         // bytes of one key row
 constexpr int kXTileB = kXKT * kXRowB;   // 16 KiB
 constexpr int kXNST = 4;                 // ring stages
 
+// max(x, 0) in one instruction, as a signed integer max on the bits: a negative float (-0.0
+// included) is a negative integer and becomes +0.0, a non-negative one is unchanged.  fmaxf on a
+// value straight from an MFMA costs two (the compiler first quiets NaNs).
+__device__ __forceinline__ float relu1(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 __global__ void __launch_bounds__(256, 2)
 index_scores_prefill_kernel(const __bf16* __restrict__ q_idx, const __bf16* __restrict__ k_idx, int64_t k_bstride,
                             const __bf16* __restrict__ w, float w_scale, int S, int T, int H, int start_pos,
@@ -113,34 +118,43 @@ index_scores_prefill_kernel(const __bf16* __restrict__ q_idx, const __bf16* __re
     if (i + kXNST - 1 < ntl) issue(i + kXNST - 1);
 
     const unsigned char* tile = ring + (i % kXNST) * kXTileB;
+    // both 32-key blocks of the tile at once: four independent accumulator chains (query x key
+    // block) over the eight k-steps, so the matrix core never waits on a dependent accumulator
+    // and each chain ends holding its final logits (no partial sums to merge); a query that sees
+    // nothing of the block (at most its last ones) is still multiplied and only its stores differ
+    bf16x8 kop[2][kXKS];
 #pragma unroll
-    for (int kb = 0; kb < kXKT / 32; ++kb) {
-      bf16x8 kop[kXKS];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int s = 0; s < kXKS; ++s)
-        kop[s] = *reinterpret_cast<const bf16x8*>(tile + kb * 32 * kXRowB + kop_row + (((2 * s + hf) ^ kop_swz) << 4));
-      const int j = i * kXKT + 32 * kb + c;
-      // both queries in four independent chains (even and odd k-steps of each), so the matrix
-      // core never waits on a dependent accumulator; a query that sees nothing of the block (at
-      // most its last ones) is still multiplied and only its stores differ
-      f32x16 acc[2][2] = {};
+        kop[kb][s] = *reinterpret_cast<const bf16x8*>(tile + kb * 32 * kXRowB + kop_row + (((2 * s + hf) ^ kop_swz) << 4));
+    f32x16 acc[2][2];
 #pragma unroll
-      for (int s = 0; s < kXKS; s += 2) {
+    for (int s = 0; s < kXKS; ++s)
 #pragma unroll
-        for (int m = 0; m < 2; ++m) acc[m][0] = mfma32(qa[m][s], kop[s], acc[m][0]);
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int m = 0; m < 2; ++m) acc[m][1] = mfma32(qa[m][s + 1], kop[s + 1], acc[m][1]);
-      }
+        for (int kb = 0; kb < 2; ++kb) acc[m][kb] = mfma32(qa[m][s], kop[kb][s], s == 0 ? f32x16{} : acc[m][kb]);
+    // keep the chains interleaved, operand reads two k-steps ahead of their MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // LDS reads of k-steps 0, 1
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
+    for (int s = 0; s < kXKS; ++s) {
+      if (s + 2 < kXKS) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // reads of k-step s + 2
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);                    // MFMAs of k-step s
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      float* out_row = scores + ((int64_t)b * S + t0 + 2 * wave + m) * T;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
         float sum = 0.f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) sum += fmaxf(acc[m][0][e] + acc[m][1][e], 0.f) * wv[m][e];
+        for (int e = 0; e < 16; ++e) sum += relu1(acc[m][kb][e]) * wv[m][e];
         // the two halves' sums, exchanged on the VALU (no LDS permute behind the operand reads):
         // v_permlane32_swap of sum with itself leaves {lower half's, upper half's} in every lane
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(sum), false, false);
         sum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-        float* out_row = scores + ((int64_t)b * S + t0 + 2 * wave + m) * T;
+        const int j = i * kXKT + 32 * kb + c;
         if (live[m] && hf == 0 && j < T) out_row[j] = j < ct[m] ? w_scale * sum : ninf;
       }
     }
