@@ -127,6 +127,10 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ srow, int T
   constexpr int J = KPT < 4 ? KPT : 4;  // chunks per thread (one 16-bit field each in the scans)
   constexpr int E = KPT / J;            // consecutive positions per chunk
   static_assert(J * E == KPT && E <= 16, "KPT is 1, 2, 4 or a multiple of 4 up to 64");
+  // one thread per histogram bin totals each pass: with fewer than 256 threads the upper bins
+  // would keep stale counts, the select could keep more than K keys and put() would be handed
+  // slots past K
+  static_assert(NT >= 256 && NT % 64 == 0, "block_topk needs at least 256 threads");
   static_assert(E * NT < 65536, "a chunk's block total fits a 16-bit field");
   using Bits = typename std::conditional<(KPT > 32), uint64_t, uint32_t>::type;
   const int tid = threadIdx.x;
