@@ -180,7 +180,7 @@ def main():
         bufs.append({"idx": torch.empty(w.B, w.S, Wc + w.K, dtype=torch.int32, device=dev),
                      "scores": torch.empty(w.B, w.S, w.T, dtype=torch.float32, device=dev),
                      "o": torch.empty_like(s["q"]),
-                     "workspace": torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)})
+                     "workspace": torch.zeros(max(ws, 1), dtype=torch.uint8, device=dev)})
     stream = torch.cuda.current_stream(dev)
     comp_key = "kv_comp_fp4" if w.comp_fmt == "fp4" else "kv_comp"
 

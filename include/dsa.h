@@ -21,7 +21,9 @@
  *  - Device pointers are caller-owned memory on the current HIP device; the
  *    library never frees or retains them past the call.  Every call only
  *    enqueues kernels on `stream` (NULL = the legacy default stream) and
- *    returns without synchronising.
+ *    returns without synchronising, with three exceptions, each stated where
+ *    it applies: dsa_init (and the first decode call on a device dsa_init has
+ *    not prepared, which runs it), dsa_device_errors, and DSA_DEBUG mode.
  *  - Tensors are dense, row-major, in the stated layout.  Where a batch stride
  *    is taken, it is in elements (rows * row length for a dense batch), so a
  *    cache slice [:B, :n] of a larger [max_B, max_n, D] buffer can be passed
@@ -32,7 +34,17 @@
  *    next call on the same thread).  No C++ exception crosses the ABI.
  *  - Index values inside idx rows are not range-checked on the device (as on
  *    the pages, an out-of-range index is a caller error); -1 marks an empty
- *    slot.
+ *    slot.  With DSA_DEBUG=1 in the environment (or dsa_set_debug(1)),
+ *    dsa_sparse_attn copies the caller's idx to the host and rejects any entry
+ *    outside [-1, rows) with DSA_ERR_INDEX before launching (one
+ *    synchronisation per call; not allowed under stream capture).
+ *  - Workspace: a call that takes one uses it as scratch.  Its first
+ *    DSA_WORKSPACE_HEADER_BYTES hold per-query rendezvous counters of the
+ *    decode kernels, which must be zero before the workspace's first use (for
+ *    example allocated zero-filled); every call leaves them zero again when
+ *    its kernels end.  Calls in stream order may share a workspace; calls that
+ *    can run at the same time (other streams, graphs replayed concurrently)
+ *    need workspaces of their own.
  */
 #ifndef DSA_H_
 #define DSA_H_
@@ -44,7 +56,8 @@
 extern "C" {
 #endif
 
-#define DSA_ABI_VERSION 1
+#define DSA_ABI_VERSION 2
+#define DSA_WORKSPACE_HEADER_BYTES 4096
 
 typedef struct ihipStream_t* dsa_stream_t; /* a hipStream_t */
 
@@ -55,7 +68,9 @@ enum dsa_status {
   DSA_ERR_DTYPE = -3,       /* unknown dtype or format code */
   DSA_ERR_UNSUPPORTED = -4, /* valid arguments with no instantiated kernel (e.g. head_dim 96) */
   DSA_ERR_HIP = -5,         /* the HIP runtime reported an error at launch */
-  DSA_ERR_WORKSPACE = -6    /* workspace NULL or smaller than the size the query returns */
+  DSA_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than the size the query returns */
+  DSA_ERR_STATE = -7,       /* a synchronising step was needed under stream capture (see dsa_init) */
+  DSA_ERR_INDEX = -8        /* DSA_DEBUG: an idx entry outside [-1, rows) */
 };
 
 enum dsa_dtype {
@@ -74,6 +89,42 @@ enum dsa_kv_format {
 /* Library identity. */
 int dsa_abi_version(void);
 const char* dsa_last_error(void);
+
+/*
+ * What the last call on this thread launched: the number of kernels it enqueued and their names
+ * joined by '+' (for example "index_scores_bf16+topk<256,8>+sparse_attn_decode<NS=8>").  The
+ * record is reset at the start of every call and is valid until the next call on the thread.
+ */
+int dsa_last_launch_count(void);
+const char* dsa_last_launches(void);
+
+/*
+ * Per-device set-up (call once per device before the first decode call, and before capturing any
+ * call into a graph): checks on which XCD each workgroup runs (the decode kernels keep all
+ * workgroups of a query on one XCD and meet in its L2, which needs workgroup i on XCD i mod 8),
+ * records how many workgroups of each decode kernel fit on the device at once, and reads
+ * DSA_DEBUG.  Launches one small kernel on a private stream and synchronises with it.
+ * Idempotent and thread-safe.  A call that needs a device dsa_init has not prepared runs it
+ * itself (one synchronisation), or returns DSA_ERR_STATE under stream capture.  Where the XCD check
+ * fails, the decode kernels are not used and the calls take their multi-launch paths.
+ */
+int dsa_init(int device);
+
+/*
+ * Reads and clears the device's sticky error bits (bit 0: a decode rendezvous timed out; that
+ * query's output was set to NaN).  Synchronises the device first.
+ */
+int dsa_device_errors(int device, uint32_t* flags);
+
+/* Turns the DSA_DEBUG index checks on (1) or off (0); returns the previous setting. */
+int dsa_set_debug(int on);
+
+/*
+ * Host-side range check of index rows (what DSA_DEBUG runs on a copy of idx): DSA_OK when every
+ * one of the `count` entries of the host array idx is -1 or in [0, n_rows); DSA_ERR_INDEX
+ * otherwise, with the position of the first bad entry in *first_bad (may be NULL).
+ */
+int dsa_check_idx(const int32_t* idx, int64_t count, int64_t n_rows, int64_t* first_bad);
 
 /*
  * Index scores (`Indexer.forward`: einsum of the index query heads with the
@@ -116,6 +167,14 @@ int dsa_index_scores(const void* q_idx, const void* k_idx, int64_t k_batch_strid
  */
 int dsa_topk(const float* scores, int B, int S, int T, int index_topk, int start_pos, int ratio,
              int offset, int32_t* idx, int64_t ld_idx, dsa_stream_t stream);
+
+/*
+ * How dsa_topk and dsa_select share the B*S rows between their two kernels: the first *wave_rows
+ * rows go to the one-wave-per-row kernel (many rows, T <= 8192; its reads of a whole number of
+ * 64-key groups must stay inside the scores buffer), the other *block_rows rows to the
+ * one-workgroup-per-row kernel.  Host arithmetic only, nothing is launched.
+ */
+int dsa_topk_plan(int B, int S, int T, int64_t* wave_rows, int64_t* block_rows);
 
 /*
  * Window index rows (`get_window_topk_idxs`):
@@ -187,7 +246,7 @@ typedef struct dsa_kv_src {
  *   o    [B, S, H, D] dtype, contiguous, written in full
  *   comp may be NULL (or have n_rows 0) when no index reaches past the window.
  *   workspace: device memory of at least dsa_sparse_attn_workspace_size(...) bytes
- *     (may be NULL when that size is 0); its contents are scratch between calls.
+ *     (may be NULL when that size is 0); zero-filled header, see the conventions above.
  *
  * Supported: dtype BF16 with D in {64, 128, 256, 512} and H in 1..128, or dtype
  * F32 with D <= 512 and H <= 64.  Accumulation is float32; the probabilities
@@ -197,7 +256,8 @@ int dsa_sparse_attn(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp
                     const int32_t* idx, int L, float scale, void* o, int dtype, int B, int S, int H,
                     int D, void* workspace, size_t workspace_bytes, dsa_stream_t stream);
 
-/* Bytes of workspace dsa_sparse_attn needs for this shape (0 when none). */
+/* Bytes of workspace dsa_sparse_attn needs for this shape (0 when none; otherwise at least
+   DSA_WORKSPACE_HEADER_BYTES). */
 size_t dsa_sparse_attn_workspace_size(int dtype, int B, int S, int H, int D, int L);
 
 /*
@@ -209,8 +269,10 @@ size_t dsa_sparse_attn_workspace_size(int dtype, int B, int S, int H, int D, int
  *
  * with L = dsa_window_cols(S, start_pos, W) + min(index_topk, T).  For decode batches that the
  * two-phase decode attention kernel takes (bf16, D = 512, H = 64, dense rows, fewer than 256
- * queries, T <= 2048) it is one launch: every workgroup of a query selects that query's index row
- * from its scores in the kernel's prologue.  Otherwise it makes the two calls above.
+ * queries, all of its workgroups resident at once, T <= 2048, the device's XCD check passed in
+ * dsa_init) it is one launch: every workgroup of a query selects that query's index row from its
+ * scores in the kernel's prologue.  Otherwise it makes the two calls above.  dsa_last_launches()
+ * tells which happened.
  *
  *   scores [B, S, T] float32; q, win, comp, sink, o, workspace as for dsa_sparse_attn, with the
  *   workspace sized by dsa_sparse_attn_workspace_size(dtype, B, S, H, D, L).
@@ -237,8 +299,9 @@ int dsa_sparse_attn_select(const float* scores, int T, int index_topk, int start
  * attention kernel, and with D_I = 128, H_I <= 64, 16-byte aligned q_idx and k_idx and
  * k_batch_stride a multiple of 8, it is one launch: the workgroups of a query each score a share
  * of the compressed rows into `scores`, meet, select the query's index row from all of its scores
- * and attend.  That needs the workgroups of a query to share one L2 (checked once per device);
- * where they do not, or the shape does not fit, it makes the two calls above.
+ * and attend.  That needs the workgroups of a query to share one L2 (checked once per device by
+ * dsa_init); where they do not, or the shape does not fit, it makes the two calls above.
+ * dsa_last_launches() tells which happened.
  *
  *   q_idx, k_idx, w, w_scale, H_I, D_I, T, start_pos, ratio: as for dsa_index_scores
  *   scores [B, S, T] float32, required: always written in full (dsa_index_scores' contract)

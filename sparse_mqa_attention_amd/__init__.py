@@ -13,6 +13,11 @@ Calls (same names as the C entry points):
     dsa_sparse_attn_select  the index rows and the attention (one launch for decode batches)
     dsa_sparse_attn_step    the whole step: index scores, index rows, attention (one launch
                             for decode batches)
+    dsa_init, dsa_device_errors, dsa_last_launches, dsa_set_debug, dsa_check_idx, dsa_topk_plan
+                            set-up, error flags and introspection
+
+The library is set up for a device (dsa_init) the first time a call here uses it.  Workspaces
+are allocated zero-filled, as the C ABI asks.
 """
 from __future__ import annotations
 
@@ -26,7 +31,8 @@ LIB_PATH = os.path.join(_HERE, "libdsa.so")
 
 DSA_F32, DSA_BF16 = 0, 1
 DSA_KV_DENSE, DSA_KV_FP4_E4M3_G16 = 0, 1
-_ERRORS = {-1: "NULL", -2: "SHAPE", -3: "DTYPE", -4: "UNSUPPORTED", -5: "HIP", -6: "WORKSPACE"}
+_ERRORS = {-1: "NULL", -2: "SHAPE", -3: "DTYPE", -4: "UNSUPPORTED", -5: "HIP", -6: "WORKSPACE", -7: "STATE",
+           -8: "INDEX"}
 
 
 class DsaError(RuntimeError):
@@ -55,6 +61,18 @@ def _load():
     i32, i64, vp, f32 = ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
     lib.dsa_abi_version.restype = i32
     lib.dsa_last_error.restype = ctypes.c_char_p
+    lib.dsa_last_launch_count.restype = i32
+    lib.dsa_last_launches.restype = ctypes.c_char_p
+    lib.dsa_init.argtypes = [i32]
+    lib.dsa_init.restype = i32
+    lib.dsa_device_errors.argtypes = [i32, ctypes.POINTER(ctypes.c_uint32)]
+    lib.dsa_device_errors.restype = i32
+    lib.dsa_set_debug.argtypes = [i32]
+    lib.dsa_set_debug.restype = i32
+    lib.dsa_check_idx.argtypes = [vp, i64, i64, ctypes.POINTER(ctypes.c_int64)]
+    lib.dsa_check_idx.restype = i32
+    lib.dsa_topk_plan.argtypes = [i32, i32, i32, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64)]
+    lib.dsa_topk_plan.restype = i32
     lib.dsa_index_scores.argtypes = [vp, vp, i64, vp, f32, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.dsa_index_scores.restype = i32
     lib.dsa_topk.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, i64, vp]
@@ -98,6 +116,19 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise DsaError(-3, f"dtype {t.dtype} is not float32/bfloat16")
 
 
+_READY = set()  # device indices dsa_init has prepared
+
+
+def dsa_init(device=None) -> None:
+    """Per-device set-up of the library (dsa_init in include/dsa.h); idempotent."""
+    d = torch.device("cuda", torch.cuda.current_device()) if device is None else torch.device(device)
+    i = d.index if d.index is not None else torch.cuda.current_device()
+    if i in _READY:
+        return
+    _check(lib.dsa_init(i))
+    _READY.add(i)
+
+
 def _dev(*ts) -> torch.device:
     dev = ts[0].device
     for t in ts:
@@ -105,7 +136,60 @@ def _dev(*ts) -> torch.device:
             continue
         if t.device != dev or dev.type != "cuda":
             raise DsaError(-2, "all tensors must be on the same GPU")
+    if dev.index not in _READY:
+        dsa_init(dev)
     return dev
+
+
+def dsa_last_launches():
+    """(count, names) of the kernels the last call on this thread launched."""
+    return int(lib.dsa_last_launch_count()), lib.dsa_last_launches().decode()
+
+
+def dsa_device_errors(device=None) -> int:
+    """Read and clear the device's sticky error bits (synchronises the device)."""
+    i = torch.cuda.current_device() if device is None else torch.device(device).index
+    v = ctypes.c_uint32(0)
+    _check(lib.dsa_device_errors(i, ctypes.byref(v)))
+    return int(v.value)
+
+
+def dsa_set_debug(on: bool) -> bool:
+    return bool(lib.dsa_set_debug(1 if on else 0))
+
+
+def dsa_check_idx(idx_host, n_rows: int):
+    """Host-side range check of an int32 numpy array: (ok, first bad position or -1)."""
+    import numpy as np
+
+    a = np.ascontiguousarray(idx_host, dtype=np.int32)
+    bad = ctypes.c_int64(-1)
+    rc = lib.dsa_check_idx(a.ctypes.data_as(ctypes.c_void_p), a.size, int(n_rows), ctypes.byref(bad))
+    if rc not in (0, -8):
+        _check(rc)
+    return rc == 0, int(bad.value)
+
+
+def dsa_topk_plan(B: int, S: int, T: int):
+    """(rows on the one-wave kernel, rows on the per-row workgroup kernel) of a top-k call."""
+    w, b = ctypes.c_int64(0), ctypes.c_int64(0)
+    _check(lib.dsa_topk_plan(int(B), int(S), int(T), ctypes.byref(w), ctypes.byref(b)))
+    return int(w.value), int(b.value)
+
+
+def _expect(name, t, shape, dtype):
+    if t is None:
+        raise DsaError(-1, f"{name} is missing")
+    if tuple(t.shape) != tuple(shape):
+        raise DsaError(-2, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise DsaError(-3, f"{name} has dtype {t.dtype}, expected {dtype}")
+
+
+def _workspace(need, workspace, dev):
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.zeros(need, dtype=torch.uint8, device=dev)  # the header must start at zero
+    return workspace
 
 
 def _stream(dev, stream):
@@ -135,16 +219,21 @@ def dsa_index_scores(q_idx, k_idx, w, w_scale: float, start_pos: int, ratio: int
 
     q_idx [B,S,H_I,D_I], k_idx [B,T,D_I] (any batch stride), w [B,S,H_I] (same dtype).
     """
-    dev = _dev(q_idx, k_idx, w)
     _need_contig("q_idx", q_idx)
     _need_contig("w", w)
     B, S, H, Dd = q_idx.shape
     T = k_idx.shape[1]
     kbs, krs = _batched_rows("k_idx", k_idx)
-    if krs != Dd:
-        raise DsaError(-2, "k_idx rows must be dense")
+    if krs != Dd or k_idx.shape[0] != B or k_idx.shape[2] != Dd:
+        raise DsaError(-2, "k_idx must be [B, T, D_I] with dense rows")
+    _expect("k_idx", k_idx, (B, T, Dd), q_idx.dtype)
+    _expect("w", w, (B, S, H), q_idx.dtype)
+    if out is not None:
+        _expect("scores", out, (B, S, T), torch.float32)
+    dev = _dev(q_idx, k_idx, w, out)
     if out is None:
         out = torch.empty(B, S, T, dtype=torch.float32, device=dev)
+    _expect("scores", out, (B, S, T), torch.float32)
     _need_contig("scores", out)
     _check(lib.dsa_index_scores(_ptr(q_idx), _ptr(k_idx), kbs, _ptr(w), float(w_scale), _dtype_code(q_idx), B, S, T,
                                 H, Dd, int(start_pos), int(ratio), _ptr(out), _stream(dev, stream)))
@@ -157,11 +246,13 @@ def dsa_topk(scores, index_topk: int, start_pos: int, ratio: int, offset: int, o
     dev = _dev(scores)
     _need_contig("scores", scores)
     B, S, T = scores.shape
+    if scores.dtype != torch.float32:
+        raise DsaError(-3, "scores must be float32")
     K = min(int(index_topk), T)
     if out is None:
         out = torch.empty(B, S, col + K, dtype=torch.int32, device=dev)
     _need_contig("idx", out)
-    if out.dtype != torch.int32 or out.shape[-1] < col + K:
+    if out.dtype != torch.int32 or tuple(out.shape[:2]) != (B, S) or out.shape[-1] < col + K:
         raise DsaError(-2, "idx must be int32 with room for the top-k columns")
     base = ctypes.c_void_p(out.data_ptr() + 4 * col)
     _check(lib.dsa_topk(_ptr(scores), B, S, T, int(index_topk), int(start_pos), int(ratio), int(offset), base,
@@ -180,6 +271,8 @@ def dsa_window_idx(out, start_pos: int, W: int, stream=None):
     """Window index rows into the first window columns of `out` [B, S, >=Wc] int32."""
     dev = _dev(out)
     _need_contig("idx", out)
+    if out.dtype != torch.int32 or out.dim() != 3:
+        raise DsaError(-3, "idx must be int32 [B, S, L]")
     B, S, ld = out.shape
     _check(lib.dsa_window_idx(B, S, int(start_pos), int(W), _ptr(out), ld, _stream(dev, stream)))
     return out
@@ -190,12 +283,14 @@ def dsa_select(scores, index_topk: int, start_pos: int, ratio: int, W: int, offs
     B, S, T = scores.shape
     dev = _dev(scores)
     _need_contig("scores", scores)
+    if scores.dtype != torch.float32:
+        raise DsaError(-3, "scores must be float32")
     Wc = dsa_window_cols(S, start_pos, W)
     K = min(int(index_topk), T)
     if out is None:
         out = torch.empty(B, S, Wc + K, dtype=torch.int32, device=dev)
     _need_contig("idx", out)
-    if out.dtype != torch.int32 or out.shape[-1] < Wc + K:
+    if out.dtype != torch.int32 or tuple(out.shape[:2]) != (B, S) or out.shape[-1] < Wc + K:
         raise DsaError(-2, "idx must be int32 with room for the window and top-k columns")
     _check(lib.dsa_select(_ptr(scores), B, S, T, int(index_topk), int(start_pos), int(ratio), int(W), int(offset),
                           _ptr(out), out.shape[-1], _stream(dev, stream)))
@@ -225,6 +320,35 @@ def dsa_sparse_attn_workspace_size(dtype_code: int, B: int, S: int, H: int, D: i
     return int(lib.dsa_sparse_attn_workspace_size(dtype_code, B, S, H, D, L))
 
 
+def _attn_operands(q, kv_win, kv_comp, sink, comp_scales, out):
+    """Shapes, dtype code, KV source descriptors and output of an attention call, checked."""
+    if q.dim() != 4:
+        raise DsaError(-2, "q must be [B, S, H, D]")
+    _need_contig("q", q)
+    B, S, H, D = q.shape
+    dt = _dtype_code(q)
+    if kv_win is None or kv_win.dim() != 3 or kv_win.shape[0] != B or kv_win.shape[2] != D:
+        raise DsaError(-2, "kv_win must be [B, n_win, D]")
+    if kv_win.dtype != q.dtype:
+        raise DsaError(-3, "kv_win must have q's dtype")
+    _expect("sink", sink, (H,), torch.float32)
+    fp4 = kv_comp is not None and kv_comp.dtype == torch.uint8
+    if kv_comp is not None:
+        if kv_comp.dim() != 3 or kv_comp.shape[0] != B or kv_comp.shape[2] != (D // 2 if fp4 else D):
+            raise DsaError(-2, "kv_comp must be [B, T, D] (or [B, T, D/2] uint8 fp4 nibbles)")
+        if not fp4 and kv_comp.dtype != q.dtype:
+            raise DsaError(-3, "kv_comp must have q's dtype (or be uint8 fp4 nibbles)")
+        if fp4:
+            _expect("comp_scales", comp_scales, (B, kv_comp.shape[1], D // 16), torch.uint8)
+    win = kv_src(kv_win)
+    comp = kv_src(kv_comp, comp_scales, DSA_KV_FP4_E4M3_G16 if fp4 else DSA_KV_DENSE)
+    if out is None:
+        out = torch.empty_like(q)
+    _expect("o", out, q.shape, q.dtype)
+    _need_contig("o", out)
+    return B, S, H, D, dt, win, comp, out
+
+
 def dsa_sparse_attn(q, kv_win, kv_comp, sink, idx, scale: float, comp_scales=None, out=None, workspace=None,
                     stream=None):
     """Sparse attention with a per-head sink; o [B,S,H,D] in q's dtype.
@@ -232,21 +356,14 @@ def dsa_sparse_attn(q, kv_win, kv_comp, sink, idx, scale: float, comp_scales=Non
     kv_win [B, n_win, D]; kv_comp [B, T, D] in q's dtype, or [B, T, D/2] uint8 fp4 nibbles with
     comp_scales [B, T, D/16] uint8 E4M3; idx [B, S, L] int32 over [window rows | compressed rows].
     """
-    dev = _dev(q, kv_win, kv_comp, sink, idx)
-    _need_contig("q", q)
+    B, S, H, D, dt, win, comp, out = _attn_operands(q, kv_win, kv_comp, sink, comp_scales, out)
     _need_contig("idx", idx)
-    B, S, H, D = q.shape
+    if idx.dim() != 3 or tuple(idx.shape[:2]) != (B, S) or idx.dtype != torch.int32:
+        raise DsaError(-2, "idx must be int32 [B, S, L]")
     L = idx.shape[-1]
-    dt = _dtype_code(q)
-    win = kv_src(kv_win)
-    fp4 = kv_comp is not None and kv_comp.dtype == torch.uint8
-    comp = kv_src(kv_comp, comp_scales, DSA_KV_FP4_E4M3_G16 if fp4 else DSA_KV_DENSE)
-    if out is None:
-        out = torch.empty_like(q)
-    _need_contig("o", out)
+    dev = _dev(q, kv_win, kv_comp, sink, idx, out)
     need = dsa_sparse_attn_workspace_size(dt, B, S, H, D, L)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    workspace = _workspace(need, workspace, dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.dsa_sparse_attn(_ptr(q), ctypes.byref(win), ctypes.byref(comp), _ptr(sink), _ptr(idx), L,
                                float(scale), _ptr(out), dt, B, S, H, D, _ptr(workspace), wbytes,
@@ -259,28 +376,20 @@ def dsa_sparse_attn_select(scores, q, kv_win, kv_comp, sink, *, index_topk: int,
     """Index rows (window + top-k, as dsa_select with offset kv_win.shape[1]) and the sparse attention
     over them; one launch for decode batches the two-phase decode kernel takes.  Returns (o, idx);
     idx [B, S, L] int32 receives the rows (allocated when not given)."""
-    dev = _dev(q, kv_win, kv_comp, sink, scores)
-    _need_contig("q", q)
+    B, S, H, D, dt, win, comp, out = _attn_operands(q, kv_win, kv_comp, sink, comp_scales, out)
     _need_contig("scores", scores)
-    B, S, H, D = q.shape
     T = scores.shape[-1]
+    _expect("scores", scores, (B, S, T), torch.float32)
+    dev = _dev(q, kv_win, kv_comp, sink, scores, out)
     Wc = dsa_window_cols(S, start_pos, W)
     L = Wc + min(int(index_topk), T)
-    dt = _dtype_code(q)
-    win = kv_src(kv_win)
-    fp4 = kv_comp is not None and kv_comp.dtype == torch.uint8
-    comp = kv_src(kv_comp, comp_scales, DSA_KV_FP4_E4M3_G16 if fp4 else DSA_KV_DENSE)
-    if out is None:
-        out = torch.empty_like(q)
-    _need_contig("o", out)
     if idx is None:
         idx = torch.empty(B, S, L, dtype=torch.int32, device=dev)
     _need_contig("idx", idx)
-    if idx.dtype != torch.int32 or idx.shape[-1] != L:
+    if idx.dtype != torch.int32 or tuple(idx.shape) != (B, S, L):
         raise DsaError(-2, "idx must be int32 [B, S, L] with L = window columns + top-k columns")
     need = dsa_sparse_attn_workspace_size(dt, B, S, H, D, L)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    workspace = _workspace(need, workspace, dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.dsa_sparse_attn_select(_ptr(scores), T, int(index_topk), int(start_pos), int(ratio), int(W), _ptr(q),
                                       ctypes.byref(win), ctypes.byref(comp), _ptr(sink), float(scale), _ptr(out), dt,
@@ -295,36 +404,32 @@ def dsa_sparse_attn_step(q_idx, k_idx, w, q, kv_win, kv_comp, sink, *, index_top
     them (as dsa_sparse_attn_select); one launch for decode batches the decode kernel takes.
     Returns (o, idx, scores); scores [B, S, T] float32 and idx [B, S, L] int32 are allocated when not
     given."""
-    dev = _dev(q_idx, k_idx, w, q, kv_win, kv_comp, sink)
     _need_contig("q_idx", q_idx)
     _need_contig("w", w)
-    _need_contig("q", q)
-    B, S, H, D = q.shape
+    B, S, H, D, dt, win, comp, out = _attn_operands(q, kv_win, kv_comp, sink, comp_scales, out)
+    if q_idx.dim() != 4 or tuple(q_idx.shape[:2]) != (B, S):
+        raise DsaError(-2, "q_idx must be [B, S, H_I, D_I]")
     H_I, D_I = q_idx.shape[2], q_idx.shape[3]
     T = k_idx.shape[1]
     kbs, krs = _batched_rows("k_idx", k_idx)
     if krs != D_I:
         raise DsaError(-2, "k_idx rows must be dense")
+    _expect("k_idx", k_idx, (B, T, D_I), q_idx.dtype)
+    _expect("w", w, (B, S, H_I), q_idx.dtype)
+    dev = _dev(q_idx, k_idx, w, q, kv_win, kv_comp, sink, out)
     Wc = dsa_window_cols(S, start_pos, W)
     L = Wc + min(int(index_topk), T)
-    dt = _dtype_code(q)
-    win = kv_src(kv_win)
-    fp4 = kv_comp is not None and kv_comp.dtype == torch.uint8
-    comp = kv_src(kv_comp, comp_scales, DSA_KV_FP4_E4M3_G16 if fp4 else DSA_KV_DENSE)
-    if out is None:
-        out = torch.empty_like(q)
-    _need_contig("o", out)
     if scores is None:
         scores = torch.empty(B, S, T, dtype=torch.float32, device=dev)
+    _expect("scores", scores, (B, S, T), torch.float32)
     _need_contig("scores", scores)
     if idx is None:
         idx = torch.empty(B, S, L, dtype=torch.int32, device=dev)
     _need_contig("idx", idx)
-    if idx.dtype != torch.int32 or idx.shape[-1] != L:
+    if idx.dtype != torch.int32 or tuple(idx.shape) != (B, S, L):
         raise DsaError(-2, "idx must be int32 [B, S, L] with L = window columns + top-k columns")
     need = dsa_sparse_attn_workspace_size(dt, B, S, H, D, L)
-    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    workspace = _workspace(need, workspace, dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.dsa_sparse_attn_step(_ptr(q_idx), _ptr(k_idx), kbs, _ptr(w), float(w_scale), H_I, D_I, T,
                                     int(index_topk), int(start_pos), int(ratio), int(W), _ptr(q), ctypes.byref(win),
@@ -361,6 +466,12 @@ def sparse_attention_step(q, kv_win, kv_comp, qI, kI, w, sink, *, start_pos: int
 
 __all__ = [
     "DsaError",
+    "dsa_init",
+    "dsa_device_errors",
+    "dsa_last_launches",
+    "dsa_set_debug",
+    "dsa_check_idx",
+    "dsa_topk_plan",
     "DsaKvSrc",
     "dsa_index_scores",
     "dsa_topk",

@@ -4,6 +4,10 @@
 
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "../../include/dsa.h"
 #include "dsa_internal.h"
@@ -11,6 +15,23 @@
 namespace dsa {
 
 static thread_local char g_err[512] = "";
+// kernels the last top-level call on this thread launched: count and '+'-joined names
+static thread_local int g_nlaunch = 0;
+static thread_local char g_launches[512] = "";
+static thread_local int g_depth = 0;
+
+// Marks a top-level entry point: clears the error text and the launch record once per call (the
+// composite calls go through the simpler ones).
+struct Entry {
+  Entry() {
+    if (g_depth++ == 0) {
+      g_err[0] = 0;
+      g_nlaunch = 0;
+      g_launches[0] = 0;
+    }
+  }
+  ~Entry() { --g_depth; }
+};
 
 int fail(int code, const char* fmt, ...) {
   va_list ap;
@@ -23,12 +44,85 @@ int fail(int code, const char* fmt, ...) {
 int check_launch(const char* what) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(DSA_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  ++g_nlaunch;
+  const size_t n = strlen(g_launches);
+  snprintf(g_launches + n, sizeof(g_launches) - n, "%s%s", n ? "+" : "", what);
+  return DSA_OK;
+}
+
+// ---- per-device set-up -------------------------------------------------------------------------
+constexpr int kMaxDevices = 64;
+static DeviceState g_dev[kMaxDevices];
+static std::mutex g_dev_mu;
+static int g_debug = -1;  // -1: not read from DSA_DEBUG yet
+
+int scratch_device_init(int dev, DeviceState& ds) {
+  (void)dev;
+  ds.scratch = nullptr;
+  return DSA_OK;
+}
+
+static bool debug_on() {
+  if (g_debug < 0) {
+    const char* e = getenv("DSA_DEBUG");
+    g_debug = (e && e[0] && strcmp(e, "0") != 0) ? 1 : 0;
+  }
+  return g_debug > 0;
+}
+
+static int init_device(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return fail(DSA_ERR_SHAPE, "dsa_init: device %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_dev_mu);
+  DeviceState& ds = g_dev[dev];
+  if (ds.ready) return DSA_OK;
+  int prev = 0;
+  if (hipGetDevice(&prev) != hipSuccess) return fail(DSA_ERR_HIP, "dsa_init: no current device");
+  if (prev != dev && hipSetDevice(dev) != hipSuccess) return fail(DSA_ERR_HIP, "dsa_init: cannot select device %d", dev);
+  int rc = decode_device_init(dev, ds);
+  if (rc == DSA_OK) rc = scratch_device_init(dev, ds);
+  if (prev != dev) hipSetDevice(prev);
+  if (rc == DSA_OK) ds.ready = 1;
+  debug_on();
+  return rc;
+}
+
+int ensure_device_init(hipStream_t st, DeviceState** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(DSA_ERR_HIP, "no usable current HIP device");
+  DeviceState& ds = g_dev[dev];
+  if (!ds.ready) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+      return fail(DSA_ERR_STATE, "device %d is not set up: call dsa_init(%d) before capturing a graph", dev, dev);
+    const int rc = init_device(dev);
+    if (rc) return rc;
+  }
+  *out = &ds;
+  return DSA_OK;
+}
+
+// DSA_DEBUG: the caller's index rows are copied to the host and range-checked before the attention
+// is launched (one synchronisation per call).
+static int debug_check_idx(const int32_t* idx, int64_t count, int64_t n_rows, hipStream_t st) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+    return fail(DSA_ERR_STATE, "DSA_DEBUG index checks cannot run under stream capture");
+  std::vector<int32_t> h((size_t)count);
+  if (hipMemcpyAsync(h.data(), idx, (size_t)count * 4, hipMemcpyDeviceToHost, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    return fail(DSA_ERR_HIP, "DSA_DEBUG: copying idx to the host failed");
+  int64_t bad = -1;
+  if (dsa_check_idx(h.data(), count, n_rows, &bad) != DSA_OK)
+    return fail(DSA_ERR_INDEX, "dsa_sparse_attn: idx entry %lld is %d, outside [-1, %lld)", (long long)bad,
+                h[(size_t)bad], (long long)n_rows);
   return DSA_OK;
 }
 
 int index_scores_launch(const void*, const void*, int64_t, const void*, float, int, int, int, int, int, int, int, int,
                         float*, hipStream_t);
 int topk_launch(const float*, int, int, int, int, int, int, int, int32_t*, int64_t, int, int, hipStream_t);
+void topk_plan(int, int, int, int64_t*, int64_t*);
 int window_idx_launch(int, int, int, int, int, int32_t*, int64_t, hipStream_t);
 int sparse_attn_bf16_launch(const void*, const dsa_kv_src*, const dsa_kv_src*, const float*, const int32_t*, int,
                             float, void*, int, int, int, int, void*, hipStream_t);
@@ -48,10 +142,60 @@ int dsa_abi_version(void) { return DSA_ABI_VERSION; }
 
 const char* dsa_last_error(void) { return dsa::g_err; }
 
+int dsa_last_launch_count(void) { return dsa::g_nlaunch; }
+
+const char* dsa_last_launches(void) { return dsa::g_launches; }
+
+int dsa_init(int device) {
+  dsa::Entry e;
+  return dsa::init_device(device);
+}
+
+int dsa_device_errors(int device, uint32_t* flags) {
+  dsa::Entry e;
+  if (!flags) return fail(DSA_ERR_NULL, "dsa_device_errors: NULL flags");
+  *flags = 0;
+  if (device < 0 || device >= dsa::kMaxDevices) return fail(DSA_ERR_SHAPE, "dsa_device_errors: device %d", device);
+  int prev = 0;
+  if (hipGetDevice(&prev) != hipSuccess) return fail(DSA_ERR_HIP, "dsa_device_errors: no current device");
+  if (prev != device && hipSetDevice(device) != hipSuccess)
+    return fail(DSA_ERR_HIP, "dsa_device_errors: cannot select device %d", device);
+  int rc = hipDeviceSynchronize() == hipSuccess ? DSA_OK : fail(DSA_ERR_HIP, "dsa_device_errors: synchronise failed");
+  if (rc == DSA_OK) rc = dsa::decode_read_errors(flags);
+  if (prev != device) hipSetDevice(prev);
+  return rc;
+}
+
+int dsa_set_debug(int on) {
+  const int prev = dsa::debug_on() ? 1 : 0;
+  dsa::g_debug = on ? 1 : 0;
+  return prev;
+}
+
+int dsa_topk_plan(int B, int S, int T, int64_t* wave_rows, int64_t* block_rows) {
+  if (B < 0 || S < 0 || T < 0 || !wave_rows || !block_rows) return DSA_ERR_SHAPE;
+  dsa::topk_plan(B, S, T, wave_rows, block_rows);
+  return DSA_OK;
+}
+
+int dsa_check_idx(const int32_t* idx, int64_t count, int64_t n_rows, int64_t* first_bad) {
+  if (first_bad) *first_bad = -1;
+  if (count < 0 || n_rows < 0) return DSA_ERR_SHAPE;
+  if (count > 0 && !idx) return DSA_ERR_NULL;
+  for (int64_t i = 0; i < count; ++i) {
+    const int32_t v = idx[i];
+    if (v < -1 || (int64_t)v >= n_rows) {
+      if (first_bad) *first_bad = i;
+      return DSA_ERR_INDEX;
+    }
+  }
+  return DSA_OK;
+}
+
 int dsa_index_scores(const void* q_idx, const void* k_idx, int64_t k_batch_stride, const void* w, float w_scale,
                      int dtype, int B, int S, int T, int H_I, int D_I, int start_pos, int ratio, float* scores,
                      dsa_stream_t stream) {
-  dsa::g_err[0] = 0;
+  dsa::Entry entry_;
   if (dtype != DSA_F32 && dtype != DSA_BF16) return fail(DSA_ERR_DTYPE, "dsa_index_scores: dtype %d", dtype);
   if (B < 0 || S < 0 || T < 0 || H_I <= 0 || D_I <= 0 || start_pos < 0 || ratio <= 0)
     return fail(DSA_ERR_SHAPE, "dsa_index_scores: bad sizes B=%d S=%d T=%d H_I=%d D_I=%d start_pos=%d ratio=%d", B, S,
@@ -74,7 +218,7 @@ int dsa_index_scores(const void* q_idx, const void* k_idx, int64_t k_batch_strid
 
 int dsa_topk(const float* scores, int B, int S, int T, int index_topk, int start_pos, int ratio, int offset,
              int32_t* idx, int64_t ld_idx, dsa_stream_t stream) {
-  dsa::g_err[0] = 0;
+  dsa::Entry entry_;
   if (B < 0 || S < 0 || T < 0 || index_topk < 0 || start_pos < 0 || ratio <= 0 || offset < 0)
     return fail(DSA_ERR_SHAPE, "dsa_topk: bad sizes B=%d S=%d T=%d index_topk=%d start_pos=%d ratio=%d offset=%d", B,
                 S, T, index_topk, start_pos, ratio, offset);
@@ -93,7 +237,7 @@ int dsa_window_cols(int S, int start_pos, int W) {
 }
 
 int dsa_window_idx(int B, int S, int start_pos, int W, int32_t* idx, int64_t ld_idx, dsa_stream_t stream) {
-  dsa::g_err[0] = 0;
+  dsa::Entry entry_;
   if (B < 0) return fail(DSA_ERR_SHAPE, "dsa_window_idx: B=%d", B);
   const int Wc = dsa_window_cols(S, start_pos, W);
   if (Wc < 0) return Wc;
@@ -105,13 +249,12 @@ int dsa_window_idx(int B, int S, int start_pos, int W, int32_t* idx, int64_t ld_
 
 int dsa_select(const float* scores, int B, int S, int T, int index_topk, int start_pos, int ratio, int W,
                int offset, int32_t* idx, int64_t ld_idx, dsa_stream_t stream) {
-  dsa::g_err[0] = 0;
+  dsa::Entry entry_;
   if (B < 0 || S < 0 || T < 0 || index_topk < 0 || start_pos < 0 || ratio <= 0 || offset < 0)
     return fail(DSA_ERR_SHAPE, "dsa_select: bad sizes B=%d S=%d T=%d index_topk=%d start_pos=%d ratio=%d offset=%d",
                 B, S, T, index_topk, start_pos, ratio, offset);
   const int Wc = dsa_window_cols(S, start_pos, W);
   if (Wc < 0) return Wc;
-  dsa::g_err[0] = 0;
   const int K = index_topk < T ? index_topk : T;
   if (ld_idx < (int64_t)Wc + K)
     return fail(DSA_ERR_SHAPE, "dsa_select: ld_idx %lld < Wc + K = %d", (long long)ld_idx, Wc + K);
@@ -156,7 +299,7 @@ static int check_src(const dsa_kv_src* s, const char* name, int dtype, int D, in
 int dsa_sparse_attn(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
                     const int32_t* idx, int L, float scale, void* o, int dtype, int B, int S, int H, int D,
                     void* workspace, size_t workspace_bytes, dsa_stream_t stream) {
-  dsa::g_err[0] = 0;
+  dsa::Entry entry_;
   if (dtype != DSA_F32 && dtype != DSA_BF16) return fail(DSA_ERR_DTYPE, "dsa_sparse_attn: dtype %d", dtype);
   if (B < 0 || S < 0 || H <= 0 || D <= 0 || L < 0)
     return fail(DSA_ERR_SHAPE, "dsa_sparse_attn: bad sizes B=%d S=%d H=%d D=%d L=%d", B, S, H, D, L);
@@ -181,6 +324,11 @@ int dsa_sparse_attn(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp
   const size_t need = dsa_sparse_attn_workspace_size(dtype, B, S, H, D, L);
   if (need > 0 && (!workspace || workspace_bytes < need))
     return fail(DSA_ERR_WORKSPACE, "dsa_sparse_attn: workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (L > 0 && dsa::debug_on()) {
+    const int64_t n_total = win->n_rows + ((comp && comp->n_rows > 0) ? comp->n_rows : 0);
+    const int rc = dsa::debug_check_idx(idx, (int64_t)B * S * L, n_total, (hipStream_t)stream);
+    if (rc) return rc;
+  }
   dsa_kv_src empty{};
   const dsa_kv_src* cs = (comp && comp->n_rows > 0) ? comp : &empty;
   if (dtype == DSA_BF16)
@@ -193,14 +341,13 @@ int dsa_sparse_attn_select(const float* scores, int T, int index_topk, int start
                            const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
                            float scale, void* o, int dtype, int B, int S, int H, int D, int32_t* idx,
                            void* workspace, size_t workspace_bytes, dsa_stream_t stream) {
-  dsa::g_err[0] = 0;
+  dsa::Entry entry_;
   if (B < 0 || S < 0 || T < 0 || index_topk < 0 || start_pos < 0 || ratio <= 0)
     return fail(DSA_ERR_SHAPE, "dsa_sparse_attn_select: bad sizes B=%d S=%d T=%d index_topk=%d start_pos=%d ratio=%d",
                 B, S, T, index_topk, start_pos, ratio);
   if (!win) return fail(DSA_ERR_NULL, "dsa_sparse_attn_select: window source missing");
   const int Wc = dsa_window_cols(S, start_pos, W);
   if (Wc < 0) return Wc;
-  dsa::g_err[0] = 0;
   const int K = index_topk < T ? index_topk : T;
   const int L = Wc + K;
   if (B == 0 || S == 0) return DSA_OK;
@@ -237,7 +384,7 @@ int dsa_sparse_attn_step(const void* q_idx, const void* k_idx, int64_t k_batch_s
                          const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink, float scale, void* o,
                          int dtype, int B, int S, int H, int D, float* scores, int32_t* idx, void* workspace,
                          size_t workspace_bytes, dsa_stream_t stream) {
-  dsa::g_err[0] = 0;
+  dsa::Entry entry_;
   if (dtype != DSA_F32 && dtype != DSA_BF16) return fail(DSA_ERR_DTYPE, "dsa_sparse_attn_step: dtype %d", dtype);
   if (B < 0 || S < 0 || T < 0 || H_I <= 0 || D_I <= 0 || index_topk < 0 || start_pos < 0 || ratio <= 0)
     return fail(DSA_ERR_SHAPE,
@@ -246,7 +393,6 @@ int dsa_sparse_attn_step(const void* q_idx, const void* k_idx, int64_t k_batch_s
   if (!win) return fail(DSA_ERR_NULL, "dsa_sparse_attn_step: window source missing");
   const int Wc = dsa_window_cols(S, start_pos, W);
   if (Wc < 0) return Wc;
-  dsa::g_err[0] = 0;
   if (B == 0 || S == 0) return DSA_OK;
   const int K = index_topk < T ? index_topk : T;
   const int L = Wc + K;

@@ -139,8 +139,28 @@ __device__ __forceinline__ int visible_rows(int start_pos, int t, int ratio) {
 
 }  // namespace dsa
 
-// ---- host-side error reporting (abi.hip) -----------------------------------
 namespace dsa {
+// ---- workspace header ------------------------------------------------------------------------
+// Every workspace starts with a header of per-query rendezvous counters (4 words per query, for up
+// to kWsSyncQueries queries) that only the decode kernels touch; they leave it zero when they end,
+// so it only has to be zero before a workspace's first use.  All other scratch follows it.
+constexpr int kWsSyncQueries = 256;
+constexpr size_t kWsHeaderBytes = (size_t)kWsSyncQueries * 16;
+
+// ---- host side: error reporting, launch record, per-device set-up (abi.cpp) ------------------
+struct DeviceState {
+  int ready;          // dsa_init has run on this device
+  int xcd_rr;         // workgroup i runs on XCD i mod 8 (the decode kernels' rendezvous needs it)
+  int resident[6];    // decode kernel variants: workgroups resident at once
+  void* scratch;      // device address of the allocation-free entry point's scratch array
+};
+
 int fail(int code, const char* fmt, ...);
+// After a launch: DSA_ERR_HIP if the runtime reports an error, else records `what` as launched.
 int check_launch(const char* what);
+// The current device's state, set up (dsa_init) if it is not yet; DSA_ERR_STATE when that would
+// have to happen under stream capture.
+int ensure_device_init(hipStream_t st, DeviceState** out);
+int decode_device_init(int dev, DeviceState& ds);
+int decode_read_errors(uint32_t* bits);
 }  // namespace dsa

@@ -464,7 +464,7 @@ int sparse_attn_bf16_launch(const void* q, const dsa_kv_src* win, const dsa_kv_s
   a.L = L;
   a.scale_log2 = scale * kLog2e;
   a.o = (__bf16*)o;
-  a.part = (float*)workspace;
+  a.part = workspace ? (float*)((char*)workspace + kWsHeaderBytes) : nullptr;  // after the header
   a.S = S;
   a.H = H;
   // decode batches: two-phase kernel without partial outputs when its shape and residency fit
@@ -508,7 +508,8 @@ size_t sparse_attn_bf16_workspace(int B, int S, int H, int D, int L, bool fp4) {
   const size_t rows = (size_t)B * S * nsplit * H;
   const size_t general = nsplit <= 1 ? 0 : rows * (size_t)D * 4 + rows * 2 * 4;
   const size_t decode = sparse_attn_decode_workspace(B, S, H, D, L, fp4);
-  return general > decode ? general : decode;
+  const size_t payload = general > decode ? general : decode;
+  return payload ? kWsHeaderBytes + payload : 0;
 }
 
 }  // namespace dsa

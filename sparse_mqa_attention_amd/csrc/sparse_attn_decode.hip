@@ -8,11 +8,13 @@
 //                  LDS (direct 16-byte global->LDS loads, all rows in flight at once), computes
 //                  the logits of all 64 heads on MFMA (S^T = K . Q^T), and publishes the
 //                  probabilities P = 2^(l - m_s) in bf16 plus its per-head max m_s and sum l_s.
-//  rendezvous      the NS workgroups of the query count themselves in on an arrival counter; the
-//                  host only takes this path when every workgroup of the grid is resident at once,
-//                  and the wait is bounded (a timeout raises an error flag and poisons the output).
-//                  P and the stats travel with device-coherent stores and loads, so the rendezvous
-//                  needs no cache-wide write-back or invalidate (those cost tens of microseconds).
+//  rendezvous      the NS workgroups of the query count themselves in on an arrival counter (in
+//                  the caller's workspace, so calls on different workspaces never meet); the host
+//                  only takes this path when every workgroup of the grid is resident at once, and
+//                  the wait is bounded (a timeout raises a sticky error flag and poisons the output).
+//                  All NS workgroups of a query run on one XCD, so P and the stats travel through
+//                  the L2 they share, with no cache-wide write-back or invalidate (those cost tens
+//                  of microseconds).
 //  phase B (dims)  workgroup s computes output columns [s*D/NS, (s+1)*D/NS) of all 64 heads over
 //                  ALL rows of the query: it re-gathers just those columns of every row (hits in
 //                  the XCD's L2, which phase A of the sibling workgroups filled) and reads P from
@@ -20,8 +22,15 @@
 //                  2^(m_s - M) before it is added, then divided by sum_s l_s 2^(m_s - M) + 2^(sink - M).
 //
 // Blocks are numbered so that all NS workgroups of a query land on one XCD (dispatch assigns
-// consecutive workgroups to the 8 XCDs round-robin), keeping the rendezvous and the re-gather in
-// one L2.  What crosses HBM is each valid row once, q, o, and the small P (Q x 64 x L bf16).
+// consecutive workgroups to the 8 XCDs round-robin, which the library checks once per device; the
+// grid is padded to a multiple of 8 queries), keeping the rendezvous and the re-gather in one L2.
+// What crosses HBM is each valid row once, q, o, and the small P (Q x 64 x L bf16).
+//
+// Stale lines in a CU's L1: a workgroup reads its siblings' P and stats only after the rendezvous,
+// and P rows ([Q][64][Lp] bf16, Lp a multiple of 16*NS) and stats ([Q][NS][64][2] fp32) of
+// different queries never share a 128-byte line, so no CU can hold an early copy of a line it
+// reads there.  Scores rows ([Q][T] fp32) do share lines between neighbouring queries, so the
+// exchanged scores are written and read at device scope (past the L1).
 #include "index_tile.h"
 #include "topk_block.h"
 
@@ -32,14 +41,13 @@ namespace {
 constexpr int kDD = 512;                 // head_dim of this path
 constexpr int kDH = 64;                  // heads of this path
 constexpr int kDecRowsMax = 96;          // rows of one phase-A split: 96 KiB of LDS
-constexpr int kDecQueriesMax = 4096;
+constexpr int kDecQueriesMax = kWsSyncQueries - 1;  // padded to a multiple of 8, the grid's queries
+                                                    // still fit the workspace header
 constexpr float kLog2eD = 1.4426950408889634f;
 constexpr uint64_t kSpinTimeoutTicks = 20000000ull;  // 0.2 s of the 100 MHz constant-rate counter
 
-// Per query: arrivals at the index-score exchange (kernels that score their own rows), arrivals
-// at the phase A/B rendezvous, and departures of its workgroups.  Zero when the code object
-// loads; the last workgroup of a query to leave resets all three, so every call finds them at 0.
-__device__ uint32_t g_dec_sync[3 * kDecQueriesMax];
+// Sticky error bits of the decode kernels (bit 0: a rendezvous timed out and that query's output
+// was set to NaN); read and cleared by dsa_device_errors.
 __device__ uint32_t g_dec_error;
 
 struct DecArgs {
@@ -53,11 +61,10 @@ struct DecArgs {
   int L;
   float scale_log2;
   __bf16* o;
-  __bf16* pbuf;  // [Q][64][Lp] phase-A probabilities
-  float* stats;  // [Q][NS][64][2] phase-A (max, sum)
-  uint32_t* xcc;  // [Q][NS] XCD of each phase-A workgroup
-  int S, Q, RPS, Lp, xcd_map;
-  int local;  // all workgroups of a query share one XCD (calibrated): P and stats go through its L2
+  __bf16* pbuf;    // [Q][64][Lp] phase-A probabilities
+  float* stats;    // [Q][NS][64][2] phase-A (max, sum)
+  uint32_t* sync;  // [Qp][4] per query: score-exchange arrivals, rendezvous arrivals, departures
+  int S, Q, Qp, RPS, Lp;
   // index rows selected in the kernel (instead of read from idx): the query's scores [T], the
   // top-k size K, visibility (start_pos, ratio), window W with Wc columns, top-k offset; s == 0
   // writes the row to idx_out when that is set
@@ -92,26 +99,6 @@ struct DecCfg {
 template <int NS>
 __device__ __forceinline__ int slice_swz(int r) {
   return NS == 8 ? (((r >> 1) & 3) << 1) : 0;
-}
-
-// Write-through store of four bf16 (one 8-byte access at device scope): memory and the writer's
-// L2 both hold the new value, so a reader on the same XCD can use plain loads.
-__device__ __forceinline__ void store_coherent(__bf16* p, bf16x4 v) {
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), __builtin_bit_cast(uint64_t, v), __ATOMIC_RELAXED,
-                     __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Eight bf16 read past any stale per-XCD cached copy (two 8-byte device-scope loads).
-__device__ __forceinline__ bf16x8 load_coherent8(const __bf16* p) {
-  const uint64_t* u = reinterpret_cast<const uint64_t*>(p);
-  u32x4 r;
-  const uint64_t lo = __hip_atomic_load(u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint64_t hi = __hip_atomic_load(u + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  r[0] = (uint32_t)lo;
-  r[1] = (uint32_t)(lo >> 32);
-  r[2] = (uint32_t)hi;
-  r[3] = (uint32_t)(hi >> 32);
-  return __builtin_bit_cast(bf16x8, r);
 }
 
 // The arrival counter is polled with a device-scope load: on gfx950 only that scope skips the
@@ -166,18 +153,17 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
   const int c = lane & 31;
   const int j16 = lane & 15;
 
+  // workgroup lb runs on XCD lb % 8; the Qp/8 queries of an XCD take its workgroups NS at a time
+  // (Qp = Q rounded up to a multiple of 8; the padding queries' workgroups leave at once)
   int q, s;
   {
     const int lb = blockIdx.x;
-    if (a.xcd_map) {
-      const int xcd = lb & 7, k = lb >> 3;
-      q = xcd * (a.Q >> 3) + k / NS;
-      s = k % NS;
-    } else {
-      q = lb / NS;
-      s = lb % NS;
-    }
+    const int xcd = lb & 7, k = lb >> 3;
+    q = xcd * (a.Qp >> 3) + k / NS;
+    s = k % NS;
   }
+  if (q >= a.Q) return;
+  uint32_t* const qsync = a.sync + 4 * q;
   const int L = a.L;
   const int bq = q / a.S;  // batch of the query's KV
   const int32_t* irow = a.idx + (int64_t)q * L;
@@ -266,7 +252,8 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
                                        : index_tile_sum<DI, 2>(qi_lds, wi_lds, kreg[n], hf, c);
             if (j < cvis) v = a.w_scale * sum;
           }
-          if (hf == 0 && j < j1) srow[j] = v;
+          // written at device scope: the row may share lines with a neighbouring query's row
+          if (hf == 0 && j < j1) __hip_atomic_store(&srow[j], v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
       }
       // every score of this workgroup has reached L2 before it counts itself in
@@ -276,7 +263,7 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
 #pragma unroll
       for (int k = 0; k < kDD / 32; ++k) qreg[k] = *reinterpret_cast<const bf16x8*>(qp + 16 * k);
       if (tid == 0) {
-        uint32_t* arrive_ix = &g_dec_sync[3 * q];
+        uint32_t* arrive_ix = &qsync[0];
         __hip_atomic_fetch_add(arrive_ix, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         const uint64_t t0 = wall_clock64();
         int to = 0;
@@ -297,8 +284,9 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
       for (int i = tid; i < a.K; i += 256) idx_lds[a.Wc + i] = i < cvis ? i + a.offset : -1;
     } else {
       int* top = idx_lds + a.Wc;
-      topk_dev::block_topk<256, SKPT>(a.scores + (int64_t)q * a.T, a.T, cvis, a.K, a.offset, tsm,
-                                      [&](int slot, int v) { top[slot] = v; });
+      // scores the siblings wrote in this launch are read at device scope (past the L1)
+      topk_dev::block_topk<256, SKPT, IX != 0>(a.scores + (int64_t)q * a.T, a.T, cvis, a.K, a.offset, tsm,
+                                               [&](int slot, int v) { top[slot] = v; });
     }
     __syncthreads();
     // the row as selected (one workgroup of the query), then its slot codes in place (each entry
@@ -397,35 +385,25 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
       // each half of the pair writes half of the rows; rows past nr carry P = 0
       if (rb < a.RPS && (g >> 1) == dh) {
         const bf16x4 pv = {(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
-        if (a.local)
-          *reinterpret_cast<bf16x4*>(prow + rb) = pv;
-        else
-          store_coherent(prow + rb, pv);
+        *reinterpret_cast<bf16x4*>(prow + rb) = pv;
       }
     }
   }
   lsum += shfl_xor(lsum, 32);
-  const uint32_t my_xcc = a.local ? 0u : xcc_id();
   if (dh == 0 && hf == 0) {
     float* st = a.stats + (((int64_t)q * NS + s) * kDH + head) * 2;
-    if (a.local) {
-      st[0] = mloc;
-      st[1] = lsum;
-    } else {
-      __hip_atomic_store(st, mloc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(st + 1, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    st[0] = mloc;
+    st[1] = lsum;
   }
-  if (tid == 0 && !a.local) __hip_atomic_store(a.xcc + (int64_t)q * NS + s, my_xcc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // =============================== arrival at the query's rendezvous
-  // P, the stats and the XCD ids were stored write-through at device scope; each wave waits for
-  // them to complete before the barrier, so they are visible to every reader once the count
-  // reaches NS.  No cache-wide write-back or invalidate.  Nothing else is in flight here.
+  // P and the stats are in the L2 the query's workgroups share once each wave's stores have
+  // completed (the wait below, before the barrier), so they are visible to every reader once the
+  // count reaches NS.  No cache-wide write-back or invalidate.  Nothing else is in flight here.
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();  // also: every wave is done with phase A's rows
-  uint32_t* arrive = &g_dec_sync[3 * q + 1];
-  uint32_t* depart = &g_dec_sync[3 * q + 2];
+  uint32_t* arrive = &qsync[1];
+  uint32_t* depart = &qsync[2];
   if (tid == 0) __hip_atomic_fetch_add(arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // =============================== phase B gather, independent of the other workgroups
@@ -465,13 +443,6 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
   }
   __builtin_amdgcn_s_waitcnt(0);  // the slices have landed
   __syncthreads();
-  // a writer on another XCD means P must be read past this XCD's L2
-  bool remote = false;
-  if (!a.local) {
-    const uint32_t wx = lane < NS ? __hip_atomic_load(a.xcc + (int64_t)q * NS + lane, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT) : my_xcc;
-    remote = __builtin_amdgcn_ballot_w64(wx != my_xcc) != 0ull;
-  }
 
   // =============================== phase B: columns [d0, d0 + DS) of every head over all rows
   const int hb = wave & 1, kh = wave >> 1;
@@ -485,12 +456,10 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
     for (int k = 0; k < C::KPS; ++k) {
       const int r0 = (kh + 2 * tl) * a.RPS + 16 * k;
       const bool ok = 16 * k < a.RPS && r0 < Lk;
-      pre[tl][k] = !ok ? bf16x8{} : remote ? load_coherent8(pcol + r0) : *reinterpret_cast<const bf16x8*>(pcol + r0);
+      pre[tl][k] = !ok ? bf16x8{} : *reinterpret_cast<const bf16x8*>(pcol + r0);
     }
   for (int i = tid; i < NS * kDH * 2; i += 256)
-    stats_lds[i] = a.local ? a.stats[(int64_t)q * NS * kDH * 2 + i]
-                           : __hip_atomic_load(a.stats + (int64_t)q * NS * kDH * 2 + i, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
+    stats_lds[i] = a.stats[(int64_t)q * NS * kDH * 2 + i];
   __syncthreads();
   const float sink2 = a.sink[headB] * kLog2eD;
   float M = sink2;
@@ -567,14 +536,14 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
   // leaves, and that one clears the pair for the next call
   if (tid == 0 &&
       __hip_atomic_fetch_add(depart, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == (uint32_t)(NS - 1)) {
-    if (IX != 0) __hip_atomic_exchange(&g_dec_sync[3 * q], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (IX != 0) __hip_atomic_exchange(&qsync[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_exchange(arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_exchange(depart, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
-// One-time check of how workgroups land on XCDs: the XCD-local rendezvous needs every
-// workgroup with the same blockIdx mod 8 on the same XCD.
+// How workgroups land on XCDs: the XCD-local rendezvous needs every workgroup with the same
+// blockIdx mod 8 on the same XCD.  Run once per device by dsa_init.
 __device__ uint32_t g_xcc_probe[2048];
 
 __global__ void xcc_probe_kernel() {
@@ -585,25 +554,7 @@ struct DecPlan {
   int ns, rps, lp, ok;
 };
 
-int g_resident_blocks[64][6] = {};  // per device and kernel variant: workgroups resident at once
-int g_xcd_local[64] = {};           // per device: 0 unknown, 1 XCD-local rendezvous valid, -1 not
-
-int xcd_local_mode(int dev, hipStream_t st) {
-  if (g_xcd_local[dev] != 0) return g_xcd_local[dev] > 0;
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(st, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return 0;  // decide later
-  int ok = 1;
-  hipLaunchKernelGGL(xcc_probe_kernel, dim3(2048), dim3(64), 0, st);
-  uint32_t ids[2048];
-  if (hipGetLastError() != hipSuccess || hipStreamSynchronize(st) != hipSuccess ||
-      hipMemcpyFromSymbol(ids, HIP_SYMBOL(g_xcc_probe), sizeof(ids)) != hipSuccess) {
-    ok = 0;
-  } else {
-    for (int i = 8; i < 2048; ++i) ok &= ids[i] == ids[i & 7];
-  }
-  g_xcd_local[dev] = ok ? 1 : -1;
-  return ok;
-}
+constexpr int kDecVariants = 6;  // (NS 8 | 16) x (idx rows given | selected | scored and selected)
 
 template <int NS, int SKPT, int IX>
 int resident_blocks(int dev) {
@@ -617,7 +568,7 @@ int resident_blocks(int dev) {
 
 DecPlan plan_decode(int Q, int H, int D, int L, bool fp4) {
   DecPlan p{0, 0, 0, 0};
-  if (D != kDD || H != kDH || fp4 || Q <= 0 || Q >= 256 || Q > kDecQueriesMax || L <= 0) return p;
+  if (D != kDD || H != kDH || fp4 || Q <= 0 || Q > kDecQueriesMax || L <= 0) return p;
   p.ns = Q > 16 ? 8 : 16;
   const int per = (L + p.ns - 1) / p.ns;
   p.rps = (per + 15) & ~15;
@@ -629,20 +580,53 @@ DecPlan plan_decode(int Q, int H, int D, int L, bool fp4) {
   return p;
 }
 
+const char* const kDecNames[kDecVariants] = {
+    "sparse_attn_decode<NS=8>",         "sparse_attn_decode<NS=16>",
+    "sparse_attn_decode<NS=8,select>",  "sparse_attn_decode<NS=16,select>",
+    "sparse_attn_decode<NS=8,score+select>", "sparse_attn_decode<NS=16,score+select>"};
+
 }  // namespace
 
+// One-time set-up of the decode kernels on device `dev` (current): the XCD placement probe (one
+// launch on a private stream, then a synchronisation) and the resident workgroup count of every
+// variant.
+int decode_device_init(int dev, DeviceState& ds) {
+  hipStream_t st = nullptr;
+  if (hipStreamCreateWithFlags(&st, hipStreamNonBlocking) != hipSuccess)
+    return fail(DSA_ERR_HIP, "dsa_init: stream creation failed on device %d", dev);
+  hipLaunchKernelGGL(xcc_probe_kernel, dim3(2048), dim3(64), 0, st);
+  uint32_t ids[2048];
+  int ok = 1;
+  if (hipGetLastError() != hipSuccess || hipStreamSynchronize(st) != hipSuccess ||
+      hipMemcpyFromSymbol(ids, HIP_SYMBOL(g_xcc_probe), sizeof(ids)) != hipSuccess) {
+    hipStreamDestroy(st);
+    return fail(DSA_ERR_HIP, "dsa_init: XCD placement probe failed on device %d", dev);
+  }
+  hipStreamDestroy(st);
+  for (int i = 8; i < 2048; ++i) ok &= ids[i] == ids[i & 7];
+  ds.xcd_rr = ok;
+  ds.resident[0] = resident_blocks<8, 0, 0>(dev);
+  ds.resident[1] = resident_blocks<16, 0, 0>(dev);
+  ds.resident[2] = resident_blocks<8, 8, 0>(dev);
+  ds.resident[3] = resident_blocks<16, 8, 0>(dev);
+  ds.resident[4] = resident_blocks<8, 8, 1>(dev);
+  ds.resident[5] = resident_blocks<16, 8, 1>(dev);
+  return DSA_OK;
+}
+
+// Bytes after the workspace header: P, then the stats.
 size_t sparse_attn_decode_workspace(int B, int S, int H, int D, int L, bool fp4) {
   const DecPlan p = plan_decode(B * S, H, D, L, fp4);
   if (!p.ok) return 0;
   const size_t Q = (size_t)B * S;
-  return Q * kDH * p.lp * 2 + Q * p.ns * kDH * 2 * 4 + Q * p.ns * 4;
+  return Q * kDH * p.lp * 2 + Q * p.ns * kDH * 2 * 4;
 }
 
 // Returns 1 and launches when the two-phase decode path applies, 0 when the caller should use
 // the general kernel, or a negative error.  With sel set, the kernel selects the index rows itself
 // (idx is not read); that needs at most 2048 scores per row.  With ix set too, it also computes
-// those scores (index head dim 128, at most 64 index heads), which needs every workgroup of a
-// query on one XCD.
+// those scores (index head dim 128, at most 64 index heads).  `workspace` is the whole caller
+// workspace: its header holds the per-query counters, P and the stats follow.
 int sparse_attn_decode_launch(const __bf16* q, const unsigned char* win, int64_t win_n, int64_t win_bs,
                               int64_t win_rs, const unsigned char* comp, int64_t comp_n, int64_t comp_bs,
                               int64_t comp_rs, const float* sink, const int32_t* idx, int L, float scale_log2,
@@ -656,19 +640,14 @@ int sparse_attn_decode_launch(const __bf16* q, const unsigned char* win, int64_t
   if ((uint64_t)win_n * (uint64_t)win_rs >= (1ull << 31) || (uint64_t)comp_n * (uint64_t)comp_rs >= (1ull << 31))
     return 0;
   if ((((uintptr_t)win | (uintptr_t)comp) & 15) || ((win_rs | win_bs | comp_rs | comp_bs) & 15)) return 0;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  DeviceState* ds = nullptr;
+  const int irc = ensure_device_init(st, &ds);
+  if (irc) return irc;
+  if (!ds->xcd_rr) return 0;  // workgroups do not land on XCDs round-robin: no XCD-local rendezvous
   const int vi = (p.ns == 8 ? 0 : 1) + (sel ? 2 : 0) + (ix ? 2 : 0);
-  int& resident = g_resident_blocks[dev][vi];
-  if (resident == 0)
-    resident = vi == 0 ? resident_blocks<8, 0, 0>(dev)
-             : vi == 1 ? resident_blocks<16, 0, 0>(dev)
-             : vi == 2 ? resident_blocks<8, 8, 0>(dev)
-             : vi == 3 ? resident_blocks<16, 8, 0>(dev)
-             : vi == 4 ? resident_blocks<8, 8, 1>(dev)
-                       : resident_blocks<16, 8, 1>(dev);
   const int Q = B * S;
-  if (Q * p.ns > resident) return 0;  // the rendezvous needs every workgroup resident at once
+  const int Qp = (Q + 7) & ~7;
+  if (Qp * p.ns > ds->resident[vi]) return 0;  // the rendezvous needs every workgroup resident at once
   DecArgs a{};
   a.q = q;
   a.win = win;
@@ -683,16 +662,14 @@ int sparse_attn_decode_launch(const __bf16* q, const unsigned char* win, int64_t
   a.L = L;
   a.scale_log2 = scale_log2;
   a.o = o;
-  a.pbuf = (__bf16*)workspace;
-  a.stats = (float*)((char*)workspace + (size_t)Q * kDH * p.lp * 2);
-  a.xcc = (uint32_t*)(a.stats + (size_t)Q * p.ns * kDH * 2);
+  a.sync = (uint32_t*)workspace;
+  a.pbuf = (__bf16*)((char*)workspace + kWsHeaderBytes);
+  a.stats = (float*)((char*)a.pbuf + (size_t)Q * kDH * p.lp * 2);
   a.S = S;
   a.Q = Q;
+  a.Qp = Qp;
   a.RPS = p.rps;
   a.Lp = p.lp;
-  a.xcd_map = (Q % 8 == 0) ? 1 : 0;
-  a.local = a.xcd_map && xcd_local_mode(dev, st);
-  if (ix && !a.local) return 0;  // the score exchange reads its siblings' plain stores from one L2
   if (sel) {
     a.scores = sel->scores;
     a.T = sel->T;
@@ -713,7 +690,7 @@ int sparse_attn_decode_launch(const __bf16* q, const unsigned char* win, int64_t
     a.w_scale = ix->w_scale;
     a.H_I = ix->H_I;
   }
-  dim3 grid(Q * p.ns);
+  dim3 grid(Qp * p.ns);
   switch (vi) {
     case 0: hipLaunchKernelGGL((sparse_attn_decode_kernel<8, 0, 0>), grid, dim3(256), 0, st, a); break;
     case 1: hipLaunchKernelGGL((sparse_attn_decode_kernel<16, 0, 0>), grid, dim3(256), 0, st, a); break;
@@ -722,8 +699,18 @@ int sparse_attn_decode_launch(const __bf16* q, const unsigned char* win, int64_t
     case 4: hipLaunchKernelGGL((sparse_attn_decode_kernel<8, 8, 1>), grid, dim3(256), 0, st, a); break;
     default: hipLaunchKernelGGL((sparse_attn_decode_kernel<16, 8, 1>), grid, dim3(256), 0, st, a); break;
   }
-  const int rc = check_launch("sparse_attn_decode");
+  const int rc = check_launch(kDecNames[vi]);
   return rc ? rc : 1;
+}
+
+// Read and clear the sticky error bits of the decode kernels (device `dev` current, idle).
+int decode_read_errors(uint32_t* bits) {
+  uint32_t v = 0, z = 0;
+  if (hipMemcpyFromSymbol(&v, HIP_SYMBOL(g_dec_error), sizeof(v)) != hipSuccess ||
+      hipMemcpyToSymbol(HIP_SYMBOL(g_dec_error), &z, sizeof(z)) != hipSuccess)
+    return fail(DSA_ERR_HIP, "dsa_device_errors: reading the error flags failed");
+  *bits = v;
+  return DSA_OK;
 }
 
 }  // namespace dsa

@@ -242,7 +242,7 @@ topk_wave_kernel(const float* __restrict__ scores, int rows, int S, int T, int K
           const bool keep = key[g] >= thr;
           const uint64_t kb = __builtin_amdgcn_ballot_w64(keep);
           const int pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(kb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)kb, 0));
-          if (keep) *(int32_t*)((char*)out + (uint32_t)pos * 4u) = 64 * g + lane + offset;
+          if (keep && pos < K) *(int32_t*)((char*)out + (uint32_t)pos * 4u) = 64 * g + lane + offset;
           base += __builtin_popcountll(kb);
         }
       }
@@ -264,7 +264,7 @@ topk_wave_kernel(const float* __restrict__ scores, int rows, int S, int T, int K
         const bool keep = key[g] > tau || (key[g] == tau && rank < remaining);
         const uint64_t kb = __builtin_amdgcn_ballot_w64(keep);
         const int pos = base + __builtin_amdgcn_mbcnt_hi((uint32_t)(kb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)kb, 0));
-        if (keep) *(int32_t*)((char*)out + (uint32_t)pos * 4u) = 64 * g + lane + offset;
+        if (keep && pos < K) *(int32_t*)((char*)out + (uint32_t)pos * 4u) = 64 * g + lane + offset;
         base += __builtin_popcountll(kb);
       }
     }
@@ -283,26 +283,45 @@ int launch_topk(const float* scores, int B, int S, int T, int K, int sp, int r, 
                 int64_t ld, int W, int Wc, hipStream_t st) {
   hipLaunchKernelGGL((topk_kernel<NT, KPT>), dim3(B * S), dim3(NT), 0, st, scores, S, T, K, sp, r, off, idx, ld, 0, W,
                      Wc);
-  return check_launch("topk");
+  return check_launch("topk_block");
 }
 
 }  // namespace
 
-// Rows 0 .. rows-tail-1 on the one-wave kernel, whose reads of 64*KPL positions per row stay inside
-// the buffer; the last `tail` rows on the per-row workgroup kernel (NT threads x KPT keys).
+// Rows 0 .. head-1 on the one-wave kernel, whose reads of up to 64*KPL positions per row stay
+// inside the buffer; the last `tail` rows on the per-row workgroup kernel (NT threads x KPT keys).
+void topk_wave_split(int64_t rows, int T, int KPL, int64_t* head, int64_t* tail) {
+  // row r reads positions r*T .. r*T + 64*KPL - 1, inside rows*T positions iff r <= rows - 64*KPL/T
+  const int64_t over = ((int64_t)64 * KPL - T + T - 1) / T;  // rows whose read span would pass the end
+  *tail = over < rows ? over : rows;
+  *head = rows - *tail;
+}
+
 template <int KPL, int NT, int KPT>
 int launch_topk_wave(const float* scores, int B, int S, int T, int K, int sp, int r, int off, int32_t* idx,
                      int64_t ld, int W, int Wc, hipStream_t st) {
-  const int rows = B * S;
-  const int tail = (64 * KPL - T + T - 1) / T;  // rows whose read span would pass the end
-  const int head = rows - tail;
-  hipLaunchKernelGGL((topk_wave_kernel<KPL>), dim3((head + 3) / 4), dim3(256), 0, st, scores, head, S, T, K, sp, r,
-                     off, idx, ld, W, Wc);
-  int rc = check_launch("topk_wave");
+  int64_t head64, tail64;
+  topk_wave_split((int64_t)B * S, T, KPL, &head64, &tail64);
+  const int head = (int)head64, tail = (int)tail64;
+  int rc = DSA_OK;
+  if (head > 0) {
+    hipLaunchKernelGGL((topk_wave_kernel<KPL>), dim3((head + 3) / 4), dim3(256), 0, st, scores, head, S, T, K, sp, r,
+                       off, idx, ld, W, Wc);
+    rc = check_launch(KPL == 32 ? "topk_wave<32>" : KPL == 64 ? "topk_wave<64>" : "topk_wave<128>");
+  }
   if (rc || tail == 0) return rc;
   hipLaunchKernelGGL((topk_kernel<NT, KPT>), dim3(tail), dim3(NT), 0, st, scores, S, T, K, sp, r, off, idx, ld,
                      head, W, Wc);
-  return check_launch("topk");
+  return check_launch("topk_block");
+}
+
+// Rows of a top-k call on the one-wave kernel and on the per-row workgroup kernel.
+void topk_plan(int B, int S, int T, int64_t* wave_rows, int64_t* block_rows) {
+  const int64_t rows = (int64_t)B * S;
+  *wave_rows = 0;
+  *block_rows = rows;
+  if (rows < 1024 || T > 8192 || T <= 0) return;
+  topk_wave_split(rows, T, T <= 2048 ? 32 : T <= 4096 ? 64 : 128, wave_rows, block_rows);
 }
 
 // idx points at the row base; a row gets Wc window entries (W the window) then its K top-k entries.

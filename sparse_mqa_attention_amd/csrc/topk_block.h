@@ -118,7 +118,10 @@ struct TopkSmem {
 // threshold and, of the keys equal to it, the lowest positions (ranked by a packed block scan that
 // is skipped when the select stopped early: then every equal key is kept); a second packed scan
 // gives each kept position its slot.
-template <int NT, int KPT, typename Put>
+//
+// CO = true reads the scores at device scope (past the CU's L1), for rows that other workgroups
+// wrote during the same launch.
+template <int NT, int KPT, bool CO = false, typename Put>
 __device__ __forceinline__ void block_topk(const float* __restrict__ srow, int T, int c, int K, int offset,
                                            TopkSmem<NT>& sm, Put put) {
   constexpr int NW = NT / 64;
@@ -146,7 +149,15 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ srow, int T
     for (int j = 0; j < J; ++j) {
       const int p0 = E * (NT * j + tid);
       const float* src = srow + (p0 < c ? p0 : 0);
-      if constexpr (E >= 4) {
+      if constexpr (CO) {  // 8-byte device-scope loads
+#pragma unroll
+        for (int q = 0; q < E / 2; ++q) {
+          const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(src + 2 * q), __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+          key[j * E + 2 * q + 0] = (uint32_t)v;
+          key[j * E + 2 * q + 1] = (uint32_t)(v >> 32);
+        }
+      } else if constexpr (E >= 4) {
 #pragma unroll
         for (int q = 0; q < E / 4; ++q) {
           const float4 v = *reinterpret_cast<const float4*>(src + 4 * q);
@@ -165,7 +176,12 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ srow, int T
 #pragma unroll
     for (int j = 0; j < J; ++j)
 #pragma unroll
-      for (int e = 0; e < E; ++e) key[j * E + e] = __float_as_uint(srow[min(E * (NT * j + tid) + e, c - 1)]);
+      for (int e = 0; e < E; ++e) {
+        const float* src = srow + min(E * (NT * j + tid) + e, c - 1);
+        key[j * E + e] = CO ? __hip_atomic_load(reinterpret_cast<const uint32_t*>(src), __ATOMIC_RELAXED,
+                                                __HIP_MEMORY_SCOPE_AGENT)
+                            : __float_as_uint(*src);
+      }
   }
   // this pass's histogram set starts at zero (the other set is cleared during the first pass)
   for (int i = tid; i < R * RP / 4; i += NT) reinterpret_cast<int4*>(sm.hist[0])[i] = int4{0, 0, 0, 0};

@@ -26,7 +26,9 @@ def test_header_declares_the_step():
     names = _declared()
     for n in ["dsa_index_scores", "dsa_topk", "dsa_window_idx", "dsa_select", "dsa_sparse_attn",
               "dsa_sparse_attn_select", "dsa_sparse_attn_step", "dsa_last_error",
-              "dsa_abi_version", "dsa_sparse_attn_workspace_size", "dsa_window_cols"]:
+              "dsa_abi_version", "dsa_sparse_attn_workspace_size", "dsa_window_cols", "dsa_init",
+              "dsa_device_errors", "dsa_last_launch_count", "dsa_last_launches", "dsa_set_debug", "dsa_check_idx",
+              "dsa_topk_plan"]:
         assert n in names
 
 
@@ -34,7 +36,7 @@ def test_library_exports_every_declared_symbol(dsa):
     lib = ctypes.CDLL(dsa.LIB_PATH)
     for n in _declared():
         assert hasattr(lib, n), n
-    assert dsa.lib.dsa_abi_version() == 1
+    assert dsa.lib.dsa_abi_version() == 2
 
 
 def test_window_cols(dsa):
@@ -146,3 +148,102 @@ def test_no_cpu_fallback_in_binding():
     # the product package never imports the oracle
     src = open(os.path.join(ROOT, "sparse_mqa_attention_amd", "__init__.py")).read()
     assert "oracle" not in src.replace("oracle is", "")
+
+
+def test_workspace_has_header(dsa):
+    lib = dsa.lib
+    # every nonzero workspace starts with the 4 KiB counter header
+    need = lib.dsa_sparse_attn_workspace_size(1, 32, 1, 64, 512, 640)
+    assert need > 4096
+    split = lib.dsa_sparse_attn_workspace_size(1, 2, 3, 32, 128, 130)  # general kernel's partials
+    assert split > 4096
+
+
+def test_check_idx_host(dsa):
+    """The DSA_DEBUG range check (host side): -1 and [0, rows) pass, anything else is rejected
+    with the first bad position."""
+    import numpy as np
+
+    assert dsa.dsa_check_idx(np.array([-1, 0, 5, 9], dtype=np.int32), 10) == (True, -1)
+    assert dsa.dsa_check_idx(np.array([3, -1, 10, 11], dtype=np.int32), 10) == (False, 2)
+    assert dsa.dsa_check_idx(np.array([0, -2], dtype=np.int32), 10) == (False, 1)
+    assert dsa.dsa_check_idx(np.zeros(0, dtype=np.int32), 0) == (True, -1)
+    assert dsa.dsa_check_idx(np.array([0], dtype=np.int32), 0) == (False, 0)
+    big = np.full(1 << 16, 7, dtype=np.int32)
+    big[-1] = -3
+    assert dsa.dsa_check_idx(big, 8) == (False, (1 << 16) - 1)
+    prev = dsa.dsa_set_debug(True)
+    assert dsa.dsa_set_debug(prev) is True
+
+
+@pytest.mark.parametrize("rows,T", [(1024, 1), (1500, 1), (2047, 1), (2047, 2), (1024, 3), (1100, 4000), (5000, 64),
+                                    (4096, 2048), (2048, 8192), (3000, 9000), (1023, 5)])
+def test_topk_row_split(dsa, rows, T):
+    """The one-wave top-k kernel reads a whole number of 64-key groups per row (up to 64*KPL keys):
+    every row it gets must keep that span inside the B*S*T scores, and the rest go to the per-row
+    kernel, never a negative count."""
+    wave, block = dsa.dsa_topk_plan(1, rows, T)
+    assert wave >= 0 and block >= 0 and wave + block == rows
+    if rows < 1024 or T > 8192:
+        assert wave == 0
+        return
+    kpl = 32 if T <= 2048 else 64 if T <= 4096 else 128
+    if wave:
+        assert (wave - 1) * T + 64 * kpl <= rows * T  # the last wave row's reads stay in the buffer
+    if block and wave + 1 <= rows - 1:
+        assert wave * T + 64 * kpl > rows * T  # the split point is the first row that would overrun
+
+
+def test_binding_validates_before_launch(dsa):
+    """Mis-shaped or mistyped operands are refused by the binding with DSA_ERR_SHAPE/DTYPE before
+    any pointer reaches the library (CPU tensors: the checks run ahead of the device check)."""
+    import torch
+
+    q = torch.zeros(1, 2, 4, 64, dtype=torch.bfloat16)
+    kv = torch.zeros(1, 5, 64, dtype=torch.bfloat16)
+    idx = torch.zeros(1, 2, 3, dtype=torch.int32)
+    sink = torch.zeros(4)
+    cases = [
+        (dict(sink=torch.zeros(4, dtype=torch.bfloat16)), -3),  # sink must be float32
+        (dict(sink=torch.zeros(5)), -2),                        # sink must be [H]
+        (dict(kv_win=torch.zeros(1, 5, 64)), -3),              # kv dtype differs from q
+        (dict(kv_win=torch.zeros(1, 5, 32, dtype=torch.bfloat16)), -2),
+        (dict(out=torch.zeros(1, 2, 4, 32, dtype=torch.bfloat16)), -2),
+        (dict(idx=torch.zeros(1, 2, 3, dtype=torch.int64)), -2),
+        (dict(kv_comp=torch.zeros(1, 3, 64)), -3),
+    ]
+    for over, code in cases:
+        a = dict(q=q, kv_win=kv, kv_comp=None, sink=sink, idx=idx, out=None)
+        a.update(over)
+        with pytest.raises(dsa.DsaError) as e:
+            dsa.dsa_sparse_attn(a["q"], a["kv_win"], a["kv_comp"], a["sink"], a["idx"], 1.0, out=a["out"])
+        assert e.value.code == code, (over, e.value)
+    qI = torch.zeros(1, 2, 4, 32, dtype=torch.bfloat16)
+    kI = torch.zeros(1, 3, 32, dtype=torch.bfloat16)
+    with pytest.raises(dsa.DsaError) as e:
+        dsa.dsa_index_scores(qI, kI, torch.zeros(1, 2, 4), 1.0, 0, 1)  # w dtype differs
+    assert e.value.code == -3
+    with pytest.raises(dsa.DsaError) as e:
+        dsa.dsa_index_scores(qI, kI, torch.zeros(1, 2, 4, dtype=torch.bfloat16), 1.0, 0, 1,
+                             out=torch.zeros(1, 2, 4))
+    assert e.value.code == -2
+    # the whole step: scores of the wrong shape
+    with pytest.raises(dsa.DsaError) as e:
+        dsa.dsa_sparse_attn_step(qI, kI, torch.zeros(1, 2, 4, dtype=torch.bfloat16), q, kv, None, sink, index_topk=2,
+                                 start_pos=0, ratio=1, W=2, scale=1.0, w_scale=1.0, scores=torch.zeros(1, 2, 5))
+    assert e.value.code == -2
+
+
+def test_init_and_errors_need_a_device(dsa):
+    """Without a GPU, the set-up and error-flag calls fail cleanly with an error code."""
+    import ctypes
+
+    import torch
+
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert dsa.lib.dsa_init(0) == -5
+    v = ctypes.c_uint32(7)
+    assert dsa.lib.dsa_device_errors(0, ctypes.byref(v)) == -5
+    assert dsa.lib.dsa_device_errors(0, None) == -1
+    assert dsa.lib.dsa_init(-1) == -2

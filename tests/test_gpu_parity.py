@@ -35,6 +35,16 @@ def _to_dev(d):
     return {k: v.to(DEV) for k, v in d.items()}
 
 
+def _launched():
+    """(count, names) of the kernels the last library call on this thread launched."""
+    return _dsa().dsa_last_launches()
+
+
+def _assert_one_launch(kind):
+    n, names = _launched()
+    assert n == 1 and kind in names, f"expected one {kind} launch, got {n}: {names}"
+
+
 def _kv_cat64(cpu_inputs, w):
     if w.comp_fmt == "fp4":
         comp = oracle.fp4_rows_decode(cpu_inputs["kv_comp_fp4"], cpu_inputs["kv_comp_scale"])
@@ -75,6 +85,12 @@ def test_window_idx(B, S, sp, W):
     (2, 600, 8000, 300, 100, 2, "normal"),
     (1, 1030, 8192, 512, 0, 4, "zeros"),
     (1, 1500, 1999, 7, 0, 1, "ties"),
+    # tiny T at 1024..2047 rows: most rows' one-wave reads would pass the end of the scores, so
+    # they go to the per-row kernel
+    (1, 1500, 1, 1, 0, 1, "normal"),
+    (1, 2047, 1, 4, 0, 1, "normal"),
+    (1, 1024, 2, 1, 0, 1, "ties"),
+    (3, 700, 2, 2, 0, 1, "normal"),
 ])
 def test_topk_bit_exact(B, S, T, K, sp, ratio, kind):
     """Given the same float32 scores, the GPU selection equals the oracle's exactly."""
@@ -298,9 +314,14 @@ def test_step_full(name):
     cpu_in = dsa_synth.generate(w, seed=0)
     dev_in = _to_dev(cpu_in)
     o, idx, scores = _step(w, dev_in)
+    n, names = _launched()
+    _log(f"  launches: {n} {names}")
+    if name == "decode_b32_ctx8k":
+        _assert_one_launch("score+select")  # the launch configuration the benchmark times
     torch.cuda.synchronize()
     rows = [(b, t) for b in range(w.B) for t in range(w.S)]
     _check_step(w, cpu_in, o, idx, scores, rows)
+    assert _dsa().dsa_device_errors() == 0
 
 
 @pytest.mark.parametrize("name,S", [("prefill_s8k", 640), ("prefill_s32k_fp4", 700), ("prefill_s8k", 2100)])
@@ -375,6 +396,12 @@ def test_sparse_attn_select(B, T, ctx, kind):
     args = (torch.from_numpy(sc).to(DEV), q.to(DEV), kv_win.to(DEV), kv_comp.to(DEV), sink.to(DEV))
     for call in range(2):
         o, idx = dsa.dsa_sparse_attn_select(*args, index_topk=K, start_pos=sp, ratio=ratio, W=nw, scale=scale)
+        n, names = _launched()
+        _log(f"  launches: {n} {names}")
+        if T <= 2048:
+            _assert_one_launch("select")
+        else:
+            assert n >= 2 and "sparse_attn_decode<" in names, names
         np.testing.assert_array_equal(idx.cpu().numpy(), exp_idx)
         err = max_abs_err(o.float().cpu().numpy(), exp_o)
         _log(f"  call {call}: max abs err {err:.3e}")
@@ -384,9 +411,12 @@ def test_sparse_attn_select(B, T, ctx, kind):
 # ------------------------------------------------------------------------ the whole step in one call
 @pytest.mark.parametrize("B,T,ctx,H_I", [
     (32, 2048, 8192, 32),   # decode, one launch: 8 workgroups per query score 256 rows each
-    (5, 1999, 7996, 64),    # 16 workgroups per query, two MFMA tiles of index heads, ragged tail
+    (5, 1999, 7996, 64),    # 16 workgroups per query, two MFMA tiles of index heads, ragged tail;
+                            # the grid is padded to 8 queries
     (3, 300, 1200, 40),     # fewer visible rows than index_topk: all kept, -1 tail
-    (16, 100, 400, 8),      # most workgroups score no rows
+    (16, 100, 400, 8),      # most workgroups score no rows; score rows share cache lines
+    (8, 1000, 4000, 64),    # 16 workgroups per query, 64 index heads
+    (24, 777, 3108, 40),    # 8 workgroups per query, 40 index heads, ragged T
     (4, 4000, 16000, 32),   # more than 2048 scores per row: index scores, then the select call
 ])
 def test_sparse_attn_step(B, T, ctx, H_I):
@@ -425,6 +455,12 @@ def test_sparse_attn_step(B, T, ctx, H_I):
     assert err <= ATTN_TOL["bf16"], err
     for call in range(3):
         o, idx, scores = dsa.dsa_sparse_attn_step(*dev, w_scale=w_scale, **kw)
+        n, names = _launched()
+        _log(f"  launches: {n} {names}")
+        if T <= 2048:
+            _assert_one_launch("score+select")
+        else:
+            assert n >= 3 and "index_scores" in names, names
         np.testing.assert_array_equal(scores.cpu().numpy(), ref_scores)
         np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
         np.testing.assert_array_equal(o.float().cpu().numpy(), ref_o)
@@ -432,18 +468,20 @@ def test_sparse_attn_step(B, T, ctx, H_I):
 
 
 # ------------------------------------------------------------------------ two-phase decode path
-@pytest.mark.parametrize("B,S,L,nc,inval", [
-    (32, 1, 640, 2048, 0.0),   # 8 splits, XCD-grouped blocks
-    (24, 1, 640, 1000, 0.1),   # 8 splits
-    (5, 1, 640, 700, 0.2),     # 16 splits, plain block order
-    (16, 1, 640, 16384, 0.0),  # 16 splits
-    (3, 1, 1000, 900, 0.3),    # 16 splits, L > 768
-    (2, 1, 17, 30, 0.0),       # most splits empty
-    (4, 2, 200, 100, 0.5),     # two queries per sequence
+@pytest.mark.parametrize("B,S,L,nc,inval,kernel", [
+    (32, 1, 640, 2048, 0.0, "sparse_attn_decode<NS=8>"),
+    (24, 1, 640, 1000, 0.1, "sparse_attn_decode<NS=8>"),
+    (5, 1, 640, 700, 0.2, "sparse_attn_decode<NS=16>"),    # grid padded to 8 queries
+    (16, 1, 640, 16384, 0.0, "sparse_attn_decode<NS=16>"),
+    (3, 1, 1000, 900, 0.3, "sparse_attn_bf16"),            # 63 rows per split exceed the decode kernel
+    (3, 1, 768, 900, 0.3, "sparse_attn_decode<NS=16>"),    # the longest row the decode kernel takes
+    (2, 1, 17, 30, 0.0, "sparse_attn_decode<NS=16>"),      # most splits empty
+    (4, 2, 200, 100, 0.5, "sparse_attn_decode<NS=16>"),    # two queries per sequence
 ])
-def test_sparse_attn_decode_path(B, S, L, nc, inval):
-    """H = 64, D = 512 bf16 with few queries: the two-phase kernel; three calls in a row check
-    that its per-query counters are left ready for the next call."""
+def test_sparse_attn_decode_path(B, S, L, nc, inval, kernel):
+    """H = 64, D = 512 bf16 with few queries: the two-phase kernel where the row fits it (the
+    general split kernel otherwise); three calls in a row check that its per-query counters are
+    left ready for the next call."""
     dsa = _dsa()
     _log(f"decode path B={B} S={S} L={L} nc={nc} invalid={inval}")
     H, D, nw = 64, 512, 128
@@ -461,9 +499,110 @@ def test_sparse_attn_decode_path(B, S, L, nc, inval):
     args = (q.to(DEV), kv_win.to(DEV), kv_comp.to(DEV), sink.to(DEV), torch.from_numpy(idx).to(DEV), scale)
     for call in range(3):
         o = dsa.dsa_sparse_attn(*args)
+        n, names = _launched()
+        assert names.split("+")[0] == kernel, names
         got = o.float().cpu().numpy()
         err = max_abs_err(got, exp)
         _log(f"  call {call}: max abs err {err:.3e}")
         assert np.all(np.isfinite(got))
         assert np.all(got[0, 0] == 0)
         assert err <= ATTN_TOL["bf16"], err
+    assert dsa.dsa_device_errors() == 0
+
+
+# ------------------------------------------------------------------------ KV sources sliced from larger caches
+@pytest.mark.parametrize("B,S,sp,nw,nc,L,fp4,kind", [
+    (4, 1, 4095, 128, 1024, 640, False, "sparse_attn_decode<NS="),  # decode kernel
+    (2, 200, 0, 200, 75, 200, False, "sparse_attn_prefill_h16"),   # one workgroup per query
+    (2, 160, 0, 160, 65, 100, True, "sparse_attn_prefill_h16"),     # fp4 rows and scales sliced
+    (2, 2, 0, 40, 30, 77, False, "sparse_attn_bf16"),              # general kernel (H=16)
+])
+def test_sparse_attn_cache_slices(B, S, sp, nw, nc, L, fp4, kind):
+    """KV sources passed as [:B, :n] slices of larger [max_B, max_n, ...] caches (batch stride
+    larger than n rows) give the oracle's output over the sliced rows."""
+    dsa = _dsa()
+    H = 16 if kind == "sparse_attn_bf16" else 64
+    D = 512
+    _log(f"cache slices B={B} S={S} nw={nw} nc={nc} L={L} fp4={fp4} ({kind})")
+    g = torch.Generator().manual_seed(nw + nc + L)
+    q = torch.randn(B, S, H, D, generator=g).to(torch.bfloat16)
+    win_cache = torch.randn(B + 2, nw + 37, D, generator=g).to(torch.bfloat16)
+    kv_win = win_cache[:B, :nw]
+    sink = torch.randn(H, generator=g)
+    if fp4:
+        packed, scales = dsa_synth.encode_fp4_e2m1_e4m3(torch.randn(B + 1, nc + 19, D, generator=g), 16)
+        comp_rows, comp_sc = packed[:B, :nc], scales[:B, :nc]
+        comp64 = oracle.fp4_rows_decode(comp_rows.contiguous(), comp_sc.contiguous())
+        comp_dev_full, sc_dev_full = packed.to(DEV), scales.to(DEV)
+        comp_dev, sc_dev = comp_dev_full[:B, :nc], sc_dev_full[:B, :nc]
+    else:
+        comp_cache = torch.randn(B + 3, nc + 50, D, generator=g).to(torch.bfloat16)
+        comp_rows = comp_cache[:B, :nc]
+        comp64 = comp_rows.contiguous()
+        comp_dev_full = comp_cache.to(DEV)
+        comp_dev, sc_dev = comp_dev_full[:B, :nc], None
+    win_dev_full = win_cache.to(DEV)
+    win_dev = win_dev_full[:B, :nw]
+    assert win_dev.stride(0) > nw * D and comp_dev.stride(0) > nc * comp_dev.shape[-1]
+    rng = np.random.default_rng(L + nc)
+    idx = _rand_idx(rng, B, S, L, nw + nc)
+    idx[..., -1] = nw + nc - 1  # the last row of the slice
+    idx[..., 0] = nw - 1        # the last window row
+    o = dsa.dsa_sparse_attn(q.to(DEV), win_dev, comp_dev, sink.to(DEV), torch.from_numpy(idx).to(DEV), D ** -0.5,
+                            comp_scales=sc_dev)
+    n, names = _launched()
+    _log(f"  launches: {n} {names}")
+    assert kind in names, names
+    exp = oracle.sparse_attn(q, oracle.kv_concat(kv_win.contiguous(), comp64), sink, idx, D ** -0.5)
+    err = max_abs_err(o.float().cpu().numpy(), exp)
+    _log(f"  max abs err {err:.3e}")
+    assert err <= ATTN_TOL["bf16"], err
+
+
+# ------------------------------------------------------------------------ DSA_DEBUG and non-finite inputs
+def test_debug_index_check_passes_valid_rows():
+    """With the debug index check on, valid index rows (including -1 and the last row) pass and
+    give the same output as without it.  (Rows out of range are refused on the host; that path is
+    tested on the CPU.)"""
+    dsa = _dsa()
+    B, S, H, D, nw, nc, L = 2, 3, 64, 512, 40, 60, 90
+    g = torch.Generator().manual_seed(5)
+    q = torch.randn(B, S, H, D, generator=g).to(torch.bfloat16).to(DEV)
+    kv_win = torch.randn(B, nw, D, generator=g).to(torch.bfloat16).to(DEV)
+    kv_comp = torch.randn(B, nc, D, generator=g).to(torch.bfloat16).to(DEV)
+    sink = torch.randn(H, generator=g).to(DEV)
+    idx = _rand_idx(np.random.default_rng(3), B, S, L, nw + nc)
+    idx[0, 0, 0] = nw + nc - 1
+    idx_d = torch.from_numpy(idx).to(DEV)
+    ref = dsa.dsa_sparse_attn(q, kv_win, kv_comp, sink, idx_d, D ** -0.5)
+    prev = dsa.dsa_set_debug(True)
+    try:
+        got = dsa.dsa_sparse_attn(q, kv_win, kv_comp, sink, idx_d, D ** -0.5)
+    finally:
+        dsa.dsa_set_debug(prev)
+    assert torch.equal(ref, got)
+
+
+@pytest.mark.parametrize("B,S,nw,nc,L", [(4, 1, 128, 500, 640), (1, 300, 300, 75, 200), (2, 2, 40, 30, 77)])
+def test_nan_in_q_propagates(B, S, nw, nc, L):
+    """A NaN in one head's query gives NaN in that head's output, as in the oracle, and leaves every
+    other (query, head) finite and correct; the call returns."""
+    dsa = _dsa()
+    H, D = 64, 512
+    g = torch.Generator().manual_seed(B + S + L)
+    q = torch.randn(B, S, H, D, generator=g).to(torch.bfloat16)
+    q[0, S - 1, 5, 17] = float("nan")
+    kv_win = torch.randn(B, nw, D, generator=g).to(torch.bfloat16)
+    kv_comp = torch.randn(B, nc, D, generator=g).to(torch.bfloat16)
+    sink = torch.randn(H, generator=g)
+    idx = _rand_idx(np.random.default_rng(L), B, S, L, nw + nc, frac_invalid=0.0)
+    o = dsa.dsa_sparse_attn(q.to(DEV), kv_win.to(DEV), kv_comp.to(DEV), sink.to(DEV), torch.from_numpy(idx).to(DEV),
+                            D ** -0.5).float().cpu().numpy()
+    with np.errstate(invalid="ignore"):
+        exp = oracle.sparse_attn(q, oracle.kv_concat(kv_win, kv_comp), sink, idx, D ** -0.5)
+    assert np.all(np.isnan(exp[0, S - 1, 5]))
+    assert np.all(np.isnan(o[0, S - 1, 5]))
+    mask = np.ones(o.shape[:3], dtype=bool)
+    mask[0, S - 1, 5] = False
+    assert np.all(np.isfinite(o[mask]))
+    assert max_abs_err(o[mask], exp[mask]) <= ATTN_TOL["bf16"]
