@@ -58,6 +58,7 @@ extern "C" {
 
 #define DSA_ABI_VERSION 2
 #define DSA_WORKSPACE_HEADER_BYTES 4096
+#define DSA_NOALLOC_SCRATCH_BYTES (32u << 20) /* scratch of dsa_sparse_attn_step_noalloc */
 
 typedef struct ihipStream_t* dsa_stream_t; /* a hipStream_t */
 
@@ -315,6 +316,30 @@ int dsa_sparse_attn_step(const void* q_idx, const void* k_idx, int64_t k_batch_s
                          const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink, float scale, void* o,
                          int dtype, int B, int S, int H, int D, float* scores, int32_t* idx, void* workspace,
                          size_t workspace_bytes, dsa_stream_t stream);
+
+/*
+ * The whole step without a workspace argument, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).  Same
+ * arguments, results and launches as dsa_sparse_attn_step, minus workspace and workspace_bytes: the
+ * scratch is a fixed array of DSA_NOALLOC_SCRATCH_BYTES (32 MiB) per device that the library
+ * holds until the process ends.  The call allocates nothing.
+ *
+ *  - dsa_init(device) must have run on the current device (DSA_ERR_STATE otherwise); it looks up
+ *    the array's device address.
+ *  - Shapes whose dsa_sparse_attn_workspace_size exceeds the array are refused with
+ *    DSA_ERR_WORKSPACE before anything is launched (decode batches of up to 32 queries with
+ *    H = 64, D = 512 and L <= 768 fit; prefill batches of 256 or more queries at D = 512 need no
+ *    scratch).
+ *  - Every call on a device shares that device's array, which keeps the last call's contents: the
+ *    rendezvous counters at its start are zero when the library loads and every call leaves them
+ *    zero.  Calls that can run at the same time on one device (other streams, concurrently
+ *    replayed graphs) race on the array and must not overlap.
+ */
+int dsa_sparse_attn_step_noalloc(const void* q_idx, const void* k_idx, int64_t k_batch_stride, const void* w,
+                                 float w_scale, int H_I, int D_I, int T, int index_topk, int start_pos, int ratio,
+                                 int W, const void* q, const dsa_kv_src* win, const dsa_kv_src* comp,
+                                 const float* sink, float scale, void* o, int dtype, int B, int S, int H, int D,
+                                 float* scores, int32_t* idx, dsa_stream_t stream);
 
 #ifdef __cplusplus
 }

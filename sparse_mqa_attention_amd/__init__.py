@@ -94,6 +94,10 @@ def _load():
                                          ctypes.POINTER(DsaKvSrc), ctypes.POINTER(DsaKvSrc), vp, f32, vp, i32, i32,
                                          i32, i32, i32, vp, vp, vp, ctypes.c_size_t, vp]
     lib.dsa_sparse_attn_step.restype = i32
+    lib.dsa_sparse_attn_step_noalloc.argtypes = [vp, vp, i64, vp, f32, i32, i32, i32, i32, i32, i32, i32, vp,
+                                                 ctypes.POINTER(DsaKvSrc), ctypes.POINTER(DsaKvSrc), vp, f32, vp,
+                                                 i32, i32, i32, i32, i32, vp, vp, vp]
+    lib.dsa_sparse_attn_step_noalloc.restype = i32
     lib.dsa_sparse_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.dsa_sparse_attn_workspace_size.restype = ctypes.c_size_t
     return lib
@@ -438,6 +442,33 @@ def dsa_sparse_attn_step(q_idx, k_idx, w, q, kv_win, kv_comp, sink, *, index_top
     return out, idx, scores
 
 
+def dsa_sparse_attn_step_noalloc(q_idx, k_idx, w, q, kv_win, kv_comp, sink, *, index_topk: int, start_pos: int,
+                                 ratio: int, W: int, scale: float, w_scale: float, out, scores, idx,
+                                 comp_scales=None, stream=None):
+    """dsa_sparse_attn_step without a workspace: the library's fixed per-device scratch array is
+    used (see include/dsa.h).  The caller passes every output (o, scores [B,S,T] float32, idx
+    [B,S,L] int32); nothing is allocated here either."""
+    _need_contig("q_idx", q_idx)
+    _need_contig("w", w)
+    B, S, H, D, dt, win, comp, out = _attn_operands(q, kv_win, kv_comp, sink, comp_scales, out)
+    H_I, D_I = q_idx.shape[2], q_idx.shape[3]
+    T = k_idx.shape[1]
+    kbs, krs = _batched_rows("k_idx", k_idx)
+    if krs != D_I:
+        raise DsaError(-2, "k_idx rows must be dense")
+    _expect("k_idx", k_idx, (B, T, D_I), q_idx.dtype)
+    _expect("w", w, (B, S, H_I), q_idx.dtype)
+    _expect("scores", scores, (B, S, T), torch.float32)
+    L = dsa_window_cols(S, start_pos, W) + min(int(index_topk), T)
+    _expect("idx", idx, (B, S, L), torch.int32)
+    dev = _dev(q_idx, k_idx, w, q, kv_win, kv_comp, sink, out, scores, idx)
+    _check(lib.dsa_sparse_attn_step_noalloc(_ptr(q_idx), _ptr(k_idx), kbs, _ptr(w), float(w_scale), H_I, D_I, T,
+                                            int(index_topk), int(start_pos), int(ratio), int(W), _ptr(q),
+                                            ctypes.byref(win), ctypes.byref(comp), _ptr(sink), float(scale),
+                                            _ptr(out), dt, B, S, H, D, _ptr(scores), _ptr(idx), _stream(dev, stream)))
+    return out, idx, scores
+
+
 def sparse_attention_step(q, kv_win, kv_comp, qI, kI, w, sink, *, start_pos: int, ratio: int, W: int,
                           index_topk: int, scale: float, w_scale: float, comp_scales=None, bufs=None,
                           stream=None):
@@ -481,6 +512,7 @@ __all__ = [
     "dsa_sparse_attn",
     "dsa_sparse_attn_select",
     "dsa_sparse_attn_step",
+    "dsa_sparse_attn_step_noalloc",
     "dsa_sparse_attn_workspace_size",
     "kv_src",
     "sparse_attention_step",

@@ -56,11 +56,8 @@ static DeviceState g_dev[kMaxDevices];
 static std::mutex g_dev_mu;
 static int g_debug = -1;  // -1: not read from DSA_DEBUG yet
 
-int scratch_device_init(int dev, DeviceState& ds) {
-  (void)dev;
-  ds.scratch = nullptr;
-  return DSA_OK;
-}
+int scratch_device_init(int dev, DeviceState& ds);
+size_t scratch_bytes();
 
 static bool debug_on() {
   if (g_debug < 0) {
@@ -425,6 +422,35 @@ int dsa_sparse_attn_step(const void* q_idx, const void* k_idx, int64_t k_batch_s
   if (rc) return rc;
   return dsa_sparse_attn_select(scores, T, index_topk, start_pos, ratio, W, q, win, comp, sink, scale, o, dtype, B, S,
                                 H, D, idx, workspace, workspace_bytes, stream);
+}
+
+int dsa_sparse_attn_step_noalloc(const void* q_idx, const void* k_idx, int64_t k_batch_stride, const void* w,
+                                 float w_scale, int H_I, int D_I, int T, int index_topk, int start_pos, int ratio,
+                                 int W, const void* q, const dsa_kv_src* win, const dsa_kv_src* comp,
+                                 const float* sink, float scale, void* o, int dtype, int B, int S, int H, int D,
+                                 float* scores, int32_t* idx, dsa_stream_t stream) {
+  dsa::Entry entry_;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= dsa::kMaxDevices)
+    return fail(DSA_ERR_HIP, "dsa_sparse_attn_step_noalloc: no usable current HIP device");
+  const dsa::DeviceState& ds = dsa::g_dev[dev];
+  if (!ds.ready || !ds.scratch)
+    return fail(DSA_ERR_STATE, "dsa_sparse_attn_step_noalloc: call dsa_init(%d) first", dev);
+  if (B < 0 || S < 0 || T < 0 || index_topk < 0 || start_pos < 0 || W <= 0)
+    return fail(DSA_ERR_SHAPE, "dsa_sparse_attn_step_noalloc: bad sizes B=%d S=%d T=%d index_topk=%d", B, S, T,
+                index_topk);
+  const int Wc = dsa_window_cols(S, start_pos, W);
+  if (Wc < 0) return Wc;
+  const int K = index_topk < T ? index_topk : T;
+  const size_t need = dsa_sparse_attn_workspace_size(dtype, B, S, H, D, Wc + K);
+  const size_t have = dsa::scratch_bytes();
+  if (need > have)
+    return fail(DSA_ERR_WORKSPACE,
+                "dsa_sparse_attn_step_noalloc: this shape needs %zu bytes of scratch, the fixed array holds %zu "
+                "(use dsa_sparse_attn_step with a workspace)",
+                need, have);
+  return dsa_sparse_attn_step(q_idx, k_idx, k_batch_stride, w, w_scale, H_I, D_I, T, index_topk, start_pos, ratio, W,
+                              q, win, comp, sink, scale, o, dtype, B, S, H, D, scores, idx, ds.scratch, have, stream);
 }
 
 }  // extern "C"
