@@ -2,14 +2,25 @@
 
 A step is one pass of the whole path over one batch of synthetic input through
 dsa_sparse_attn_step: index scores, index rows (window rows and top-k selection) and sparse
-attention.  For decode batches that is one kernel; otherwise the index scores, the index rows and
-the attention are three launches (every stage a libdsa kernel).  Inputs are resident in HBM before
-timing starts; several input sets are rotated so that the 256 MB Infinity Cache cannot serve one
-step from the previous one.
+attention.  For decode batches the library runs that as one kernel; otherwise it is three launches
+(index scores, index rows, attention), every one a libdsa kernel.  Which kernels ran is read back
+from the library (dsa_last_launches), not assumed.  Inputs are resident in HBM before timing
+starts; several input sets are rotated so that the 256 MB Infinity Cache cannot serve one step
+from the previous one.
 
-Prints one JSON line (see `--help`).  The roofline object covers the dominant kernel (the decode
-kernel that scores, selects and attends, or the sparse attention kernel), timed with HIP events on
-the stream it runs on; the CPU baseline is the oracle timed on a bounded sample on the host.
+Default run: every bf16 workload (decode_b32_ctx8k, prefill_s8k, decode_b16_ctx64k,
+prefill_s32k_fp4) in one process, then ONE JSON line whose headline (value, config, roofline,
+cpu_baseline) is the largest, prefill_s32k_fp4, and whose "workloads" object carries each
+workload's step time, kernels and roofline.  The roofline covers each workload's dominant kernel
+(the one-launch decode step, or the sparse attention kernel): `achieved` is its algorithmic work
+per launch over its average duration in a graph of 100 back-to-back launches, timed with HIP events
+on the stream it runs on; `median_launch_us` is the median of 100 launches timed one by one.  The
+CPU baseline is the oracle, timed on a bounded sample of the headline workload on the host.
+
+Calibration modes (each prints one JSON line and exits):
+  --copy-calibration MIB   a plain device copy of MIB MiB, three times (scale of the HBM byte counters)
+  --calibrate              attainable figures on this GPU: streaming copy bandwidth, a large bf16
+                           GEMM (hipBLASLt through torch) and the per-launch floor of a tiny kernel
 """
 from __future__ import annotations
 
@@ -18,6 +29,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -28,6 +40,9 @@ METRIC = "sparse-attn query-tokens/s (decode & prefill) at 1 GPU; % HBM / MFMA p
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 ROTATE_BYTES = 768 << 20  # rotate input sets until they span more than the Infinity Cache (256 MB)
+HEADLINE = "prefill_s32k_fp4"  # the largest workload
+LINE_WORKLOADS = ["decode_b32_ctx8k", "prefill_s8k", "decode_b16_ctx64k", "prefill_s32k_fp4"]
+HOST_CORES = 16  # the CPU share of one GPU on the benchmark machines
 # the sources each dominant kernel is compiled from: a change to any of them drops the HBM traffic
 # figure taken on the old sources
 KERNEL_SOURCES = {
@@ -39,18 +54,21 @@ KERNEL_SOURCES = {
 
 
 def _args():
-    p = argparse.ArgumentParser(description=__doc__)
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--steps", type=int, default=100, help="timed steps per workload")
     p.add_argument("--warmup", type=int, default=10)
-    p.add_argument("--workload", default="decode_b32_ctx8k")
+    p.add_argument("--workload", default="all", help="one workload name, or 'all' (the default line)")
+    p.add_argument("--launches", type=int, default=100, help="dominant-kernel launches timed for avg and median")
     p.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing (profiling runs)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device copy of MIB MiB three times (scale of the HBM byte counters)")
+    p.add_argument("--calibrate", action="store_true", help="only measure attainable copy, GEMM and launch figures")
     return p.parse_args()
 
 
+# ---------------------------------------------------------------------------- calibration modes
 def copy_calibration(mib: int):
     """A plain device-to-device copy of known size, three times: reads and writes mib MiB each."""
     import torch
@@ -65,6 +83,63 @@ def copy_calibration(mib: int):
     print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
 
 
+def _graph_time_ms(fn, reps: int, inner: int):
+    """Average ms of fn() over `inner` calls captured in one graph, replayed `reps` times."""
+    import torch
+
+    stream = torch.cuda.current_stream()
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(inner):
+            fn()
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / (reps * inner)
+
+
+def calibrate():
+    """Attainable figures on this GPU, each timed with HIP events over graphs of back-to-back calls."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    out = {"calibration": "MI355X attainable figures"}
+    # streaming copy: 2 GiB read + 2 GiB written per call
+    n = 2 << 30
+    x = torch.ones(n, dtype=torch.uint8, device=dev)
+    y = torch.empty_like(x)
+    ms = _graph_time_ms(lambda: y.copy_(x), reps=5, inner=4)
+    out["copy_bytes_per_call"] = 2 * n
+    out["copy_gbs"] = round(2 * n / (ms * 1e-3) / 1e9, 1)
+    del x, y
+    # dense bf16 GEMM 8192 x 8192 x 8192 through torch (hipBLASLt)
+    m = 8192
+    a = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(m, m, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(m, m, device=dev, dtype=torch.bfloat16)
+    ms = _graph_time_ms(lambda: torch.matmul(a, b, out=c), reps=5, inner=4)
+    out["gemm_shape"] = [m, m, m]
+    out["gemm_bf16_tflops"] = round(2.0 * m ** 3 / (ms * 1e-3) / 1e12, 1)
+    del a, b, c
+    # launch floor: a one-workgroup fill kernel, 100 back to back in a graph
+    z = torch.empty(64, device=dev)
+    out["tiny_kernel_us_back_to_back"] = round(_graph_time_ms(lambda: z.fill_(1.0), reps=5, inner=100) * 1e3, 3)
+    # a 256-workgroup fill (256 x 1 KiB)
+    z2 = torch.empty(256 * 256, device=dev)
+    out["fill_256_workgroups_us_back_to_back"] = round(
+        _graph_time_ms(lambda: z2.fill_(1.0), reps=5, inner=100) * 1e3, 3)
+    out["peaks_used"] = {"hbm_gbs": PEAK_HBM_GBS, "bf16_tflops": PEAK_BF16_TFLOPS}
+    print(json.dumps(out), flush=True)
+
+
+# ---------------------------------------------------------------------------- traffic records
 def kernel_src_sha(mode: str) -> str:
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[mode]:
@@ -122,7 +197,9 @@ def cpu_baseline(w, cpu_in, target_s: float):
 
     import oracle
 
-    cores = max(1, min(16, os.cpu_count() or 1))
+    # every host core the machine gives one GPU: the benchmark machines grant 16 per GPU whatever
+    # os.cpu_count() reports, so the pool never exceeds that
+    cores = max(1, min(HOST_CORES, os.cpu_count() or 1))
     comp = (oracle.fp4_rows_decode(cpu_in["kv_comp_fp4"], cpu_in["kv_comp_scale"]) if w.comp_fmt == "fp4"
             else cpu_in["kv_comp"])
     f64 = lambda x: x.float().numpy().astype(np.float64)  # noqa: E731
@@ -136,7 +213,7 @@ def cpu_baseline(w, cpu_in, target_s: float):
     t0 = time.perf_counter()
     with mp.get_context("fork").Pool(cores, initializer=_pool_init) as pool:
         i = 0
-        while time.perf_counter() - t0 < target_s and done < 64 * len(order):
+        while time.perf_counter() - t0 < target_s and done < len(order):
             batch = [order[(i + k) % len(order)] for k in range(2 * cores)]
             i += len(batch)
             pool.map(_oracle_query, batch, chunksize=1)
@@ -144,29 +221,28 @@ def cpu_baseline(w, cpu_in, target_s: float):
     el = time.perf_counter() - t0
     _ORACLE_JOB.clear()
     return {"value": round(done / el, 2), "unit": "query-tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{done} queries of {w.name} in random order, each the oracle's scores + top-k + window row "
-                      f"+ attention in float64 NumPy, {cores} worker processes x 1 BLAS thread, {el:.1f} s wall"}
+            "sample": f"{done} distinct queries of {w.name} drawn at random, each the oracle's scores + top-k + "
+                      f"window row + attention in float64 NumPy, {cores} worker processes x 1 BLAS thread "
+                      f"(the host-core share of one GPU), {el:.1f} s wall"}
 
 
-# ---------------------------------------------------------------------------- GPU run
-def main():
-    a = _args()
-    if a.copy_calibration:
-        copy_calibration(a.copy_calibration)
-        return
-    if a.gpus != 1:
-        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}); the path shards by batch/query "
-              "without collectives and is measured at one GPU's share", file=sys.stderr)
-        sys.exit(2)
-    import numpy as np
+# ---------------------------------------------------------------------------- one workload
+def visible_pairs(w) -> int:
+    """Visible (query, compressed row) pairs of the step: sum over queries of min(T, c(t))."""
+    tot = 0
+    for t in range(w.S):
+        tot += min(w.T, (w.start_pos + t + 1) // w.ratio)
+    return w.B * tot
+
+
+def run_workload(w, a, log):
+    """Times one workload's step and dominant kernel; returns (entry dict, set 0 inputs)."""
     import torch
 
     import dsa_synth
     import sparse_mqa_attention_amd as dsa
 
-    w = dsa_synth.get(a.workload)
     dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
     set0 = dsa_synth.generate(w, seed=0, device=dev)
     set_bytes = sum(dsa_synth.nbytes(t) for t in set0.values())
     n_sets = max(1, min(8, math.ceil(ROTATE_BYTES / set_bytes)))
@@ -174,9 +250,10 @@ def main():
     scale = w.D ** -0.5
     w_scale = w.D_I ** -0.5 * w.H_I ** -0.5
     Wc = dsa.dsa_window_cols(w.S, w.start_pos, w.W)
+    dcode = 1 if w.dtype == "bf16" else 0
     bufs = []
     for s in sets:
-        ws = dsa.dsa_sparse_attn_workspace_size(1 if w.dtype == "bf16" else 0, w.B, w.S, w.H, w.D, w.L)
+        ws = dsa.dsa_sparse_attn_workspace_size(dcode, w.B, w.S, w.H, w.D, w.L)
         bufs.append({"idx": torch.empty(w.B, w.S, Wc + w.K, dtype=torch.int32, device=dev),
                      "scores": torch.empty(w.B, w.S, w.T, dtype=torch.float32, device=dev),
                      "o": torch.empty_like(s["q"]),
@@ -184,46 +261,29 @@ def main():
     stream = torch.cuda.current_stream(dev)
     comp_key = "kv_comp_fp4" if w.comp_fmt == "fp4" else "kv_comp"
 
-    # Decode batches the two-phase decode kernel takes score, select and attend inside it (one
-    # launch for the whole step); elsewhere the step is index scores, index rows and attention.
-    fused = (w.mode == "decode" and w.dtype == "bf16" and w.comp_fmt != "fp4" and w.T <= 2048 and w.D == 512
-             and w.H == 64 and w.B * w.S < 256 and w.D_I == 128 and w.H_I <= 64)
-
-    def stage_step(i):
+    def step(i):
         s, bf = sets[i % n_sets], bufs[i % n_sets]
         dsa.dsa_sparse_attn_step(s["qI"], s["kI"], s["w"], s["q"], s["kv_win"], s[comp_key], s["sink"],
                                  index_topk=w.index_topk, start_pos=w.start_pos, ratio=w.ratio, W=w.W, scale=scale,
                                  w_scale=w_scale, comp_scales=s.get("kv_comp_scale"), out=bf["o"],
                                  scores=bf["scores"], idx=bf["idx"], workspace=bf["workspace"])
 
-    def stage_index(i):
-        s, bf = sets[i % n_sets], bufs[i % n_sets]
-        dsa.dsa_index_scores(s["qI"], s["kI"], s["w"], w_scale, w.start_pos, w.ratio, out=bf["scores"])
-
-    def stage_select(i):
-        s, bf = sets[i % n_sets], bufs[i % n_sets]
-        dsa.dsa_select(bf["scores"], w.index_topk, w.start_pos, w.ratio, w.W, w.n_win, out=bf["idx"])
-
-    def stage_attn(i):
+    def attn(i):
         s, bf = sets[i % n_sets], bufs[i % n_sets]
         dsa.dsa_sparse_attn(s["q"], s["kv_win"], s[comp_key], s["sink"], bf["idx"], scale,
                             comp_scales=s.get("kv_comp_scale"), out=bf["o"], workspace=bf["workspace"])
 
-    step = stage_step
+    def rest(i):
+        s, bf = sets[i % n_sets], bufs[i % n_sets]
+        dsa.dsa_index_scores(s["qI"], s["kI"], s["w"], w_scale, w.start_pos, w.ratio, out=bf["scores"])
+        dsa.dsa_select(bf["scores"], w.index_topk, w.start_pos, w.ratio, w.W, w.n_win, out=bf["idx"])
 
-    # the dominant kernel and the rest of the step, timed apart
-    if fused:
-        dominant, rest = stage_step, None
-    else:
-        dominant = stage_attn
-
-        def rest(i):
-            stage_index(i)
-            stage_select(i)
-
-    # Steps are captured into HIP graphs of G consecutive steps (rotating input sets), so the
-    # timed region measures the GPU, not the host's launch rate.
-    G = max(1, min(a.steps, 10))
+    # eager warmup (initialises every set) and the library's own record of what a step launches
+    for i in range(max(n_sets, min(a.warmup, 2 * n_sets))):
+        step(i)
+    n_launch, names = dsa.dsa_last_launches()
+    torch.cuda.synchronize()
+    fused = n_launch == 1  # the whole step in one kernel (read back from the library)
 
     def capture(fn, first, count):
         g = torch.cuda.CUDAGraph()
@@ -232,18 +292,15 @@ def main():
                 fn(first + k)
         return g
 
-    for i in range(min(a.warmup, n_sets)):  # eager warmup: compile-free, initialises every set
-        step(i)
-    torch.cuda.synchronize()
+    # K steps: graphs of G consecutive steps (rotating input sets), bracketed by HIP events
+    G = max(1, min(a.steps, 10))
     full = capture(step, 0, G)
     rem = a.steps % G
     tail = capture(step, 0, rem) if rem else None
     for _ in range(max(1, a.warmup // G)):
         full.replay()
     torch.cuda.synchronize()
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     w0 = time.perf_counter()
     t_start.record(stream)
     for _ in range(a.steps // G):
@@ -253,97 +310,166 @@ def main():
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    gpu_ms = t_start.elapsed_time(t_end)
-    ms_per_step = gpu_ms / a.steps
+    ms_per_step = t_start.elapsed_time(t_end) / a.steps
+    del full, tail
 
-    # the dominant kernel alone: R launches back to back in one graph, bracketed by HIP events
-    R = 20
-    attn_graph = capture(dominant, 0, R)
-    sel_graph = capture(rest, 0, R) if rest is not None else None
-    attn_graph.replay()
+    # the dominant kernel: R launches back to back in one graph (average), and R launches timed one
+    # by one (median), each on the launch stream
+    dominant = step if fused else attn
+    dominant(0)
+    dom_names = dsa.dsa_last_launches()[1]
+    R = a.launches
+    g_avg = capture(dominant, 0, R)
+    g_avg.replay()
     torch.cuda.synchronize()
-    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record(stream)
-    attn_graph.replay()
+    g_avg.replay()
     e1.record(stream)
-    if sel_graph is not None:
-        sel_graph.replay()
-    e2.record(stream)
     torch.cuda.synchronize()
-    attn_avg_ms = e0.elapsed_time(e1) / R
-    sel_avg_ms = e1.elapsed_time(e2) / R
-    if fused:
-        parts = f"index scores+window+top-k+attention (one kernel) {attn_avg_ms * 1e3:.2f} us"
-    else:
-        parts = f"attention {attn_avg_ms * 1e3:.2f} us, window+index+top-k {sel_avg_ms * 1e3:.2f} us"
-    print(f"[bench] {w.name}: step {ms_per_step * 1e3:.2f} us (wall {wall / a.steps * 1e6:.2f} us), {parts}",
-          file=sys.stderr)
+    avg_ms = e0.elapsed_time(e1) / R
+    del g_avg
+    singles = [capture(dominant, i, 1) for i in range(n_sets)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(R + 1)]
+    for i in range(R):
+        evs[i].record(stream)
+        singles[i % n_sets].replay()
+    evs[R].record(stream)
+    torch.cuda.synchronize()
+    med_ms = statistics.median(evs[i].elapsed_time(evs[i + 1]) for i in range(R))
+    del singles
+    rest_ms = None
+    if not fused:
+        rest_ms = _graph_time_ms(lambda: rest(0), reps=2, inner=20)
 
-    # algorithmic work of one sparse-attention launch: every valid slot's row once, q, o, idx, sink
+    # algorithmic work of one attention pass: every valid slot's row once, q, o, idx, sink
     idx_all = torch.stack([bufs[i % n_sets]["idx"] for i in range(n_sets)])
-    valid_per_set = (idx_all >= 0).view(n_sets, -1).sum(dim=1).double().mean().item()
+    valid = (idx_all >= 0).view(n_sets, -1).sum(dim=1).double().mean().item()
     esz = 2 if w.dtype == "bf16" else 4
     q_bytes = w.B * w.S * w.H * w.D * esz
     if w.comp_fmt == "fp4":
         # valid window rows are bf16 rows; compressed rows are D/2 nibble bytes + D/16 scale bytes
         win_valid = (idx_all[..., :Wc] >= 0).view(n_sets, -1).sum(dim=1).double().mean().item()
-        comp_valid = valid_per_set - win_valid
-        row_bytes = win_valid * w.D * esz + comp_valid * (w.D // 2 + w.D // 16)
+        row_bytes = win_valid * w.D * esz + (valid - win_valid) * (w.D // 2 + w.D // 16)
     else:
-        row_bytes = valid_per_set * w.D * esz
-    alg_bytes = 2 * q_bytes + w.B * w.S * w.L * 4 + w.H * 4 + row_bytes
-    if fused:
-        # the kernel also reads the index keys, index queries and head weights, and writes each
-        # query's scores and reads them back once
-        alg_bytes += (w.B * w.T * w.D_I * 2 + w.B * w.S * w.H_I * (w.D_I + 1) * 2 + 2 * w.B * w.S * w.T * 4)
-    alg_flops = 4.0 * w.H * w.D * valid_per_set
-    if w.mode == "decode":
-        achieved = alg_bytes / (attn_avg_ms * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4)}
-        per_launch = alg_bytes
+        row_bytes = valid * w.D * esz
+    attn_bytes = 2 * q_bytes + w.B * w.S * w.L * 4 + w.H * 4 + row_bytes
+    # the index part: keys once per batch, index queries and head weights, scores written and read once
+    index_bytes = (w.B * w.T * w.D_I * esz + w.B * w.S * w.H_I * (w.D_I + 1) * esz + 2 * w.B * w.S * w.T * 4)
+    attn_flops = 4.0 * w.H * w.D * valid
+    index_flops = 2.0 * w.H_I * w.D_I * visible_pairs(w)
+    decode = w.mode == "decode"
+    if decode:
+        per_launch = attn_bytes + (index_bytes if fused else 0)
+        ach = per_launch / (avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4)}
+        step_ach = (attn_bytes + index_bytes) / (ms_per_step * 1e-3) / 1e9
+        step_roof = {"bound": "hbm", "achieved": round(step_ach, 1), "unit": "GB/s",
+                     "frac": round(step_ach / PEAK_HBM_GBS, 4), "algorithmic": attn_bytes + index_bytes}
     else:
-        achieved = alg_flops / (attn_avg_ms * 1e-3) / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4)}
-        per_launch = alg_flops
-    sha = kernel_src_sha(w.mode)
+        per_launch = attn_flops
+        ach = per_launch / (avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+        step_ach = (attn_flops + index_flops) / (ms_per_step * 1e-3) / 1e12
+        step_roof = {"bound": "mfma", "achieved": round(step_ach, 1), "unit": "TFLOP/s",
+                     "frac": round(step_ach / PEAK_BF16_TFLOPS, 4), "algorithmic": attn_flops + index_flops}
+    sha = kernel_src_sha("decode" if decode else "prefill")
     roof["traffic"] = _traffic(w.name, sha)
-    if fused:
-        roof["kernel"] = ("dsa_sparse_attn_step (index scores + index rows + gather-attention + split combine, "
-                          "one kernel)")
-    else:
-        roof["kernel"] = "dsa_sparse_attn" + (" (gather-attention + split combine)" if
-                                              dsa.dsa_sparse_attn_workspace_size(1, w.B, w.S, w.H, w.D, w.L) else "")
-    roof["avg_launch_us"] = round(attn_avg_ms * 1e3, 2)
+    roof["kernel"] = dom_names
+    roof["avg_launch_us"] = round(avg_ms * 1e3, 2)
+    roof["median_launch_us"] = round(med_ms * 1e3, 2)
+    roof["launches_timed"] = R
     roof["algorithmic_per_launch"] = per_launch
+    entry = {
+        "ms_per_step": round(ms_per_step, 5),
+        "query_tokens_per_s": round(w.B * w.S / (ms_per_step * 1e-3), 1),
+        "launches_per_step": n_launch,
+        "kernels": names,
+        "roofline": roof,
+        "step_roofline": step_roof,
+        "rest_of_step_us": None if rest_ms is None else round(rest_ms * 1e3, 2),
+        "config": {"workload": w.name, "mode": w.mode, "batch": w.B, "query_tokens": w.S, "context": w.end_pos,
+                   "heads": w.H, "head_dim": w.D, "window": w.W, "compress_ratio": w.ratio, "index_heads": w.H_I,
+                   "index_head_dim": w.D_I, "index_topk": w.index_topk,
+                   "compressed_kv": "fp4 e2m1 + E4M3/16" if w.comp_fmt == "fp4" else w.dtype,
+                   "input_sets_rotated": n_sets, "kernel_src_sha": sha},
+    }
+    log(f"[bench] {w.name}: step {ms_per_step * 1e3:.2f} us (wall {wall / a.steps * 1e6:.2f} us), {n_launch} "
+        f"launch(es) {names}; dominant {dom_names}: avg {avg_ms * 1e3:.2f} us, median {med_ms * 1e3:.2f} us, "
+        f"{roof['achieved']} {roof['unit']} = {roof['frac'] * 100:.1f}% of peak"
+        + ("" if rest_ms is None else f"; index+select {rest_ms * 1e3:.2f} us"))
+    for bf in bufs:
+        bf.clear()
+    keep = set0
+    del sets, bufs
+    return entry, keep
 
+
+# ---------------------------------------------------------------------------- main
+def main():
+    a = _args()
+    if a.copy_calibration:
+        copy_calibration(a.copy_calibration)
+        return
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {a.gpus}); the path shards by batch/query "
+              "without collectives and is measured at one GPU's share", file=sys.stderr)
+        sys.exit(2)
+    if a.calibrate:
+        calibrate()
+        return
+    import torch
+
+    import dsa_synth
+    import sparse_mqa_attention_amd as dsa
+
+    def log(msg):
+        print(msg, file=sys.stderr, flush=True)
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dsa.dsa_init(dev)
+    names = LINE_WORKLOADS if a.workload == "all" else [a.workload]
+    headline = HEADLINE if a.workload == "all" else a.workload
+    entries = {}
+    head_set = None
+    for name in names:
+        w = dsa_synth.get(name)
+        entry, set0 = run_workload(w, a, log)
+        entries[name] = entry
+        if name == headline:
+            head_set = {k: v.cpu() for k, v in set0.items()} if not a.no_cpu_baseline else None
+        del set0
+        torch.cuda.empty_cache()
+    errs = dsa.dsa_device_errors(dev)
+    if errs:
+        log(f"[bench] device error flags {errs:#x}: a decode rendezvous timed out")
+    hw = dsa_synth.get(headline)
+    h = entries[headline]
     cpu = None
-    if not a.no_cpu_baseline:
-        cpu_in = {k: v.cpu() for k, v in set0.items()}
-        cpu = cpu_baseline(w, cpu_in, a.cpu_seconds)
-
-    queries = w.B * w.S
+    if head_set is not None:
+        log(f"[bench] CPU oracle baseline on {headline} ({a.cpu_seconds:.0f} s sample)")
+        cpu = cpu_baseline(hw, head_set, a.cpu_seconds)
     line = {
         "metric": METRIC,
-        "value": round(queries / (ms_per_step * 1e-3), 1),
+        "value": h["query_tokens_per_s"],
         "unit": "query-tokens/s",
         "n_gpus": 1,
         "steps": a.steps,
         "warmup": a.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": h["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "dtype": "bf16" if hw.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": w.name, "mode": w.mode, "batch": w.B, "query_tokens": w.S,
-                   "context": w.end_pos, "heads": w.H, "head_dim": w.D, "window": w.W, "compress_ratio": w.ratio,
-                   "index_heads": w.H_I, "index_head_dim": w.D_I, "index_topk": w.index_topk,
-                   "compressed_kv": "fp4 e2m1 + E4M3/16" if w.comp_fmt == "fp4" else w.dtype,
-                   "input_sets_rotated": n_sets, "kernel_src_sha": sha},
-        "roofline": roof,
+        "config": h["config"],
+        "roofline": h["roofline"],
         "cpu_baseline": cpu,
+        "device_error_flags": errs,
+        "workloads": {k: {kk: vv for kk, vv in v.items() if kk != "config"} for k, v in entries.items()},
     }
     print(json.dumps(line), flush=True)
 
