@@ -9,9 +9,11 @@ starts; several input sets are rotated so that the 256 MB Infinity Cache cannot 
 from the previous one.
 
 Default run: every bf16 workload (decode_b32_ctx8k, prefill_s8k, decode_b16_ctx64k,
-prefill_s32k_fp4) in one process, then ONE JSON line whose headline (value, config, roofline,
-cpu_baseline) is the largest, prefill_s32k_fp4, and whose "workloads" object carries each
-workload's step time, kernels and roofline.  The roofline covers each workload's dominant kernel
+prefill_s32k_fp4, and the page config's ratios 2 and 1 at 64K-context decode and 8K prefill) in one
+process, then ONE JSON line whose headline (value, config, roofline, cpu_baseline) is the largest,
+prefill_s32k_fp4, and whose "workloads" object carries each workload's step time, kernels and
+roofline.  Some workloads are also timed as a layer group: one step on the index source layer
+plus the attention of the layers that reuse its index rows.  The roofline covers each workload's dominant kernel
 (the one-launch decode step, or the sparse attention kernel): `achieved` is its algorithmic work
 per launch over its average duration in a graph of 100 back-to-back launches, timed with HIP events
 on the stream it runs on; `median_launch_us` is the median of 100 launches timed one by one.  The
@@ -41,7 +43,13 @@ PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
 ROTATE_BYTES = 768 << 20  # rotate input sets until they span more than the Infinity Cache (256 MB)
 HEADLINE = "prefill_s32k_fp4"  # the largest workload
-LINE_WORKLOADS = ["decode_b32_ctx8k", "prefill_s8k", "decode_b16_ctx64k", "prefill_s32k_fp4"]
+LINE_WORKLOADS = ["decode_b32_ctx8k", "prefill_s8k", "decode_b16_ctx64k", "prefill_s32k_fp4",
+                  "decode_b16_ctx64k_r2", "decode_b16_ctx64k_r1", "prefill_s8k_r2", "prefill_s8k_r1"]
+# workloads also timed as a layer group: one index source layer and the layers that reuse its index
+# rows (the page's index sources sit every 4 layers from layer 20 on, all reading layer 20's
+# compressed KV), each layer with its own queries, window KV and sinks
+GROUP_LAYERS = 4
+GROUP_WORKLOADS = ["decode_b32_ctx8k", "decode_b16_ctx64k_r2", "decode_b16_ctx64k_r1", "prefill_s8k_r1"]
 HOST_CORES = 16  # the CPU share of one GPU on the benchmark machines
 # the sources each dominant kernel is compiled from: a change to any of them drops the HBM traffic
 # figure taken on the old sources
@@ -342,6 +350,43 @@ def run_workload(w, a, log):
     if not fused:
         rest_ms = _graph_time_ms(lambda: rest(0), reps=2, inner=20)
 
+    # a layer group: the step on the index source layer, then the attention of the layers that reuse
+    # its index rows (own queries, window KV and sinks; the shared compressed KV)
+    group = None
+    if w.name in GROUP_WORKLOADS:
+        layers = []
+        for li in range(1, GROUP_LAYERS):
+            g = dsa_synth.generate(w, seed=1000 + li, device=dev)
+            layers.append({"q": g["q"], "kv_win": g["kv_win"], "sink": g["sink"], "o": torch.empty_like(g["q"])})
+            del g
+        torch.cuda.empty_cache()
+
+        def layer_group(i):
+            step(i)
+            s, bf = sets[i % n_sets], bufs[i % n_sets]
+            for ly in layers:
+                dsa.dsa_sparse_attn(ly["q"], ly["kv_win"], s[comp_key], ly["sink"], bf["idx"], scale,
+                                    comp_scales=s.get("kv_comp_scale"), out=ly["o"], workspace=bf["workspace"])
+
+        layer_group(0)
+        group_launches = dsa.dsa_last_launches()
+        torch.cuda.synchronize()
+        gg = capture(layer_group, 0, max(1, min(10, 2 * n_sets)))
+        gg.replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        reps = 3
+        for _ in range(reps):
+            gg.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        group_ms = e0.elapsed_time(e1) / (reps * max(1, min(10, 2 * n_sets)))
+        del gg, layers
+        group = {"layers": GROUP_LAYERS, "us": round(group_ms * 1e3, 2),
+                 "query_tokens_per_s_per_layer": round(GROUP_LAYERS * w.B * w.S / (group_ms * 1e-3), 1),
+                 "speedup_vs_a_step_per_layer": round(GROUP_LAYERS * ms_per_step / group_ms, 3),
+                 "reusing_layer_kernels": group_launches[1]}
+
     # algorithmic work of one attention pass: every valid slot's row once, q, o, idx, sink
     idx_all = torch.stack([bufs[i % n_sets]["idx"] for i in range(n_sets)])
     valid = (idx_all >= 0).view(n_sets, -1).sum(dim=1).double().mean().item()
@@ -390,6 +435,7 @@ def run_workload(w, a, log):
         "roofline": roof,
         "step_roofline": step_roof,
         "rest_of_step_us": None if rest_ms is None else round(rest_ms * 1e3, 2),
+        "layer_group": group,
         "config": {"workload": w.name, "mode": w.mode, "batch": w.B, "query_tokens": w.S, "context": w.end_pos,
                    "heads": w.H, "head_dim": w.D, "window": w.W, "compress_ratio": w.ratio, "index_heads": w.H_I,
                    "index_head_dim": w.D_I, "index_topk": w.index_topk,
@@ -399,7 +445,9 @@ def run_workload(w, a, log):
     log(f"[bench] {w.name}: step {ms_per_step * 1e3:.2f} us (wall {wall / a.steps * 1e6:.2f} us), {n_launch} "
         f"launch(es) {names}; dominant {dom_names}: avg {avg_ms * 1e3:.2f} us, median {med_ms * 1e3:.2f} us, "
         f"{roof['achieved']} {roof['unit']} = {roof['frac'] * 100:.1f}% of peak"
-        + ("" if rest_ms is None else f"; index+select {rest_ms * 1e3:.2f} us"))
+        + ("" if rest_ms is None else f"; index+select {rest_ms * 1e3:.2f} us")
+        + ("" if group is None else f"; {GROUP_LAYERS}-layer group {group['us']} us "
+           f"({group['speedup_vs_a_step_per_layer']}x a step per layer)"))
     for bf in bufs:
         bf.clear()
     keep = set0

@@ -8,9 +8,10 @@ seeded random draws that fill the inputs.
 Shapes and value distributions follow the DeepSeek V4.1 model page
 ("Attention" class, "Indexer" class and the model config JSON): 64 query heads
 of dim 512 sharing one KV row per position (used as key and value), a
-128-slot sliding window, 32 index heads of dim 128, index_topk 512.  The
-compress ratio of the workloads is 4 (the page's config uses 2 and 1 on real
-layers; ratio is a runtime parameter everywhere).
+128-slot sliding window, 32 index heads of dim 128, index_topk 512.  The five
+base workloads use compress ratio 4; the `_r2` and `_r1` workloads use the
+ratios the page's config gives its layers (2 on layers 2-19, 1 on layers
+20-39), at the same shapes.
 
 Draw order per workload: q, kv_win, kv_comp, qI, kI, w, sink.  Values are
 N(0,1) in fp32, rounded to bf16 (round-to-nearest-even) for bf16 workloads;
@@ -108,6 +109,15 @@ WORKLOADS = {
                  W=128, ratio=4, H_I=32, D_I=128, index_topk=512, dtype="bf16"),
         Workload("prefill_s32k_fp4", "prefill", B=1, S=32768, start_pos=0, H=64, D=512, rope_dim=64,
                  W=128, ratio=4, H_I=32, D_I=128, index_topk=512, dtype="bf16", comp_fmt="fp4"),
+        # the page config's own ratios: 2 on layers 2-19, 1 on layers 20-39 (compress_ratios)
+        Workload("decode_b16_ctx64k_r2", "decode", B=16, S=1, start_pos=65535, H=64, D=512, rope_dim=64,
+                 W=128, ratio=2, H_I=32, D_I=128, index_topk=512, dtype="bf16"),
+        Workload("decode_b16_ctx64k_r1", "decode", B=16, S=1, start_pos=65535, H=64, D=512, rope_dim=64,
+                 W=128, ratio=1, H_I=32, D_I=128, index_topk=512, dtype="bf16"),
+        Workload("prefill_s8k_r2", "prefill", B=1, S=8192, start_pos=0, H=64, D=512, rope_dim=64,
+                 W=128, ratio=2, H_I=32, D_I=128, index_topk=512, dtype="bf16"),
+        Workload("prefill_s8k_r1", "prefill", B=1, S=8192, start_pos=0, H=64, D=512, rope_dim=64,
+                 W=128, ratio=1, H_I=32, D_I=128, index_topk=512, dtype="bf16"),
     ]
 }
 # the order in which the workloads are listed for the method (tiny case first)

@@ -333,7 +333,7 @@ int topk_launch(const float* scores, int B, int S, int T, int K, int start_pos, 
     if (T <= 4096) return launch_topk_wave<64, 512, 8>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, st);
     if (T <= 8192) return launch_topk_wave<128, 1024, 8>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, st);
   }
-  // T <= 256*KPT with KPT <= 32, or 1024 threads x 64 keys for the longest rows
+  // T <= 256*KPT with KPT <= 8, then 1024 threads x up to 64 keys for the longest rows (64K context at ratio 1)
   if (T <= 256) return launch_topk<256, 1>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, st);
   if (T <= 512) return launch_topk<256, 2>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, st);
   if (T <= 1024) return launch_topk<256, 4>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, st);
@@ -342,7 +342,8 @@ int topk_launch(const float* scores, int B, int S, int T, int K, int start_pos, 
   if (T <= 8192) return launch_topk<1024, 8>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, st);
   if (T <= 16384) return launch_topk<1024, 16>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, st);
   if (T <= 32768) return launch_topk<1024, 32>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, st);
-  return fail(DSA_ERR_UNSUPPORTED, "dsa_topk: T=%d exceeds the supported 32768 rows", T);
+  if (T <= 65536) return launch_topk<1024, 64>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, st);
+  return fail(DSA_ERR_UNSUPPORTED, "dsa_topk: T=%d exceeds the supported 65536 rows", T);
 }
 
 int window_idx_launch(int B, int S, int start_pos, int W, int Wc, int32_t* idx, int64_t ld_idx, hipStream_t st) {

@@ -103,21 +103,67 @@ struct TopkSmem {
   uint64_t scan[2][NW];
 };
 
+// Raw bits of the E consecutive scores of a chunk starting at p0 (a chunk past c reads the row's
+// start instead, so every load stays inside the row).  Vector loads need whole chunks inside the
+// row (T a multiple of E) and an aligned row.  CO: 8-byte device-scope loads (past the CU's L1).
+template <int E, bool CO>
+__device__ __forceinline__ void load_chunk(const float* __restrict__ srow, int p0, int c, bool vec,
+                                           uint32_t (&k)[E]) {
+  if (vec) {
+    const float* src = srow + (p0 < c ? p0 : 0);
+    if constexpr (CO) {
+#pragma unroll
+      for (int q = 0; q < E / 2; ++q) {
+        const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(src + 2 * q), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT);
+        k[2 * q + 0] = (uint32_t)v;
+        k[2 * q + 1] = (uint32_t)(v >> 32);
+      }
+    } else if constexpr (E >= 4) {
+#pragma unroll
+      for (int q = 0; q < E / 4; ++q) {
+        const float4 v = *reinterpret_cast<const float4*>(src + 4 * q);
+        k[4 * q + 0] = __float_as_uint(v.x);
+        k[4 * q + 1] = __float_as_uint(v.y);
+        k[4 * q + 2] = __float_as_uint(v.z);
+        k[4 * q + 3] = __float_as_uint(v.w);
+      }
+    } else if constexpr (E == 2) {
+      const float2 v = *reinterpret_cast<const float2*>(src);
+      k[0] = __float_as_uint(v.x);
+      k[1] = __float_as_uint(v.y);
+    } else {
+      k[0] = __float_as_uint(src[0]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float* src = srow + min(p0 + e, c - 1);
+      k[e] = CO ? __hip_atomic_load(reinterpret_cast<const uint32_t*>(src), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                : __float_as_uint(*src);
+    }
+  }
+}
+
 // The K best of the c visible scores srow[0..c) (c > K, c <= NT * KPT; the row holds T >= c
 // scores), ties to the lower position, emitted in ascending position order as
 // put(slot, position + offset), slot 0..K-1.  Every thread of the NT-thread block calls it.
 //
-// Thread t keeps KPT scores in registers as order-preserving 32-bit keys (a larger float gives a
-// larger key; -0.0 is folded onto +0.0): J chunks of E consecutive positions, chunk j covering
-// positions E*(NT*j + t) .. +E-1, so the loads of a wave are contiguous and vectorised.  A radix
-// select finds the key of the K-th best score, 8 bits per pass, starting at the highest bit where
-// the row's keys differ, and stops early once the chosen bin holds exactly the keys still to be
-// taken.  Each pass counts into R copies of the histogram (lane l into copy l % R, so keys that
-// share a bin, as whole exponent ranges do in the first pass, spread their atomics over R
-// addresses) and costs two barriers.  Then one pass over the registers keeps every key above the
-// threshold and, of the keys equal to it, the lowest positions (ranked by a packed block scan that
-// is skipped when the select stopped early: then every equal key is kept); a second packed scan
-// gives each kept position its slot.
+// Thread t holds KPT scores as order-preserving 32-bit keys (a larger float gives a larger key;
+// -0.0 is folded onto +0.0): J chunks of E consecutive positions, chunk j covering positions
+// E*(NT*j + t) .. +E-1, so the loads of a wave are contiguous and vectorised.  A radix select finds
+// the key of the K-th best score, 8 bits per pass, starting at the highest bit where the row's keys
+// differ, and stops early once the chosen bin holds exactly the keys still to be taken.  Each pass
+// counts into R copies of the histogram (lane l into copy l % R, so keys that share a bin, as whole
+// exponent ranges do in the first pass, spread their atomics over R addresses) and costs two
+// barriers.  Then one pass over the keys keeps every key above the threshold and, of the keys equal
+// to it, the lowest positions (ranked by a packed block scan that is skipped when the select stopped
+// early: then every equal key is kept); a second packed scan gives each kept position its slot.
+//
+// Up to 32 keys per thread stay in registers for the whole select.  64 keys per thread (rows of up
+// to 65536 scores at 1024 threads) would not fit the 128 registers a thread has at that block size,
+// so then each pass re-reads its chunk's scores from the row (L2-resident after the first pass)
+// and only one chunk's keys are live at a time.
 //
 // CO = true reads the scores at device scope (past the CU's L1), for rows that other workgroups
 // wrote during the same launch.
@@ -129,6 +175,7 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ srow, int T
   constexpr int RP = TopkSmem<NT>::RP;
   constexpr int J = KPT < 4 ? KPT : 4;  // chunks per thread (one 16-bit field each in the scans)
   constexpr int E = KPT / J;            // consecutive positions per chunk
+  constexpr bool ST = KPT > 32;         // keys re-read per pass instead of held in registers
   static_assert(J * E == KPT && E <= 16, "KPT is 1, 2, 4 or a multiple of 4 up to 64");
   // one thread per histogram bin totals each pass: with fewer than 256 threads the upper bins
   // would keep stale counts, the select could keep more than K keys and put() would be handed
@@ -139,60 +186,67 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ srow, int T
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
-  uint32_t key[KPT];
-  // loads first, then branch-free keys, so the loads overlap.  Vector loads need whole chunks
-  // inside the row (T a multiple of E) and an aligned row; a chunk past c reads chunk 0 instead.
   constexpr int VA = E >= 4 ? 16 : 4 * E;
   const bool vec = E > 1 && T % E == 0 && (reinterpret_cast<uintptr_t>(srow) & (VA - 1)) == 0;
-  if (vec) {
+  // order keys of chunk j (0 for an invisible position, below every real key)
+  auto to_keys = [&](int j, uint32_t (&k)[E]) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool vis = E * (NT * j + tid) + e < c;
+      k[e] = vis ? order_key(__uint_as_float(k[e])) : 0u;
+    }
+  };
+  uint32_t key[ST ? 1 : KPT];  // all keys (held mode)
+  // the keys of chunk j in kc: from the registers, or re-read from the row
+  auto chunk_keys = [&](int j, uint32_t (&kc)[E]) {
+    if constexpr (ST) {
+      // an offset the compiler cannot see through, so the re-reads stay in their pass instead of
+      // being hoisted out of the pass loop (which would hold every key again)
+      int z = 0;
+      asm volatile("" : "+v"(z));
+      load_chunk<E, CO>(srow + z, E * (NT * j + tid), c, vec, kc);
+      to_keys(j, kc);
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) kc[e] = key[j * E + e];
+    }
+  };
+  if constexpr (!ST) {
+    // loads first, then branch-free keys, so the loads overlap
 #pragma unroll
     for (int j = 0; j < J; ++j) {
-      const int p0 = E * (NT * j + tid);
-      const float* src = srow + (p0 < c ? p0 : 0);
-      if constexpr (CO) {  // 8-byte device-scope loads
+      uint32_t kc[E];
+      load_chunk<E, CO>(srow, E * (NT * j + tid), c, vec, kc);
 #pragma unroll
-        for (int q = 0; q < E / 2; ++q) {
-          const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(src + 2 * q), __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT);
-          key[j * E + 2 * q + 0] = (uint32_t)v;
-          key[j * E + 2 * q + 1] = (uint32_t)(v >> 32);
-        }
-      } else if constexpr (E >= 4) {
-#pragma unroll
-        for (int q = 0; q < E / 4; ++q) {
-          const float4 v = *reinterpret_cast<const float4*>(src + 4 * q);
-          key[j * E + 4 * q + 0] = __float_as_uint(v.x);
-          key[j * E + 4 * q + 1] = __float_as_uint(v.y);
-          key[j * E + 4 * q + 2] = __float_as_uint(v.z);
-          key[j * E + 4 * q + 3] = __float_as_uint(v.w);
-        }
-      } else {
-        const float2 v = *reinterpret_cast<const float2*>(src);
-        key[j * E + 0] = __float_as_uint(v.x);
-        key[j * E + 1] = __float_as_uint(v.y);
-      }
+      for (int e = 0; e < E; ++e) key[j * E + e] = kc[e];
     }
-  } else {
-#pragma unroll
-    for (int j = 0; j < J; ++j)
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float* src = srow + min(E * (NT * j + tid) + e, c - 1);
-        key[j * E + e] = CO ? __hip_atomic_load(reinterpret_cast<const uint32_t*>(src), __ATOMIC_RELAXED,
-                                                __HIP_MEMORY_SCOPE_AGENT)
-                            : __float_as_uint(*src);
-      }
   }
   // this pass's histogram set starts at zero (the other set is cleared during the first pass)
   for (int i = tid; i < R * RP / 4; i += NT) reinterpret_cast<int4*>(sm.hist[0])[i] = int4{0, 0, 0, 0};
   uint32_t kand = 0xFFFFFFFFu, kor = 0u;
+  auto and_or_chunk = [&](int j) {
+    uint32_t kc[E];
+    if constexpr (ST) {
+      load_chunk<E, CO>(srow, E * (NT * j + tid), c, vec, kc);
+    } else {
 #pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const bool vis = E * (NT * (i / E) + tid) + i % E < c;
-    const uint32_t k = order_key(__uint_as_float(key[i]));
-    key[i] = vis ? k : 0u;  // invisible: below every real key
-    kand &= vis ? k : 0xFFFFFFFFu;
-    kor |= vis ? k : 0u;
+      for (int e = 0; e < E; ++e) kc[e] = key[j * E + e];
+    }
+    to_keys(j, kc);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const bool vis = E * (NT * j + tid) + e < c;
+      if constexpr (!ST) key[j * E + e] = kc[e];
+      kand &= vis ? kc[e] : 0xFFFFFFFFu;
+      kor |= vis ? kc[e] : 0u;
+    }
+  };
+  if constexpr (ST) {
+#pragma unroll 1
+    for (int j = 0; j < J; ++j) and_or_chunk(j);
+  } else {
+#pragma unroll
+    for (int j = 0; j < J; ++j) and_or_chunk(j);
   }
   wave_and_or(kand, kor);
   if (lane == 0) {
@@ -220,10 +274,21 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ srow, int T
       const int width = hb - lo + 1;
       const uint32_t dmask = ((width == 32) ? 0xFFFFFFFFu : ((1u << width) - 1u)) << lo;
       int* h = sm.hist[set] + (lane & (R - 1)) * RP;
+      auto count_chunk = [&](int j) {
+        uint32_t kc[E];
+        chunk_keys(j, kc);
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const bool vis = E * (NT * (i / E) + tid) + i % E < c;
-        if (vis && (key[i] & mask) == prefix) atomicAdd(&h[(key[i] & dmask) >> lo], 1);
+        for (int e = 0; e < E; ++e) {
+          const bool vis = E * (NT * j + tid) + e < c;
+          if (vis && (kc[e] & mask) == prefix) atomicAdd(&h[(kc[e] & dmask) >> lo], 1);
+        }
+      };
+      if constexpr (ST) {
+#pragma unroll 1
+        for (int j = 0; j < J; ++j) count_chunk(j);  // one chunk's loads in flight at a time
+      } else {
+#pragma unroll
+        for (int j = 0; j < J; ++j) count_chunk(j);
       }
       __syncthreads();
       // bin totals of this pass; the other set, last read before this pass's counting, is cleared
@@ -267,50 +332,58 @@ __device__ __forceinline__ void block_topk(const float* __restrict__ srow, int T
   // Under `mask` (the bits fixed so far), `prefix` is the K-th best visible key: keep the keys above
   // it and the first `remaining` keys equal to it in position order
   const uint32_t tau = prefix;
-  int eq_base[J];
-#pragma unroll
-  for (int j = 0; j < J; ++j) eq_base[j] = 0;
+  // rank of this thread's first key equal to tau in chunk j among all such keys (0 when exact:
+  // then every equal key is kept and no ranks are needed)
+  uint64_t eq_tot = 0, eq_before = 0;
   if (!exact) {
     uint64_t eqw = 0;
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
+    auto eq_chunk = [&](int j) {
+      uint32_t kc[E];
+      chunk_keys(j, kc);
       int n = 0;
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int i = j * E + e;
-        n += (E * (NT * j + tid) + e < c && (key[i] & mask) == tau) ? 1 : 0;
-      }
+      for (int e = 0; e < E; ++e) n += (E * (NT * j + tid) + e < c && (kc[e] & mask) == tau) ? 1 : 0;
       eqw |= (uint64_t)n << (16 * j);
-    }
-    uint64_t eq_tot;
-    const uint64_t eq_before = block_scan_packed<NT>(eqw, sm.scan[0], &eq_tot);
+    };
+    if constexpr (ST) {
+#pragma unroll 1
+      for (int j = 0; j < J; ++j) eq_chunk(j);
+    } else {
 #pragma unroll
-    for (int j = 0; j < J; ++j) eq_base[j] = fields_below(eq_tot, j) + field16(eq_before, j);
+      for (int j = 0; j < J; ++j) eq_chunk(j);
+    }
+    eq_before = block_scan_packed<NT>(eqw, sm.scan[0], &eq_tot);
   }
   Bits keep_bits = 0u;
-  if (exact) {  // every key at or above the threshold is taken
+  auto keep_chunk = [&](int j) {
+    uint32_t kc[E];
+    chunk_keys(j, kc);
+    int rank = exact ? 0 : fields_below(eq_tot, j) + field16(eq_before, j);
+    Bits kb = 0u;
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const bool vis = E * (NT * (i / E) + tid) + i % E < c;
-      keep_bits |= (vis && (key[i] & mask) >= tau) ? (Bits)1 << i : (Bits)0;
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < J; ++j) {
-      int rank = eq_base[j];
-#pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int i = j * E + e;
-        const bool vis = E * (NT * j + tid) + e < c;
-        const uint32_t mk = key[i] & mask;
-        bool k = vis && mk > tau;
+    for (int e = 0; e < E; ++e) {
+      const bool vis = E * (NT * j + tid) + e < c;
+      const uint32_t mk = kc[e] & mask;
+      bool k;
+      if (exact) {  // every key at or above the threshold is taken
+        k = vis && mk >= tau;
+      } else {
+        k = vis && mk > tau;
         if (vis && mk == tau) {
           k = rank < remaining;
           ++rank;
         }
-        keep_bits |= k ? (Bits)1 << i : (Bits)0;
       }
+      kb |= k ? (Bits)1 << e : (Bits)0;
     }
+    keep_bits |= kb << (j * E);
+  };
+  if constexpr (ST) {
+#pragma unroll 1
+    for (int j = 0; j < J; ++j) keep_chunk(j);
+  } else {
+#pragma unroll
+    for (int j = 0; j < J; ++j) keep_chunk(j);
   }
   constexpr uint32_t CM = (1u << E) - 1u;  // one chunk's bits
   uint64_t kw = 0;

@@ -79,6 +79,10 @@ def test_window_idx(B, S, sp, W):
     (2, 1, 16384, 512, 65535, 4, "normal"),
     (1, 1, 16384, 512, 65535, 4, "ties"),
     (1, 1, 30000, 700, 29999, 1, "normal"),
+    # the page config's ratio 1 at 64K context: 65536 scores per row (keys re-read per pass)
+    (2, 1, 65536, 512, 65535, 1, "normal"),
+    (1, 1, 65536, 512, 65535, 1, "ties"),
+    (3, 1, 40000, 512, 79999, 2, "zeros"),
     (1, 3, 600, 1, 1797, 3, "normal"),
     # 1024+ rows: one wave per row (2048, 4096 and 8192 keys per lane group)
     (1, 1100, 4000, 512, 0, 1, "ties"),
@@ -606,3 +610,43 @@ def test_nan_in_q_propagates(B, S, nw, nc, L):
     mask[0, S - 1, 5] = False
     assert np.all(np.isfinite(o[mask]))
     assert max_abs_err(o[mask], exp[mask]) <= ATTN_TOL["bf16"]
+
+
+# ------------------------------------------------------------------------ the page config's ratios (2 and 1)
+def _device_set_to_cpu(w, dev_in):
+    need = {"q", "kv_win", "kv_comp", "kv_comp_fp4", "kv_comp_scale", "kI", "sink", "qI", "w"}
+    return {k: v.cpu() for k, v in dev_in.items() if k in need}
+
+
+@pytest.mark.parametrize("name", ["decode_b16_ctx64k_r2", "decode_b16_ctx64k_r1"])
+def test_step_full_real_ratio_decode(name):
+    """Decode at 64K context with the ratios of the page's layers (T = 32768 and 65536 index rows
+    per query), every query checked: scores, index rows by the parity rules, attention."""
+    w = dsa_synth.get(name)
+    _log(f"step {name} (full check, T={w.T})")
+    dev_in = dsa_synth.generate(w, seed=0, device=DEV)
+    o, idx, scores = _step(w, dev_in)
+    n, names = _launched()
+    _log(f"  launches: {n} {names}")
+    assert "topk_block" in names and "sparse_attn_decode<NS=16>" in names, names
+    torch.cuda.synchronize()
+    cpu_in = _device_set_to_cpu(w, dev_in)
+    rows = [(b, t) for b in range(w.B) for t in range(w.S)]
+    _check_step(w, cpu_in, o, idx, scores, rows)
+    assert _dsa().dsa_device_errors() == 0
+
+
+@pytest.mark.parametrize("name", ["prefill_s8k_r2", "prefill_s8k_r1"])
+def test_step_real_ratio_prefill_sampled(name):
+    """Prefill of 8192 tokens with ratios 2 and 1 (T = 4096 and 8192), in the launch configuration
+    the benchmark times, on sampled queries (including the c(t) = K crossover)."""
+    w = dsa_synth.get(name)
+    _log(f"step {name} (full size, sampled, T={w.T})")
+    dev_in = dsa_synth.generate(w, seed=0, device=DEV)
+    o, idx, scores = _step(w, dev_in)
+    n, names = _launched()
+    _log(f"  launches: {n} {names}")
+    torch.cuda.synchronize()
+    cpu_in = _device_set_to_cpu(w, dev_in)
+    rows = sample_rows(w, n_random=12)
+    _check_step(w, cpu_in, o, idx, scores, rows)
