@@ -30,6 +30,7 @@ __all__ = [
     "get",
     "generate",
     "encode_fp4_e2m1_e4m3",
+    "encode_mxfp4_e8m0",
     "scaled",
     "nbytes",
 ]
@@ -52,6 +53,7 @@ class Workload:
     index_topk: int
     dtype: str  # "f32" or "bf16": q, kv, index q/k, head weights, output
     comp_fmt: str = "same"  # "same" (as dtype) or "fp4" (e2m1 + E4M3 scale per 16)
+    index_fmt: str = "same"  # "same" (as dtype) or "mxfp4" (index q/k as e2m1 + E8M0 scale per 32)
 
     # ---- derived sizes (no arithmetic of the method, only bookkeeping) ----
     @property
@@ -94,6 +96,8 @@ class Workload:
             assert self.start_pos == 0, self
         if self.comp_fmt == "fp4":
             assert self.dtype == "bf16" and self.D % 16 == 0
+        if self.index_fmt == "mxfp4":
+            assert self.dtype == "bf16" and self.D_I % 32 == 0
 
 
 WORKLOADS = {
@@ -118,6 +122,16 @@ WORKLOADS = {
                  W=128, ratio=2, H_I=32, D_I=128, index_topk=512, dtype="bf16"),
         Workload("prefill_s8k_r1", "prefill", B=1, S=8192, start_pos=0, H=64, D=512, rope_dim=64,
                  W=128, ratio=1, H_I=32, D_I=128, index_topk=512, dtype="bf16"),
+        # the indexer in the precision the pages give it: index queries and keys fp4 with E8M0 scales
+        # per 32 elements (the same shapes as the bf16-indexer workloads)
+        Workload("decode_b32_ctx8k_mxfp4", "decode", B=32, S=1, start_pos=8191, H=64, D=512, rope_dim=64,
+                 W=128, ratio=4, H_I=32, D_I=128, index_topk=512, dtype="bf16", index_fmt="mxfp4"),
+        Workload("decode_b16_ctx64k_mxfp4", "decode", B=16, S=1, start_pos=65535, H=64, D=512, rope_dim=64,
+                 W=128, ratio=4, H_I=32, D_I=128, index_topk=512, dtype="bf16", index_fmt="mxfp4"),
+        Workload("decode_b16_ctx64k_r1_mxfp4", "decode", B=16, S=1, start_pos=65535, H=64, D=512, rope_dim=64,
+                 W=128, ratio=1, H_I=32, D_I=128, index_topk=512, dtype="bf16", index_fmt="mxfp4"),
+        Workload("prefill_s8k_mxfp4", "prefill", B=1, S=8192, start_pos=0, H=64, D=512, rope_dim=64,
+                 W=128, ratio=4, H_I=32, D_I=128, index_topk=512, dtype="bf16", index_fmt="mxfp4"),
     ]
 }
 # the order in which the workloads are listed for the method (tiny case first)
@@ -190,12 +204,50 @@ def encode_fp4_e2m1_e4m3(x: torch.Tensor, group: int = 16):
     return packed.contiguous(), s8.view(torch.uint8).reshape(*x.shape[:-1], x.shape[-1] // group).contiguous()
 
 
+def encode_mxfp4_e8m0(x: torch.Tensor, block: int = 32):
+    """Encode rows [..., D] as packed e2m1 nibbles plus one E8M0 scale per `block`.
+
+    The generator's encoder for the indexer's fp4 (the pages name the format,
+    fp4 with E8M0 scales per 32, but not the quantiser): the scale is the
+    smallest power of two 2**e with amax / 2**e <= 6 (so nothing clips; e is
+    clamped to [-127, 127], and an all-zero block takes e = -127); each element
+    is x / 2**e rounded to the nearest e2m1 value, ties to the even code.  Byte
+    k of a row holds element 2k in its low nibble; the scale byte is e + 127.
+
+    Returns (packed uint8 [..., D/2], scales uint8 [..., D/block]).
+    """
+    assert x.shape[-1] % block == 0
+    xs = x.float().reshape(*x.shape[:-1], x.shape[-1] // block, block)
+    amax = xs.abs().amax(dim=-1)
+    safe = torch.where(amax > 0, amax, torch.ones_like(amax))
+    e = torch.ceil(torch.log2(safe / 6.0))
+    # log2 can land a hair off an exact power of two: step e until 6 * 2**e is the first bound >= amax
+    e = torch.where(6.0 * torch.exp2(e - 1) >= safe, e - 1, e)
+    e = torch.where(6.0 * torch.exp2(e) < safe, e + 1, e)
+    e = torch.where(amax > 0, e, torch.full_like(e, -127.0)).clamp(-127, 127)
+    y = xs / torch.exp2(e).unsqueeze(-1)
+    m = y.abs()
+    code = torch.zeros_like(m, dtype=torch.int32)
+    for i in range(7):
+        mid = 0.5 * (_E2M1_GRID[i] + _E2M1_GRID[i + 1])
+        code += (m > mid).int()
+        if (i + 1) % 2 == 0:
+            code += (m == mid).int()
+    code = code.clamp(max=7) | torch.where(y < 0, 8, 0).int()
+    code = code.reshape(*x.shape[:-1], x.shape[-1]).to(torch.uint8)
+    packed = code[..., 0::2] | (code[..., 1::2] << 4)
+    scales = (e + 127).to(torch.uint8).reshape(*x.shape[:-1], x.shape[-1] // block)
+    return packed.contiguous(), scales.contiguous()
+
+
 def generate(w: Workload, seed: int = 0, device="cpu") -> dict:
     """Seeded inputs of a workload, all on `device`.
 
     Keys: q [B,S,H,D], kv_win [B,n_win,D], kv_comp [B,T,D] (or, for the fp4
     workload, kv_comp_fp4 [B,T,D/2] uint8 and kv_comp_scale [B,T,D/16] uint8),
-    qI [B,S,H_I,D_I], kI [B,T,D_I], w [B,S,H_I], sink [H] fp32.
+    qI [B,S,H_I,D_I], kI [B,T,D_I] (or, for the MXFP4 indexer, qI_fp4
+    [B,S,H_I,D_I/2], qI_scale [B,S,H_I,D_I/32], kI_fp4 [B,T,D_I/2], kI_scale
+    [B,T,D_I/32], all uint8), w [B,S,H_I], sink [H] fp32.
     The draws are made on `device` with its own generator, so CPU and GPU
     draws of one seed differ; each is deterministic.
     """
@@ -213,8 +265,15 @@ def generate(w: Workload, seed: int = 0, device="cpu") -> dict:
         del raw
     else:
         out["kv_comp"] = _randn((w.B, w.T, w.D), gen, dev, dt)
-    out["qI"] = _randn((w.B, w.S, w.H_I, w.D_I), gen, dev, dt)
-    out["kI"] = _randn((w.B, w.T, w.D_I), gen, dev, dt)
+    if w.index_fmt == "mxfp4":
+        raw = _randn((w.B, w.S, w.H_I, w.D_I), gen, dev, torch.float32)
+        out["qI_fp4"], out["qI_scale"] = encode_mxfp4_e8m0(raw, 32)
+        raw = _randn((w.B, w.T, w.D_I), gen, dev, torch.float32)
+        out["kI_fp4"], out["kI_scale"] = encode_mxfp4_e8m0(raw, 32)
+        del raw
+    else:
+        out["qI"] = _randn((w.B, w.S, w.H_I, w.D_I), gen, dev, dt)
+        out["kI"] = _randn((w.B, w.T, w.D_I), gen, dev, dt)
     out["w"] = (_randn((w.B, w.S, w.H_I), gen, dev, torch.float32) * 0.5).to(dt)
     out["sink"] = _randn((w.H,), gen, dev, torch.float32)
     return out

@@ -24,6 +24,10 @@ model pages by the class or function that holds the step:
                       denominator only, -1 slots ignored, all-invalid rows -> 0
 * fp4 compressed KV -- `_compress_kv` (page "reindex-layer/read-weights"): e2m1
                       values with one E4M3 scale per 16 elements
+* MXFP4 index q/k   -- `Indexer.forward` quantises the index queries and keys to
+                      fp4, and `_compress_kv` states the indexer's blocks: 32
+                      elements per E8M0 (power-of-two) scale.  The scores are the
+                      same definition over the decoded values.
 
 Readings where the pages leave a step open (each also listed with the design
 notes): ties in the top-k go to the lower position; scores are exact (not the
@@ -48,6 +52,8 @@ __all__ = [
     "e2m1_decode",
     "e4m3_decode",
     "fp4_rows_decode",
+    "e8m0_decode",
+    "mxfp4_rows_decode",
     "kv_concat",
     "sparse_attn",
     "sparse_attn_rows",
@@ -232,6 +238,31 @@ def fp4_rows_decode(packed, scales, group: int = 16) -> np.ndarray:
     vals[..., 1::2] = hi
     s = np.repeat(e4m3_decode(sc), group, axis=-1)
     return vals * s
+
+
+# ----------------------------------------------------------------------------
+# MXFP4: e2m1 with E8M0 block scales (the indexer's format)
+# ----------------------------------------------------------------------------
+def e8m0_decode(code) -> np.ndarray:
+    """E8M0 scale (OCP Microscaling spec): an unsigned 8-bit biased exponent, value
+    2**(code - 127); code 255 is NaN.  No sign, no mantissa."""
+    c = np.asarray(code, dtype=np.int64) & 0xFF
+    return np.where(c == 255, np.nan, np.ldexp(1.0, c - 127))
+
+
+def mxfp4_rows_decode(packed, scales, block: int = 32) -> np.ndarray:
+    """Index rows from packed e2m1 nibbles [..., D/2] and E8M0 scales [..., D/block].
+
+    `_compress_kv` / `Indexer.forward`: blocks of 32 consecutive elements share one
+    E8M0 scale; element 2k is the low nibble of byte k, element 2k+1 the high
+    nibble.  value = e2m1(nibble) * 2**(scale - 127).
+    """
+    p = np.asarray(packed.cpu().numpy() if hasattr(packed, "cpu") else packed, dtype=np.int64)
+    sc = np.asarray(scales.cpu().numpy() if hasattr(scales, "cpu") else scales, dtype=np.int64)
+    vals = np.empty(p.shape[:-1] + (p.shape[-1] * 2,), dtype=np.float64)
+    vals[..., 0::2] = e2m1_decode(p & 0xF)
+    vals[..., 1::2] = e2m1_decode(p >> 4)
+    return vals * np.repeat(e8m0_decode(sc), block, axis=-1)
 
 
 # ----------------------------------------------------------------------------

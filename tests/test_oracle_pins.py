@@ -146,6 +146,98 @@ def test_fp4_products_exact_in_bf16():
     assert torch.equal(prod.to(torch.bfloat16).double(), prod)
 
 
+# ---------------------------------------------------------------- MXFP4 (indexer fp4, E8M0 / 32)
+def test_e8m0_golden_and_library():
+    for ln in _lines("e8m0_points.txt"):
+        code, val = ln.split()
+        got = float(oracle.e8m0_decode(int(code, 16)))
+        if val == "nan":
+            assert math.isnan(got)
+        else:
+            assert got == float(val)
+    # all 256 codes against torch's float8_e8m0fnu conversion
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    lib = codes.view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    ours = oracle.e8m0_decode(np.arange(256))
+    np.testing.assert_array_equal(np.isnan(ours), np.isnan(lib))
+    ok = ~np.isnan(lib)
+    np.testing.assert_array_equal(ours[ok], lib[ok])
+
+
+def test_mxfp4_packing_and_blocks():
+    # D = 64: two blocks of 32 elements, two scale bytes
+    packed = np.zeros((1, 32), dtype=np.uint8)
+    packed[0, 0] = 0x21   # element 0 = code 1 (0.5), element 1 = code 2 (1.0)
+    packed[0, 15] = 0x9F  # element 30 = code 15 (-6), element 31 = code 9 (-0.5): last of block 0
+    packed[0, 16] = 0x07  # element 32 = +6: first of block 1
+    scales = np.array([[0x7E, 0x81]], dtype=np.uint8)  # block 0 x 0.5, block 1 x 4
+    v = oracle.mxfp4_rows_decode(packed, scales)
+    assert v.shape == (1, 64)
+    assert v[0, 0] == 0.25 and v[0, 1] == 0.5
+    assert v[0, 30] == -3.0 and v[0, 31] == -0.25
+    assert v[0, 32] == 24.0 and v[0, 33] == 0.0
+    assert np.count_nonzero(v) == 5
+
+
+def test_mxfp4_decode_against_generator_encoder():
+    import dsa_synth
+
+    g = torch.Generator().manual_seed(4)
+    x = torch.randn(4, 32, 128, generator=g) * torch.exp(torch.randn(4, 32, 1, generator=g))
+    x[0, 0, :32] = 0.0  # an all-zero block
+    packed, scales = dsa_synth.encode_mxfp4_e8m0(x, 32)
+    assert packed.shape == (4, 32, 64) and scales.shape == (4, 32, 4)
+    dec = oracle.mxfp4_rows_decode(packed, scales)
+    xs = x.double().numpy()
+    sc = np.repeat(oracle.e8m0_decode(scales.numpy()), 32, axis=-1)
+    # nothing clips (the scale covers the block maximum within the e2m1 range of 6), and rounding
+    # to the nearest grid value costs at most half of the widest step (2, between 4 and 6)
+    assert np.all(np.abs(xs) <= 6 * sc)
+    assert np.all(np.abs(dec - xs) <= 1.0 * sc)
+    ratio = np.abs(dec / sc)
+    assert set(np.unique(ratio).tolist()) <= {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0}
+    assert np.all(dec[0, 0, :32] == 0)
+    # values already on a block's grid come back exactly
+    again = oracle.mxfp4_rows_decode(*dsa_synth.encode_mxfp4_e8m0(torch.from_numpy(dec).float(), 32))
+    np.testing.assert_array_equal(again, dec)
+    # every decoded value is exact in bf16 (the page keeps the fake-quantised index keys in bf16)
+    t = torch.from_numpy(dec)
+    assert torch.equal(t.to(torch.bfloat16).double(), t)
+
+
+def test_mxfp4_index_scores_brute():
+    """Scores on MXFP4 index inputs: a scalar loop that decodes every element from the golden
+    e2m1 and E8M0 tables itself equals the oracle's decode followed by its score definition."""
+    import dsa_synth
+
+    e2m1 = {int(c, 16): float(v) for c, v in (ln.split() for ln in _lines("fp4_e2m1.txt"))}
+    g = torch.Generator().manual_seed(9)
+    B, S, T, H, D = 1, 3, 5, 2, 64
+    qp, qs = dsa_synth.encode_mxfp4_e8m0(torch.randn(B, S, H, D, generator=g), 32)
+    kp, ks = dsa_synth.encode_mxfp4_e8m0(torch.randn(B, T, D, generator=g) * 4, 32)
+    w = torch.randn(B, S, H, generator=g).double().numpy()
+    sp, ratio, ws = 7, 2, 0.3
+    got = oracle.index_scores(oracle.mxfp4_rows_decode(qp, qs), oracle.mxfp4_rows_decode(kp, ks), w, ws, sp, ratio)
+
+    def elem(packed, scales, idx, d):
+        byte = int(packed[idx + (d // 2,)])
+        code = byte & 0xF if d % 2 == 0 else byte >> 4
+        return e2m1[code] * 2.0 ** (int(scales[idx + (d // 32,)]) - 127)
+
+    qpn, qsn, kpn, ksn = qp.numpy(), qs.numpy(), kp.numpy(), ks.numpy()
+    for t in range(S):
+        c = (sp + t + 1) // ratio
+        for j in range(T):
+            if j >= c:
+                assert got[0, t, j] == -np.inf
+                continue
+            tot = 0.0
+            for h in range(H):
+                dot = sum(elem(qpn, qsn, (0, t, h), d) * elem(kpn, ksn, (0, j), d) for d in range(D))
+                tot += w[0, t, h] * max(dot, 0.0)
+            assert abs(got[0, t, j] - ws * tot) <= 1e-12 * max(1.0, abs(ws * tot))
+
+
 # ---------------------------------------------------------------- index scores
 def test_index_scores_hand_golden():
     d = {ln.split()[0]: ln.split()[1:] for ln in _lines("index_scores_hand.txt")}
@@ -414,3 +506,31 @@ def test_planted_slips_are_caught(monkeypatch):
     s = np.array([5.0, 5.0, 5.0, 5.0])
     assert od.topk_select_row(s, 2, 4, 0).tolist() == [0, 1]
     assert _topk_brute(s.tolist(), 2, 4, 0) == [0, 1]
+
+
+def test_planted_mxfp4_slips_are_caught(monkeypatch):
+    """Plausible mistakes in the MXFP4 decode (nibble order swapped, a block of 16 instead of 32,
+    a bias of 128) each break a pin."""
+    import oracle.dsa_oracle as od
+
+    test_mxfp4_packing_and_blocks()
+    real = od.mxfp4_rows_decode
+
+    def swapped(packed, scales, block=32):
+        p = np.asarray(packed, dtype=np.int64)
+        return real(((p & 0xF) << 4) | (p >> 4), scales, block)
+
+    def block16(packed, scales, block=32):  # the compressed KV's group size with the indexer's scales
+        sc = np.asarray(scales)
+        return real(packed, np.concatenate([sc, sc], axis=-1), 16)
+
+    for slip in (swapped, block16):
+        monkeypatch.setattr(od, "mxfp4_rows_decode", slip)
+        monkeypatch.setattr(oracle, "mxfp4_rows_decode", slip)
+        with pytest.raises(AssertionError):
+            test_mxfp4_packing_and_blocks()
+        monkeypatch.undo()
+    monkeypatch.setattr(od.np, "ldexp", lambda m, e: m * 2.0 ** (np.asarray(e) - 1))
+    with pytest.raises(AssertionError):
+        test_e8m0_golden_and_library()
+    monkeypatch.undo()
