@@ -5,6 +5,7 @@
  * caller's HIP stream, none allocating device memory):
  *
  *   dsa_index_scores  score every compressed KV row for every query
+ *   dsa_index_scores_mxfp4  the same with the indexer's fp4 (E8M0 per 32) query and key rows
  *   dsa_topk          keep the index_topk best visible rows per query
  *   dsa_window_idx    the sliding-window part of each query's index row
  *   dsa_select        window part and top-k part of the index rows in one launch
@@ -149,6 +150,26 @@ int dsa_check_idx(const int32_t* idx, int64_t count, int64_t n_rows, int64_t* fi
 int dsa_index_scores(const void* q_idx, const void* k_idx, int64_t k_batch_stride, const void* w,
                      float w_scale, int dtype, int B, int S, int T, int H_I, int D_I, int start_pos,
                      int ratio, float* scores, dsa_stream_t stream);
+
+/*
+ * Index scores with the indexer's fp4 operands (`Indexer.forward` quantises the index queries and
+ * keys to fp4; `_compress_kv` gives the indexer's blocks: 32 elements per E8M0 scale):
+ * the same scores as dsa_index_scores over the decoded values
+ *   value = e2m1(nibble) * 2^(scale byte - 127)   (scale byte 255 is NaN),
+ * element 2k of a row in the low nibble of byte k, elements 32i .. 32i+31 scaled by scale byte i.
+ *
+ *   q_idx   [B, S, H_I, D_I/2] uint8 packed e2m1     q_scale [B, S, H_I, D_I/32] uint8 E8M0
+ *   k_idx   [B, k_batch_rows, D_I/2] uint8           k_scale [B, k_batch_rows, D_I/32] uint8
+ *           (rows 0 .. T-1 of each batch are read; k_batch_rows >= T, so a cache slice needs no copy)
+ *   w       [B, S, H_I] bf16 raw head weights;  scores [B, S, T] float32, written in full
+ *
+ * Products are exact (block-scaled MFMA on e2m1 operands), sums float32.  Supported: D_I in
+ * {64, 128, 256}, H_I in 1..64; q_idx and k_idx 16-byte aligned.  Same visibility rules and errors as
+ * dsa_index_scores.
+ */
+int dsa_index_scores_mxfp4(const uint8_t* q_idx, const uint8_t* q_scale, const uint8_t* k_idx,
+                           const uint8_t* k_scale, int64_t k_batch_rows, const void* w, float w_scale, int B, int S,
+                           int T, int H_I, int D_I, int start_pos, int ratio, float* scores, dsa_stream_t stream);
 
 /*
  * Top-k selection (`Indexer.forward`: top-k by score, re-sorted into position
@@ -316,6 +337,23 @@ int dsa_sparse_attn_step(const void* q_idx, const void* k_idx, int64_t k_batch_s
                          const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink, float scale, void* o,
                          int dtype, int B, int S, int H, int D, float* scores, int32_t* idx, void* workspace,
                          size_t workspace_bytes, dsa_stream_t stream);
+
+/*
+ * The whole step with the indexer's fp4 operands: the same results as
+ *
+ *   dsa_index_scores_mxfp4(q_idx, q_scale, k_idx, k_scale, k_batch_rows, w, w_scale, B, S, T, H_I, D_I,
+ *                          start_pos, ratio, scores, stream)
+ *   dsa_sparse_attn_select(scores, T, index_topk, start_pos, ratio, W, q, win, comp, sink, scale, o,
+ *                          dtype, B, S, H, D, idx, workspace, workspace_bytes, stream)
+ *
+ * (dtype must be DSA_BF16).  Errors: those of the two calls.
+ */
+int dsa_sparse_attn_step_mxfp4(const uint8_t* q_idx, const uint8_t* q_scale, const uint8_t* k_idx,
+                               const uint8_t* k_scale, int64_t k_batch_rows, const void* w, float w_scale, int H_I,
+                               int D_I, int T, int index_topk, int start_pos, int ratio, int W, const void* q,
+                               const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink, float scale,
+                               void* o, int dtype, int B, int S, int H, int D, float* scores, int32_t* idx,
+                               void* workspace, size_t workspace_bytes, dsa_stream_t stream);
 
 /*
  * The whole step without a workspace argument, for callers that cannot allocate device memory

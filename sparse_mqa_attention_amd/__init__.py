@@ -75,6 +75,12 @@ def _load():
     lib.dsa_topk_plan.restype = i32
     lib.dsa_index_scores.argtypes = [vp, vp, i64, vp, f32, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.dsa_index_scores.restype = i32
+    lib.dsa_index_scores_mxfp4.argtypes = [vp, vp, vp, vp, i64, vp, f32, i32, i32, i32, i32, i32, i32, i32, vp, vp]
+    lib.dsa_index_scores_mxfp4.restype = i32
+    lib.dsa_sparse_attn_step_mxfp4.argtypes = [vp, vp, vp, vp, i64, vp, f32, i32, i32, i32, i32, i32, i32, i32, vp,
+                                               ctypes.POINTER(DsaKvSrc), ctypes.POINTER(DsaKvSrc), vp, f32, vp, i32,
+                                               i32, i32, i32, i32, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.dsa_sparse_attn_step_mxfp4.restype = i32
     lib.dsa_topk.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, i64, vp]
     lib.dsa_topk.restype = i32
     lib.dsa_select.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, i64, vp]
@@ -242,6 +248,81 @@ def dsa_index_scores(q_idx, k_idx, w, w_scale: float, start_pos: int, ratio: int
     _check(lib.dsa_index_scores(_ptr(q_idx), _ptr(k_idx), kbs, _ptr(w), float(w_scale), _dtype_code(q_idx), B, S, T,
                                 H, Dd, int(start_pos), int(ratio), _ptr(out), _stream(dev, stream)))
     return out
+
+
+def _mx_index_operands(qI, qI_scale, kI, kI_scale, w):
+    """Shapes of MXFP4 index operands, checked: (B, S, H_I, D_I, T, k_batch_rows)."""
+    for name, t in (("qI", qI), ("qI_scale", qI_scale), ("kI", kI), ("kI_scale", kI_scale)):
+        if t is None or t.dtype != torch.uint8:
+            raise DsaError(-3, f"{name} must be uint8 (packed e2m1 nibbles / E8M0 scale bytes)")
+    _need_contig("qI", qI)
+    _need_contig("qI_scale", qI_scale)
+    if qI.dim() != 4 or kI.dim() != 3:
+        raise DsaError(-2, "qI must be [B, S, H_I, D_I/2] and kI [B, T, D_I/2]")
+    B, S, H, half = qI.shape
+    D_I = 2 * half
+    T = kI.shape[1]
+    _expect("qI_scale", qI_scale, (B, S, H, D_I // 32), torch.uint8)
+    if kI.shape[0] != B or kI.shape[2] != half or kI.stride(2) != 1 or kI.stride(1) != half:
+        raise DsaError(-2, "kI must be [B, T, D_I/2] with dense rows")
+    if tuple(kI_scale.shape) != (B, T, D_I // 32) or kI_scale.stride(2) != 1 or kI_scale.stride(1) != D_I // 32:
+        raise DsaError(-2, "kI_scale must be [B, T, D_I/32] with dense rows")
+    rows = kI.stride(0) // half
+    if kI.stride(0) % half or kI_scale.stride(0) != rows * (D_I // 32):
+        raise DsaError(-2, "kI and kI_scale must be slices of caches with the same row count per batch")
+    if w.dtype != torch.bfloat16:
+        raise DsaError(-3, "w must be bfloat16")
+    _expect("w", w, (B, S, H), torch.bfloat16)
+    _need_contig("w", w)
+    return B, S, H, D_I, T, rows
+
+
+def dsa_index_scores_mxfp4(qI, qI_scale, kI, kI_scale, w, w_scale: float, start_pos: int, ratio: int, out=None,
+                           stream=None):
+    """Index scores [B, S, T] float32 from MXFP4 index operands; see `dsa_index_scores_mxfp4` in
+    include/dsa.h.  qI [B,S,H_I,D_I/2] uint8, qI_scale [B,S,H_I,D_I/32] uint8, kI [B,T,D_I/2] uint8,
+    kI_scale [B,T,D_I/32] uint8 (cache slices allowed), w [B,S,H_I] bf16."""
+    B, S, H, D_I, T, rows = _mx_index_operands(qI, qI_scale, kI, kI_scale, w)
+    if out is not None:
+        _expect("scores", out, (B, S, T), torch.float32)
+    dev = _dev(qI, qI_scale, kI, kI_scale, w, out)
+    if out is None:
+        out = torch.empty(B, S, T, dtype=torch.float32, device=dev)
+    _need_contig("scores", out)
+    _check(lib.dsa_index_scores_mxfp4(_ptr(qI), _ptr(qI_scale), _ptr(kI), _ptr(kI_scale), rows, _ptr(w),
+                                      float(w_scale), B, S, T, H, D_I, int(start_pos), int(ratio), _ptr(out),
+                                      _stream(dev, stream)))
+    return out
+
+
+def dsa_sparse_attn_step_mxfp4(qI, qI_scale, kI, kI_scale, w, q, kv_win, kv_comp, sink, *, index_topk: int,
+                               start_pos: int, ratio: int, W: int, scale: float, w_scale: float, comp_scales=None,
+                               out=None, scores=None, idx=None, workspace=None, stream=None):
+    """The whole step with MXFP4 index operands (dsa_sparse_attn_step_mxfp4): returns (o, idx, scores)."""
+    B, S, H_I, D_I, T, rows = _mx_index_operands(qI, qI_scale, kI, kI_scale, w)
+    Bq, Sq, H, D, dt, win, comp, out = _attn_operands(q, kv_win, kv_comp, sink, comp_scales, out)
+    if (Bq, Sq) != (B, S):
+        raise DsaError(-2, "q and the index queries disagree on [B, S]")
+    Wc = dsa_window_cols(S, start_pos, W)
+    L = Wc + min(int(index_topk), T)
+    if scores is not None:
+        _expect("scores", scores, (B, S, T), torch.float32)
+    if idx is not None:
+        _expect("idx", idx, (B, S, L), torch.int32)
+    dev = _dev(qI, qI_scale, kI, kI_scale, w, q, kv_win, kv_comp, sink, out, scores, idx)
+    if scores is None:
+        scores = torch.empty(B, S, T, dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty(B, S, L, dtype=torch.int32, device=dev)
+    need = dsa_sparse_attn_workspace_size(dt, B, S, H, D, L)
+    workspace = _workspace(need, workspace, dev)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.dsa_sparse_attn_step_mxfp4(_ptr(qI), _ptr(qI_scale), _ptr(kI), _ptr(kI_scale), rows, _ptr(w),
+                                          float(w_scale), H_I, D_I, T, int(index_topk), int(start_pos), int(ratio),
+                                          int(W), _ptr(q), ctypes.byref(win), ctypes.byref(comp), _ptr(sink),
+                                          float(scale), _ptr(out), dt, B, S, H, D, _ptr(scores), _ptr(idx),
+                                          _ptr(workspace), wbytes, _stream(dev, stream)))
+    return out, idx, scores
 
 
 def dsa_topk(scores, index_topk: int, start_pos: int, ratio: int, offset: int, out=None, col: int = 0,
@@ -470,15 +551,24 @@ def dsa_sparse_attn_step_noalloc(q_idx, k_idx, w, q, kv_win, kv_comp, sink, *, i
 
 
 def sparse_attention_step(q, kv_win, kv_comp, qI, kI, w, sink, *, start_pos: int, ratio: int, W: int,
-                          index_topk: int, scale: float, w_scale: float, comp_scales=None, bufs=None,
-                          stream=None):
+                          index_topk: int, scale: float, w_scale: float, comp_scales=None, index_scales=None,
+                          bufs=None, stream=None):
     """One pass of the whole step: window rows, index scores, top-k, sparse attention.
 
+    qI/kI are bf16/fp32 index rows, or uint8 MXFP4 nibbles with index_scales = (qI_scale, kI_scale).
     Returns (o, idx, scores).  `bufs` may carry preallocated 'scores', 'idx', 'o', 'workspace'.
     """
     bufs = {} if bufs is None else bufs
     B, S = q.shape[:2]
     T = kI.shape[1]
+    if qI.dtype == torch.uint8:
+        if index_scales is None:
+            raise DsaError(-1, "MXFP4 index operands need index_scales=(qI_scale, kI_scale)")
+        return dsa_sparse_attn_step_mxfp4(qI, index_scales[0], kI, index_scales[1], w, q, kv_win, kv_comp, sink,
+                                          index_topk=index_topk, start_pos=start_pos, ratio=ratio, W=W, scale=scale,
+                                          w_scale=w_scale, comp_scales=comp_scales, out=bufs.get("o"),
+                                          scores=bufs.get("scores"), idx=bufs.get("idx"),
+                                          workspace=bufs.get("workspace"), stream=stream)
     Wc = dsa_window_cols(S, start_pos, W)
     K = min(index_topk, T)
     idx = bufs.get("idx")
@@ -505,6 +595,8 @@ __all__ = [
     "dsa_topk_plan",
     "DsaKvSrc",
     "dsa_index_scores",
+    "dsa_index_scores_mxfp4",
+    "dsa_sparse_attn_step_mxfp4",
     "dsa_topk",
     "dsa_select",
     "dsa_window_cols",

@@ -10,7 +10,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
-SOURCES = ["abi.cpp", "index_scores.hip", "index_scores_prefill.hip", "topk.hip", "sparse_attn.hip", "sparse_attn_decode.hip",
+SOURCES = ["abi.cpp", "index_scores.hip", "index_scores_prefill.hip", "index_scores_mxfp4.hip", "topk.hip", "sparse_attn.hip", "sparse_attn_decode.hip",
            "sparse_attn_prefill_h16.hip", "sparse_attn_f32.hip", "noalloc.hip"]
 ARCH = "gfx950"
 # packed fp32 VALU forms are kept out of the generated code

@@ -119,6 +119,8 @@ static int debug_check_idx(const int32_t* idx, int64_t count, int64_t n_rows, hi
 int index_scores_launch(const void*, const void*, int64_t, const void*, float, int, int, int, int, int, int, int, int,
                         float*, hipStream_t);
 int topk_launch(const float*, int, int, int, int, int, int, int, int32_t*, int64_t, int, int, hipStream_t);
+int index_scores_mxfp4_launch(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, int64_t, const void*,
+                              float, int, int, int, int, int, int, int, float*, hipStream_t);
 void topk_plan(int, int, int, int64_t*, int64_t*);
 int window_idx_launch(int, int, int, int, int, int32_t*, int64_t, hipStream_t);
 int sparse_attn_bf16_launch(const void*, const dsa_kv_src*, const dsa_kv_src*, const float*, const int32_t*, int,
@@ -211,6 +213,29 @@ int dsa_index_scores(const void* q_idx, const void* k_idx, int64_t k_batch_strid
     return fail(DSA_ERR_SHAPE, "dsa_index_scores: k_batch_stride must be a multiple of 8 elements");
   return dsa::index_scores_launch(q_idx, k_idx, k_batch_stride, w, w_scale, dtype, B, S, T, H_I, D_I, start_pos,
                                   ratio, scores, (hipStream_t)stream);
+}
+
+int dsa_index_scores_mxfp4(const uint8_t* q_idx, const uint8_t* q_scale, const uint8_t* k_idx,
+                           const uint8_t* k_scale, int64_t k_batch_rows, const void* w, float w_scale, int B, int S,
+                           int T, int H_I, int D_I, int start_pos, int ratio, float* scores, dsa_stream_t stream) {
+  dsa::Entry entry_;
+  if (B < 0 || S < 0 || T < 0 || H_I <= 0 || D_I <= 0 || start_pos < 0 || ratio <= 0)
+    return fail(DSA_ERR_SHAPE, "dsa_index_scores_mxfp4: bad sizes B=%d S=%d T=%d H_I=%d D_I=%d start_pos=%d ratio=%d",
+                B, S, T, H_I, D_I, start_pos, ratio);
+  if ((int64_t)T > ((int64_t)start_pos + S) / ratio)
+    return fail(DSA_ERR_SHAPE, "dsa_index_scores_mxfp4: T=%d exceeds (start_pos+S)/ratio=%lld", T,
+                (long long)(((int64_t)start_pos + S) / ratio));
+  if (H_I > 64) return fail(DSA_ERR_UNSUPPORTED, "dsa_index_scores_mxfp4: H_I=%d > 64", H_I);
+  if (D_I != 64 && D_I != 128 && D_I != 256)
+    return fail(DSA_ERR_UNSUPPORTED, "dsa_index_scores_mxfp4: D_I=%d not in {64, 128, 256}", D_I);
+  if (B == 0 || S == 0 || T == 0) return DSA_OK;
+  if (!q_idx || !q_scale || !k_idx || !k_scale || !w || !scores)
+    return fail(DSA_ERR_NULL, "dsa_index_scores_mxfp4: NULL tensor pointer");
+  if (k_batch_rows < T) return fail(DSA_ERR_SHAPE, "dsa_index_scores_mxfp4: k_batch_rows %lld < T", (long long)k_batch_rows);
+  if (((uintptr_t)q_idx | (uintptr_t)k_idx) & 15)
+    return fail(DSA_ERR_SHAPE, "dsa_index_scores_mxfp4: q_idx and k_idx must be 16-byte aligned");
+  return dsa::index_scores_mxfp4_launch(q_idx, q_scale, k_idx, k_scale, k_batch_rows, w, w_scale, B, S, T, H_I, D_I,
+                                        start_pos, ratio, scores, (hipStream_t)stream);
 }
 
 int dsa_topk(const float* scores, int B, int S, int T, int index_topk, int start_pos, int ratio, int offset,
@@ -451,6 +476,29 @@ int dsa_sparse_attn_step_noalloc(const void* q_idx, const void* k_idx, int64_t k
                 need, have);
   return dsa_sparse_attn_step(q_idx, k_idx, k_batch_stride, w, w_scale, H_I, D_I, T, index_topk, start_pos, ratio, W,
                               q, win, comp, sink, scale, o, dtype, B, S, H, D, scores, idx, ds.scratch, have, stream);
+}
+
+int dsa_sparse_attn_step_mxfp4(const uint8_t* q_idx, const uint8_t* q_scale, const uint8_t* k_idx,
+                               const uint8_t* k_scale, int64_t k_batch_rows, const void* w, float w_scale, int H_I,
+                               int D_I, int T, int index_topk, int start_pos, int ratio, int W, const void* q,
+                               const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink, float scale,
+                               void* o, int dtype, int B, int S, int H, int D, float* scores, int32_t* idx,
+                               void* workspace, size_t workspace_bytes, dsa_stream_t stream) {
+  dsa::Entry entry_;
+  if (dtype != DSA_BF16) return fail(DSA_ERR_DTYPE, "dsa_sparse_attn_step_mxfp4: the attention dtype must be bf16");
+  if (!win) return fail(DSA_ERR_NULL, "dsa_sparse_attn_step_mxfp4: window source missing");
+  const int Wc = dsa_window_cols(S, start_pos, W);
+  if (Wc < 0) return Wc;
+  // validate the attention half before anything is launched
+  if (B < 0 || S < 0 || T < 0 || index_topk < 0 || start_pos < 0 || ratio <= 0)
+    return fail(DSA_ERR_SHAPE, "dsa_sparse_attn_step_mxfp4: bad sizes B=%d S=%d T=%d index_topk=%d", B, S, T,
+                index_topk);
+  if (B == 0 || S == 0) return DSA_OK;
+  int rc = dsa_index_scores_mxfp4(q_idx, q_scale, k_idx, k_scale, k_batch_rows, w, w_scale, B, S, T, H_I, D_I,
+                                  start_pos, ratio, scores, stream);
+  if (rc) return rc;
+  return dsa_sparse_attn_select(scores, T, index_topk, start_pos, ratio, W, q, win, comp, sink, scale, o, dtype, B, S,
+                                H, D, idx, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -270,10 +270,21 @@ def test_sparse_attn(B, S, H, D, nw, nc, L, dtype, fp4):
 # ------------------------------------------------------------------------ whole step per workload
 def _step(w, dev_in, bufs=None):
     dsa = _dsa()
+    mx = "qI_fp4" in dev_in
     return dsa.sparse_attention_step(
-        dev_in["q"], dev_in["kv_win"], dev_in.get("kv_comp", dev_in.get("kv_comp_fp4")), dev_in["qI"], dev_in["kI"],
+        dev_in["q"], dev_in["kv_win"], dev_in.get("kv_comp", dev_in.get("kv_comp_fp4")),
+        dev_in["qI_fp4"] if mx else dev_in["qI"], dev_in["kI_fp4"] if mx else dev_in["kI"],
         dev_in["w"], dev_in["sink"], start_pos=w.start_pos, ratio=w.ratio, W=w.W, index_topk=w.index_topk,
-        scale=w.D ** -0.5, w_scale=w.D_I ** -0.5 * w.H_I ** -0.5, comp_scales=dev_in.get("kv_comp_scale"), bufs=bufs)
+        scale=w.D ** -0.5, w_scale=w.D_I ** -0.5 * w.H_I ** -0.5, comp_scales=dev_in.get("kv_comp_scale"),
+        index_scales=(dev_in["qI_scale"], dev_in["kI_scale"]) if mx else None, bufs=bufs)
+
+
+def _index_f64(cpu_in):
+    """Index queries and keys as float64 arrays (the MXFP4 ones decoded by the oracle)."""
+    if "qI_fp4" in cpu_in:
+        return (oracle.mxfp4_rows_decode(cpu_in["qI_fp4"], cpu_in["qI_scale"]),
+                oracle.mxfp4_rows_decode(cpu_in["kI_fp4"], cpu_in["kI_scale"]))
+    return (cpu_in["qI"].float().numpy().astype(np.float64), cpu_in["kI"].float().numpy().astype(np.float64))
 
 
 def _check_step(w, cpu_in, o, idx, scores, rows):
@@ -284,8 +295,7 @@ def _check_step(w, cpu_in, o, idx, scores, rows):
     sc = scores.cpu() if scores is not None else None
     for (b, t) in rows:
         got_scores[(b, t)] = sc[b, t].numpy() if sc is not None else None
-    q64 = cpu_in["qI"].float().numpy().astype(np.float64)
-    k64 = cpu_in["kI"].float().numpy().astype(np.float64)
+    q64, k64 = _index_f64(cpu_in)
     w64 = cpu_in["w"].float().numpy().astype(np.float64)
     exp_rows = oracle.index_scores_rows(q64, k64, w64, w_scale, w.start_pos, w.ratio, rows)
     idx_cpu = idx.cpu().numpy()
@@ -614,7 +624,8 @@ def test_nan_in_q_propagates(B, S, nw, nc, L):
 
 # ------------------------------------------------------------------------ the page config's ratios (2 and 1)
 def _device_set_to_cpu(w, dev_in):
-    need = {"q", "kv_win", "kv_comp", "kv_comp_fp4", "kv_comp_scale", "kI", "sink", "qI", "w"}
+    need = {"q", "kv_win", "kv_comp", "kv_comp_fp4", "kv_comp_scale", "kI", "sink", "qI", "w", "qI_fp4", "qI_scale",
+            "kI_fp4", "kI_scale"}
     return {k: v.cpu() for k, v in dev_in.items() if k in need}
 
 
@@ -650,3 +661,69 @@ def test_step_real_ratio_prefill_sampled(name):
     cpu_in = _device_set_to_cpu(w, dev_in)
     rows = sample_rows(w, n_random=12)
     _check_step(w, cpu_in, o, idx, scores, rows)
+
+
+# ------------------------------------------------------------------------ MXFP4 indexer (fp4 q/k, E8M0 per 32)
+@pytest.mark.parametrize("B,S,sp,T,H,DI,ratio", [
+    (3, 1, 1234, 308, 32, 128, 4),    # decode, ragged 256-row block
+    (2, 1, 8191, 2048, 64, 128, 4),   # decode, two MFMA tiles of heads
+    (2, 70, 0, 35, 32, 128, 2),       # prefill, several 16-query blocks
+    (1, 300, 0, 300, 4, 64, 1),       # few heads (padded to a tile), index head dim 64
+    (2, 33, 0, 16, 48, 256, 2),       # index head dim 256
+    (1, 130, 5, 1, 32, 128, 4),       # a single compressed row
+    (1, 520, 0, 260, 40, 128, 2),
+])
+def test_index_scores_mxfp4(B, S, sp, T, H, DI, ratio):
+    """Scores from packed fp4 index rows with E8M0 block scales against the oracle's decode and
+    score definition, within the fp32 accumulation bound; keys passed as a slice of a larger cache."""
+    dsa = _dsa()
+    _log(f"index_scores_mxfp4 case B={B} S={S} sp={sp} T={T} H={H} DI={DI} r={ratio}")
+    g = torch.Generator().manual_seed(S * 11 + T + DI)
+    # per-row magnitudes spread over several binades, so the blocks take different scales
+    qx = torch.randn(B, S, H, DI, generator=g) * torch.exp2(torch.randint(-3, 4, (B, S, H, 1), generator=g).float())
+    kx = torch.randn(B, T + 5, DI, generator=g) * torch.exp2(torch.randint(-3, 4, (B, T + 5, 1), generator=g).float())
+    qp, qs = dsa_synth.encode_mxfp4_e8m0(qx, 32)
+    kp, ks = dsa_synth.encode_mxfp4_e8m0(kx, 32)
+    w = (torch.randn(B, S, H, generator=g) * 0.5).to(torch.bfloat16)
+    w_scale = DI ** -0.5 * H ** -0.5
+    kp_d, ks_d = kp.to(DEV), ks.to(DEV)
+    got = dsa.dsa_index_scores_mxfp4(qp.to(DEV), qs.to(DEV), kp_d[:, :T], ks_d[:, :T], w.to(DEV), w_scale, sp,
+                                     ratio).cpu().numpy()
+    n, names = _launched()
+    assert names == "index_scores_mxfp4", names
+    q64 = oracle.mxfp4_rows_decode(qp, qs)
+    k64 = oracle.mxfp4_rows_decode(kp[:, :T], ks[:, :T])
+    w64 = w.float().numpy().astype(np.float64)
+    exp = oracle.index_scores(q64, k64, w64, w_scale, sp, ratio)
+    worst = 0.0
+    for b in range(B):
+        for t in range(S):
+            e = exp[b, t]
+            inv = np.isinf(e)
+            assert np.all(np.isneginf(got[b, t][inv]))
+            bound = score_bound(q64[b, t][None], k64[b], w64[b, t][None], w_scale)[0]
+            err = np.abs(got[b, t][~inv] - e[~inv])
+            lim = 1e-5 * bound[~inv] + 1e-30
+            assert np.all(err <= lim), f"({b},{t}): score error {err.max():.3e} above the fp32 bound"
+            if err.size:
+                worst = max(worst, float((err / lim).max()))
+    _log(f"  worst error / bound {worst:.3f}")
+
+
+@pytest.mark.parametrize("name,full", [("decode_b32_ctx8k_mxfp4", True), ("decode_b16_ctx64k_mxfp4", True),
+                                       ("decode_b16_ctx64k_r1_mxfp4", True), ("prefill_s8k_mxfp4", False)])
+def test_step_mxfp4(name, full):
+    """The whole step with the MXFP4 indexer at full size: every decode query, sampled prefill
+    queries (scores, index rows by the parity rules, attention)."""
+    w = dsa_synth.get(name)
+    _log(f"step {name} ({'full check' if full else 'sampled'}, T={w.T})")
+    dev_in = dsa_synth.generate(w, seed=0, device=DEV)
+    o, idx, scores = _step(w, dev_in)
+    n, names = _launched()
+    _log(f"  launches: {n} {names}")
+    assert names.startswith("index_scores_mxfp4+"), names
+    torch.cuda.synchronize()
+    cpu_in = _device_set_to_cpu(w, dev_in)
+    rows = [(b, t) for b in range(w.B) for t in range(w.S)] if full else sample_rows(w, n_random=12)
+    _check_step(w, cpu_in, o, idx, scores, rows)
+    assert _dsa().dsa_device_errors() == 0
