@@ -44,12 +44,15 @@ PEAK_BF16_TFLOPS = 2500.0
 ROTATE_BYTES = 768 << 20  # rotate input sets until they span more than the Infinity Cache (256 MB)
 HEADLINE = "prefill_s32k_fp4"  # the largest workload
 LINE_WORKLOADS = ["decode_b32_ctx8k", "prefill_s8k", "decode_b16_ctx64k", "prefill_s32k_fp4",
-                  "decode_b16_ctx64k_r2", "decode_b16_ctx64k_r1", "prefill_s8k_r2", "prefill_s8k_r1"]
+                  "decode_b16_ctx64k_r2", "decode_b16_ctx64k_r1", "prefill_s8k_r2", "prefill_s8k_r1",
+                  "decode_b32_ctx8k_mxfp4", "decode_b16_ctx64k_mxfp4", "decode_b16_ctx64k_r1_mxfp4",
+                  "prefill_s8k_mxfp4"]
 # workloads also timed as a layer group: one index source layer and the layers that reuse its index
 # rows (the page's index sources sit every 4 layers from layer 20 on, all reading layer 20's
 # compressed KV), each layer with its own queries, window KV and sinks
 GROUP_LAYERS = 4
-GROUP_WORKLOADS = ["decode_b32_ctx8k", "decode_b16_ctx64k_r2", "decode_b16_ctx64k_r1", "prefill_s8k_r1"]
+GROUP_WORKLOADS = ["decode_b32_ctx8k", "decode_b16_ctx64k_r2", "decode_b16_ctx64k_r1", "prefill_s8k_r1",
+                   "decode_b16_ctx64k_r1_mxfp4"]
 HOST_CORES = 16  # the CPU share of one GPU on the benchmark machines
 # the sources each dominant kernel is compiled from: a change to any of them drops the HBM traffic
 # figure taken on the old sources
@@ -211,8 +214,13 @@ def cpu_baseline(w, cpu_in, target_s: float):
     comp = (oracle.fp4_rows_decode(cpu_in["kv_comp_fp4"], cpu_in["kv_comp_scale"]) if w.comp_fmt == "fp4"
             else cpu_in["kv_comp"])
     f64 = lambda x: x.float().numpy().astype(np.float64)  # noqa: E731
+    if "qI_fp4" in cpu_in:  # the MXFP4 indexer: the oracle decodes the packed rows
+        qI = oracle.mxfp4_rows_decode(cpu_in["qI_fp4"], cpu_in["qI_scale"])
+        kI = oracle.mxfp4_rows_decode(cpu_in["kI_fp4"], cpu_in["kI_scale"])
+    else:
+        qI, kI = f64(cpu_in["qI"]), f64(cpu_in["kI"])
     _ORACLE_JOB.update(w=w, kv=oracle.kv_concat(cpu_in["kv_win"], comp), win=oracle.window_rows(w.W, 1, w.S,
-                       w.start_pos)[0], sink=f64(cpu_in["sink"]), qI=f64(cpu_in["qI"]), kI=f64(cpu_in["kI"]),
+                       w.start_pos)[0], sink=f64(cpu_in["sink"]), qI=qI, kI=kI,
                        wt=f64(cpu_in["w"]), q=cpu_in["q"], w_scale=w.D_I ** -0.5 * w.H_I ** -0.5)
     rng = np.random.default_rng(0)
     order = [(b, t) for b in range(w.B) for t in range(w.S)]
@@ -261,7 +269,7 @@ def run_workload(w, a, log):
     dcode = 1 if w.dtype == "bf16" else 0
     bufs = []
     for s in sets:
-        ws = dsa.dsa_sparse_attn_workspace_size(dcode, w.B, w.S, w.H, w.D, w.L)
+        ws = dsa.dsa_step_workspace_size(dcode, w.B, w.S, w.H, w.D, w.T, w.index_topk, w.start_pos, w.W)
         bufs.append({"idx": torch.empty(w.B, w.S, Wc + w.K, dtype=torch.int32, device=dev),
                      "scores": torch.empty(w.B, w.S, w.T, dtype=torch.float32, device=dev),
                      "o": torch.empty_like(s["q"]),
@@ -269,12 +277,26 @@ def run_workload(w, a, log):
     stream = torch.cuda.current_stream(dev)
     comp_key = "kv_comp_fp4" if w.comp_fmt == "fp4" else "kv_comp"
 
+    mx = w.index_fmt == "mxfp4"
+
     def step(i):
         s, bf = sets[i % n_sets], bufs[i % n_sets]
-        dsa.dsa_sparse_attn_step(s["qI"], s["kI"], s["w"], s["q"], s["kv_win"], s[comp_key], s["sink"],
-                                 index_topk=w.index_topk, start_pos=w.start_pos, ratio=w.ratio, W=w.W, scale=scale,
-                                 w_scale=w_scale, comp_scales=s.get("kv_comp_scale"), out=bf["o"],
-                                 scores=bf["scores"], idx=bf["idx"], workspace=bf["workspace"])
+        kw = dict(index_topk=w.index_topk, start_pos=w.start_pos, ratio=w.ratio, W=w.W, scale=scale, w_scale=w_scale,
+                  comp_scales=s.get("kv_comp_scale"), out=bf["o"], scores=bf["scores"], idx=bf["idx"],
+                  workspace=bf["workspace"])
+        if mx:
+            dsa.dsa_sparse_attn_step_mxfp4(s["qI_fp4"], s["qI_scale"], s["kI_fp4"], s["kI_scale"], s["w"], s["q"],
+                                           s["kv_win"], s[comp_key], s["sink"], **kw)
+        else:
+            dsa.dsa_sparse_attn_step(s["qI"], s["kI"], s["w"], s["q"], s["kv_win"], s[comp_key], s["sink"], **kw)
+
+    def index(i):
+        s, bf = sets[i % n_sets], bufs[i % n_sets]
+        if mx:
+            dsa.dsa_index_scores_mxfp4(s["qI_fp4"], s["qI_scale"], s["kI_fp4"], s["kI_scale"], s["w"], w_scale,
+                                       w.start_pos, w.ratio, out=bf["scores"])
+        else:
+            dsa.dsa_index_scores(s["qI"], s["kI"], s["w"], w_scale, w.start_pos, w.ratio, out=bf["scores"])
 
     def attn(i):
         s, bf = sets[i % n_sets], bufs[i % n_sets]
@@ -283,8 +305,9 @@ def run_workload(w, a, log):
 
     def rest(i):
         s, bf = sets[i % n_sets], bufs[i % n_sets]
-        dsa.dsa_index_scores(s["qI"], s["kI"], s["w"], w_scale, w.start_pos, w.ratio, out=bf["scores"])
-        dsa.dsa_select(bf["scores"], w.index_topk, w.start_pos, w.ratio, w.W, w.n_win, out=bf["idx"])
+        index(i)
+        dsa.dsa_select(bf["scores"], w.index_topk, w.start_pos, w.ratio, w.W, w.n_win, out=bf["idx"],
+                       workspace=bf["workspace"])
 
     # eager warmup (initialises every set) and the library's own record of what a step launches
     for i in range(max(n_sets, min(a.warmup, 2 * n_sets))):
@@ -346,9 +369,10 @@ def run_workload(w, a, log):
     torch.cuda.synchronize()
     med_ms = statistics.median(evs[i].elapsed_time(evs[i + 1]) for i in range(R))
     del singles
-    rest_ms = None
+    rest_ms = index_ms = None
     if not fused:
         rest_ms = _graph_time_ms(lambda: rest(0), reps=2, inner=20)
+        index_ms = _graph_time_ms(lambda: index(0), reps=2, inner=20)
 
     # a layer group: the step on the index source layer, then the attention of the layers that reuse
     # its index rows (own queries, window KV and sinks; the shared compressed KV)
@@ -400,7 +424,9 @@ def run_workload(w, a, log):
         row_bytes = valid * w.D * esz
     attn_bytes = 2 * q_bytes + w.B * w.S * w.L * 4 + w.H * 4 + row_bytes
     # the index part: keys once per batch, index queries and head weights, scores written and read once
-    index_bytes = (w.B * w.T * w.D_I * esz + w.B * w.S * w.H_I * (w.D_I + 1) * esz + 2 * w.B * w.S * w.T * 4)
+    # (MXFP4 index rows: D_I/2 nibble bytes + D_I/32 scale bytes each)
+    irow = (w.D_I // 2 + w.D_I // 32) if mx else w.D_I * esz
+    index_bytes = (w.B * w.T * irow + w.B * w.S * w.H_I * (irow + esz) + 2 * w.B * w.S * w.T * 4)
     attn_flops = 4.0 * w.H * w.D * valid
     index_flops = 2.0 * w.H_I * w.D_I * visible_pairs(w)
     decode = w.mode == "decode"
@@ -435,11 +461,17 @@ def run_workload(w, a, log):
         "roofline": roof,
         "step_roofline": step_roof,
         "rest_of_step_us": None if rest_ms is None else round(rest_ms * 1e3, 2),
+        "index_kernel": None if index_ms is None else {
+            "us": round(index_ms * 1e3, 2), "algorithmic_bytes": w.B * w.T * irow + w.B * w.S * w.H_I * (irow + esz)
+            + w.B * w.S * w.T * 4, "achieved_gbs": round((w.B * w.T * irow + w.B * w.S * w.H_I * (irow + esz)
+                                                          + w.B * w.S * w.T * 4) / (index_ms * 1e-3) / 1e9, 1),
+            "index_rows": "mxfp4 e2m1 + E8M0/32" if mx else w.dtype},
         "layer_group": group,
         "config": {"workload": w.name, "mode": w.mode, "batch": w.B, "query_tokens": w.S, "context": w.end_pos,
                    "heads": w.H, "head_dim": w.D, "window": w.W, "compress_ratio": w.ratio, "index_heads": w.H_I,
                    "index_head_dim": w.D_I, "index_topk": w.index_topk,
                    "compressed_kv": "fp4 e2m1 + E4M3/16" if w.comp_fmt == "fp4" else w.dtype,
+                   "index_rows": "mxfp4 e2m1 + E8M0/32" if mx else w.dtype,
                    "input_sets_rotated": n_sets, "kernel_src_sha": sha},
     }
     log(f"[bench] {w.name}: step {ms_per_step * 1e3:.2f} us (wall {wall / a.steps * 1e6:.2f} us), {n_launch} "

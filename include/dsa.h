@@ -185,10 +185,20 @@ int dsa_index_scores_mxfp4(const uint8_t* q_idx, const uint8_t* q_scale, const u
  *   idx    int32, row (b,t) starts at idx + (b*S + t) * ld_idx; K entries are written,
  *          so a [B, S, Wc + K] buffer is filled at its tail by passing idx + Wc, ld_idx = Wc + K.
  *
- * Supported: T <= 32768.  NaN scores are outside the contract.
+ *   workspace: device memory of dsa_topk_workspace_size(B, S, T, index_topk) bytes (zero-filled
+ *          header as for every workspace; may be NULL when that size is 0).  With it, rows of few
+ *          queries and more than 4096 scores are selected in two launches over 4096-score chunks
+ *          (the chunks' best K as candidates, then the best K of those); without it (NULL), by one
+ *          workgroup per row.  Both give the same result.
+ *
+ * Supported: T <= 65536.  NaN scores are outside the contract.
  */
 int dsa_topk(const float* scores, int B, int S, int T, int index_topk, int start_pos, int ratio,
-             int offset, int32_t* idx, int64_t ld_idx, dsa_stream_t stream);
+             int offset, int32_t* idx, int64_t ld_idx, void* workspace, size_t workspace_bytes,
+             dsa_stream_t stream);
+
+/* Bytes of workspace dsa_topk and dsa_select use for this shape (0 when none). */
+size_t dsa_topk_workspace_size(int B, int S, int T, int index_topk);
 
 /*
  * How dsa_topk and dsa_select share the B*S rows between their two kernels: the first *wave_rows
@@ -225,11 +235,13 @@ int dsa_window_cols(int S, int start_pos, int W);
  *
  *   scores [B, S, T] float32 (may be NULL when T == 0)
  *   idx    int32, row (b,t) starts at idx + (b*S + t) * ld_idx, ld_idx >= Wc + K.
+ *   workspace: as for dsa_topk.
  *
  * Errors: those of dsa_window_idx and dsa_topk.
  */
 int dsa_select(const float* scores, int B, int S, int T, int index_topk, int start_pos, int ratio, int W,
-               int offset, int32_t* idx, int64_t ld_idx, dsa_stream_t stream);
+               int offset, int32_t* idx, int64_t ld_idx, void* workspace, size_t workspace_bytes,
+               dsa_stream_t stream);
 
 /*
  * One KV source of sparse attention.  Rows are D elements of the call's dtype
@@ -282,11 +294,17 @@ int dsa_sparse_attn(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp
    DSA_WORKSPACE_HEADER_BYTES). */
 size_t dsa_sparse_attn_workspace_size(int dtype, int B, int S, int H, int D, int L);
 
+/* Bytes of workspace dsa_sparse_attn_select, dsa_sparse_attn_step and dsa_sparse_attn_step_mxfp4
+   need: enough for the index-row selection and for the attention over rows of
+   L = dsa_window_cols(S, start_pos, W) + min(index_topk, T) entries (0 when none). */
+size_t dsa_step_workspace_size(int dtype, int B, int S, int H, int D, int T, int index_topk, int start_pos,
+                               int W);
+
 /*
  * The index rows and the attention over them (`Indexer.forward`, `get_window_topk_idxs` and
  * `sparse_attn` as `Attention.forward` chains them): the same results as
  *
- *   dsa_select(scores, B, S, T, index_topk, start_pos, ratio, W, win->n_rows, idx, L, stream)
+ *   dsa_select(scores, B, S, T, index_topk, start_pos, ratio, W, win->n_rows, idx, L, workspace, ...)
  *   dsa_sparse_attn(q, win, comp, sink, idx, L, scale, o, dtype, B, S, H, D, workspace, ...)
  *
  * with L = dsa_window_cols(S, start_pos, W) + min(index_topk, T).  For decode batches that the
@@ -297,7 +315,7 @@ size_t dsa_sparse_attn_workspace_size(int dtype, int B, int S, int H, int D, int
  * tells which happened.
  *
  *   scores [B, S, T] float32; q, win, comp, sink, o, workspace as for dsa_sparse_attn, with the
- *   workspace sized by dsa_sparse_attn_workspace_size(dtype, B, S, H, D, L).
+ *   workspace sized by dsa_step_workspace_size(dtype, B, S, H, D, T, index_topk, start_pos, W).
  *   idx    [B, S, L] int32, contiguous: receives the index rows.  It may be NULL when the one-launch
  *          path applies (the rows are then not written out); DSA_ERR_NULL when it does not.
  *
@@ -364,7 +382,7 @@ int dsa_sparse_attn_step_mxfp4(const uint8_t* q_idx, const uint8_t* q_scale, con
  *
  *  - dsa_init(device) must have run on the current device (DSA_ERR_STATE otherwise); it looks up
  *    the array's device address.
- *  - Shapes whose dsa_sparse_attn_workspace_size exceeds the array are refused with
+ *  - Shapes whose dsa_step_workspace_size exceeds the array are refused with
  *    DSA_ERR_WORKSPACE before anything is launched (decode batches of up to 32 queries with
  *    H = 64, D = 512 and L <= 768 fit; prefill batches of 256 or more queries at D = 512 need no
  *    scratch).

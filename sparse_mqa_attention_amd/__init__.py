@@ -81,10 +81,14 @@ def _load():
                                                ctypes.POINTER(DsaKvSrc), ctypes.POINTER(DsaKvSrc), vp, f32, vp, i32,
                                                i32, i32, i32, i32, vp, vp, vp, ctypes.c_size_t, vp]
     lib.dsa_sparse_attn_step_mxfp4.restype = i32
-    lib.dsa_topk.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, i64, vp]
+    lib.dsa_topk.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, i64, vp, ctypes.c_size_t, vp]
     lib.dsa_topk.restype = i32
-    lib.dsa_select.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, i64, vp]
+    lib.dsa_topk_workspace_size.argtypes = [i32, i32, i32, i32]
+    lib.dsa_topk_workspace_size.restype = ctypes.c_size_t
+    lib.dsa_select.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, i32, vp, i64, vp, ctypes.c_size_t, vp]
     lib.dsa_select.restype = i32
+    lib.dsa_step_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, i32]
+    lib.dsa_step_workspace_size.restype = ctypes.c_size_t
     lib.dsa_window_idx.argtypes = [i32, i32, i32, i32, vp, i64, vp]
     lib.dsa_window_idx.restype = i32
     lib.dsa_window_cols.argtypes = [i32, i32, i32]
@@ -314,7 +318,7 @@ def dsa_sparse_attn_step_mxfp4(qI, qI_scale, kI, kI_scale, w, q, kv_win, kv_comp
         scores = torch.empty(B, S, T, dtype=torch.float32, device=dev)
     if idx is None:
         idx = torch.empty(B, S, L, dtype=torch.int32, device=dev)
-    need = dsa_sparse_attn_workspace_size(dt, B, S, H, D, L)
+    need = dsa_step_workspace_size(dt, B, S, H, D, T, index_topk, start_pos, W)
     workspace = _workspace(need, workspace, dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.dsa_sparse_attn_step_mxfp4(_ptr(qI), _ptr(qI_scale), _ptr(kI), _ptr(kI_scale), rows, _ptr(w),
@@ -325,8 +329,21 @@ def dsa_sparse_attn_step_mxfp4(qI, qI_scale, kI, kI_scale, w, q, kv_win, kv_comp
     return out, idx, scores
 
 
+def dsa_topk_workspace_size(B: int, S: int, T: int, index_topk: int) -> int:
+    return int(lib.dsa_topk_workspace_size(int(B), int(S), int(T), int(index_topk)))
+
+
+def dsa_step_workspace_size(dtype_code: int, B: int, S: int, H: int, D: int, T: int, index_topk: int,
+                            start_pos: int, W: int) -> int:
+    return int(lib.dsa_step_workspace_size(dtype_code, B, S, H, D, T, int(index_topk), int(start_pos), int(W)))
+
+
+def _wbytes(workspace):
+    return 0 if workspace is None else workspace.numel() * workspace.element_size()
+
+
 def dsa_topk(scores, index_topk: int, start_pos: int, ratio: int, offset: int, out=None, col: int = 0,
-             stream=None):
+             workspace=None, stream=None):
     """Top-k index rows; writes K = min(index_topk, T) columns of `out` [B,S,>=col+K] from `col` on."""
     dev = _dev(scores)
     _need_contig("scores", scores)
@@ -340,8 +357,9 @@ def dsa_topk(scores, index_topk: int, start_pos: int, ratio: int, offset: int, o
     if out.dtype != torch.int32 or tuple(out.shape[:2]) != (B, S) or out.shape[-1] < col + K:
         raise DsaError(-2, "idx must be int32 with room for the top-k columns")
     base = ctypes.c_void_p(out.data_ptr() + 4 * col)
+    workspace = _workspace(dsa_topk_workspace_size(B, S, T, index_topk), workspace, dev)
     _check(lib.dsa_topk(_ptr(scores), B, S, T, int(index_topk), int(start_pos), int(ratio), int(offset), base,
-                        out.shape[-1], _stream(dev, stream)))
+                        out.shape[-1], _ptr(workspace), _wbytes(workspace), _stream(dev, stream)))
     return out
 
 
@@ -363,7 +381,8 @@ def dsa_window_idx(out, start_pos: int, W: int, stream=None):
     return out
 
 
-def dsa_select(scores, index_topk: int, start_pos: int, ratio: int, W: int, offset: int, out=None, stream=None):
+def dsa_select(scores, index_topk: int, start_pos: int, ratio: int, W: int, offset: int, out=None, workspace=None,
+               stream=None):
     """Whole index rows [B, S, Wc + K]: window columns, then the top-k columns (one launch)."""
     B, S, T = scores.shape
     dev = _dev(scores)
@@ -377,8 +396,9 @@ def dsa_select(scores, index_topk: int, start_pos: int, ratio: int, W: int, offs
     _need_contig("idx", out)
     if out.dtype != torch.int32 or tuple(out.shape[:2]) != (B, S) or out.shape[-1] < Wc + K:
         raise DsaError(-2, "idx must be int32 with room for the window and top-k columns")
+    workspace = _workspace(dsa_topk_workspace_size(B, S, T, index_topk), workspace, dev)
     _check(lib.dsa_select(_ptr(scores), B, S, T, int(index_topk), int(start_pos), int(ratio), int(W), int(offset),
-                          _ptr(out), out.shape[-1], _stream(dev, stream)))
+                          _ptr(out), out.shape[-1], _ptr(workspace), _wbytes(workspace), _stream(dev, stream)))
     return out
 
 
@@ -473,7 +493,7 @@ def dsa_sparse_attn_select(scores, q, kv_win, kv_comp, sink, *, index_topk: int,
     _need_contig("idx", idx)
     if idx.dtype != torch.int32 or tuple(idx.shape) != (B, S, L):
         raise DsaError(-2, "idx must be int32 [B, S, L] with L = window columns + top-k columns")
-    need = dsa_sparse_attn_workspace_size(dt, B, S, H, D, L)
+    need = dsa_step_workspace_size(dt, B, S, H, D, T, index_topk, start_pos, W)
     workspace = _workspace(need, workspace, dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.dsa_sparse_attn_select(_ptr(scores), T, int(index_topk), int(start_pos), int(ratio), int(W), _ptr(q),
@@ -513,7 +533,7 @@ def dsa_sparse_attn_step(q_idx, k_idx, w, q, kv_win, kv_comp, sink, *, index_top
     _need_contig("idx", idx)
     if idx.dtype != torch.int32 or tuple(idx.shape) != (B, S, L):
         raise DsaError(-2, "idx must be int32 [B, S, L] with L = window columns + top-k columns")
-    need = dsa_sparse_attn_workspace_size(dt, B, S, H, D, L)
+    need = dsa_step_workspace_size(dt, B, S, H, D, T, index_topk, start_pos, W)
     workspace = _workspace(need, workspace, dev)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.dsa_sparse_attn_step(_ptr(q_idx), _ptr(k_idx), kbs, _ptr(w), float(w_scale), H_I, D_I, T,
@@ -606,6 +626,8 @@ __all__ = [
     "dsa_sparse_attn_step",
     "dsa_sparse_attn_step_noalloc",
     "dsa_sparse_attn_workspace_size",
+    "dsa_topk_workspace_size",
+    "dsa_step_workspace_size",
     "kv_src",
     "sparse_attention_step",
     "lib",

@@ -118,7 +118,8 @@ static int debug_check_idx(const int32_t* idx, int64_t count, int64_t n_rows, hi
 
 int index_scores_launch(const void*, const void*, int64_t, const void*, float, int, int, int, int, int, int, int, int,
                         float*, hipStream_t);
-int topk_launch(const float*, int, int, int, int, int, int, int, int32_t*, int64_t, int, int, hipStream_t);
+int topk_launch(const float*, int, int, int, int, int, int, int, int32_t*, int64_t, int, int, void*, hipStream_t);
+size_t topk_split_bytes(int, int, int, int);
 int index_scores_mxfp4_launch(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, int64_t, const void*,
                               float, int, int, int, int, int, int, int, float*, hipStream_t);
 void topk_plan(int, int, int, int64_t*, int64_t*);
@@ -238,8 +239,22 @@ int dsa_index_scores_mxfp4(const uint8_t* q_idx, const uint8_t* q_scale, const u
                                         start_pos, ratio, scores, (hipStream_t)stream);
 }
 
+size_t dsa_topk_workspace_size(int B, int S, int T, int index_topk) {
+  if (B <= 0 || S <= 0 || T <= 0 || index_topk <= 0) return 0;
+  const int K = index_topk < T ? index_topk : T;
+  const size_t p = dsa::topk_split_bytes(B, S, T, K);
+  return p ? dsa::kWsHeaderBytes + p : 0;
+}
+
+// the workspace past its header when it holds the split select's candidates, else null
+static void* topk_payload(int B, int S, int T, int K, void* workspace, size_t workspace_bytes) {
+  const size_t p = dsa::topk_split_bytes(B, S, T, K);
+  if (!p || !workspace || workspace_bytes < dsa::kWsHeaderBytes + p) return nullptr;
+  return (char*)workspace + dsa::kWsHeaderBytes;
+}
+
 int dsa_topk(const float* scores, int B, int S, int T, int index_topk, int start_pos, int ratio, int offset,
-             int32_t* idx, int64_t ld_idx, dsa_stream_t stream) {
+             int32_t* idx, int64_t ld_idx, void* workspace, size_t workspace_bytes, dsa_stream_t stream) {
   dsa::Entry entry_;
   if (B < 0 || S < 0 || T < 0 || index_topk < 0 || start_pos < 0 || ratio <= 0 || offset < 0)
     return fail(DSA_ERR_SHAPE, "dsa_topk: bad sizes B=%d S=%d T=%d index_topk=%d start_pos=%d ratio=%d offset=%d", B,
@@ -248,7 +263,8 @@ int dsa_topk(const float* scores, int B, int S, int T, int index_topk, int start
   if (ld_idx < K) return fail(DSA_ERR_SHAPE, "dsa_topk: ld_idx %lld < K=%d", (long long)ld_idx, K);
   if (B == 0 || S == 0 || K == 0) return DSA_OK;
   if (!scores || !idx) return fail(DSA_ERR_NULL, "dsa_topk: NULL pointer");
-  return dsa::topk_launch(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, 0, 0, (hipStream_t)stream);
+  return dsa::topk_launch(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, 0, 0,
+                          topk_payload(B, S, T, K, workspace, workspace_bytes), (hipStream_t)stream);
 }
 
 int dsa_window_cols(int S, int start_pos, int W) {
@@ -270,7 +286,8 @@ int dsa_window_idx(int B, int S, int start_pos, int W, int32_t* idx, int64_t ld_
 }
 
 int dsa_select(const float* scores, int B, int S, int T, int index_topk, int start_pos, int ratio, int W,
-               int offset, int32_t* idx, int64_t ld_idx, dsa_stream_t stream) {
+               int offset, int32_t* idx, int64_t ld_idx, void* workspace, size_t workspace_bytes,
+               dsa_stream_t stream) {
   dsa::Entry entry_;
   if (B < 0 || S < 0 || T < 0 || index_topk < 0 || start_pos < 0 || ratio <= 0 || offset < 0)
     return fail(DSA_ERR_SHAPE, "dsa_select: bad sizes B=%d S=%d T=%d index_topk=%d start_pos=%d ratio=%d offset=%d",
@@ -283,7 +300,8 @@ int dsa_select(const float* scores, int B, int S, int T, int index_topk, int sta
   if (B == 0 || S == 0 || Wc + K == 0) return DSA_OK;
   if (!idx || (K > 0 && !scores)) return fail(DSA_ERR_NULL, "dsa_select: NULL pointer");
   if (K == 0) return dsa::window_idx_launch(B, S, start_pos, W, Wc, idx, ld_idx, (hipStream_t)stream);
-  return dsa::topk_launch(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, (hipStream_t)stream);
+  return dsa::topk_launch(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc,
+                          topk_payload(B, S, T, K, workspace, workspace_bytes), (hipStream_t)stream);
 }
 
 size_t dsa_sparse_attn_workspace_size(int dtype, int B, int S, int H, int D, int L) {
@@ -292,6 +310,17 @@ size_t dsa_sparse_attn_workspace_size(int dtype, int B, int S, int H, int D, int
   const size_t a = dsa::sparse_attn_bf16_workspace(B, S, H, D, L, false);
   const size_t b = dsa::sparse_attn_bf16_workspace(B, S, H, D, L, true);
   return a > b ? a : b;
+}
+
+size_t dsa_step_workspace_size(int dtype, int B, int S, int H, int D, int T, int index_topk, int start_pos,
+                               int W) {
+  if (B <= 0 || S <= 0 || T < 0 || index_topk < 0) return 0;
+  const int Wc = dsa_window_cols(S, start_pos, W);
+  if (Wc < 0) return 0;
+  const int K = index_topk < T ? index_topk : T;
+  const size_t a = dsa_sparse_attn_workspace_size(dtype, B, S, H, D, Wc + K);
+  const size_t t = dsa_topk_workspace_size(B, S, T, index_topk);
+  return a > t ? a : t;
 }
 
 static int check_src(const dsa_kv_src* s, const char* name, int dtype, int D, int B, bool required) {
@@ -383,7 +412,7 @@ int dsa_sparse_attn_select(const float* scores, int T, int index_topk, int start
     if (rc) return rc;
     rc = check_src(comp, "compressed", dtype, D, B, false);
     if (rc) return rc;
-    const size_t need = dsa_sparse_attn_workspace_size(dtype, B, S, H, D, L);
+    const size_t need = dsa_step_workspace_size(dtype, B, S, H, D, T, index_topk, start_pos, W);
     if (need > 0 && (!workspace || workspace_bytes < need))
       return fail(DSA_ERR_WORKSPACE, "dsa_sparse_attn_select: workspace of %zu bytes needed, %zu given", need,
                   workspace_bytes);
@@ -396,7 +425,12 @@ int dsa_sparse_attn_select(const float* scores, int T, int index_topk, int start
   }
   // otherwise: the index rows into idx, then the attention over them
   if (!idx) return fail(DSA_ERR_NULL, "dsa_sparse_attn_select: idx needed for this shape");
-  int rc = dsa_select(scores, B, S, T, index_topk, start_pos, ratio, W, offset, idx, L, stream);
+  const size_t need = dsa_step_workspace_size(dtype, B, S, H, D, T, index_topk, start_pos, W);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "dsa_sparse_attn_select: workspace of %zu bytes needed, %zu given", need,
+                workspace_bytes);
+  int rc = dsa_select(scores, B, S, T, index_topk, start_pos, ratio, W, offset, idx, L, workspace, workspace_bytes,
+                      stream);
   if (rc) return rc;
   return dsa_sparse_attn(q, win, comp, sink, idx, L, scale, o, dtype, B, S, H, D, workspace, workspace_bytes, stream);
 }
@@ -428,7 +462,7 @@ int dsa_sparse_attn_step(const void* q_idx, const void* k_idx, int64_t k_batch_s
     if (rc) return rc;
     rc = check_src(comp, "compressed", dtype, D, B, false);
     if (rc) return rc;
-    const size_t need = dsa_sparse_attn_workspace_size(dtype, B, S, H, D, L);
+    const size_t need = dsa_step_workspace_size(dtype, B, S, H, D, T, index_topk, start_pos, W);
     if (need > 0 && (!workspace || workspace_bytes < need))
       return fail(DSA_ERR_WORKSPACE, "dsa_sparse_attn_step: workspace of %zu bytes needed, %zu given", need,
                   workspace_bytes);
@@ -441,7 +475,12 @@ int dsa_sparse_attn_step(const void* q_idx, const void* k_idx, int64_t k_batch_s
                                              (hipStream_t)stream);
     if (rc != 0) return rc < 0 ? rc : DSA_OK;
   }
-  // otherwise: the index scores, then the index rows and the attention
+  // otherwise: the index scores, then the index rows and the attention (the workspace is checked
+  // before anything is launched)
+  const size_t need = dsa_step_workspace_size(dtype, B, S, H, D, T, index_topk, start_pos, W);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "dsa_sparse_attn_step: workspace of %zu bytes needed, %zu given", need,
+                workspace_bytes);
   int rc = dsa_index_scores(q_idx, k_idx, k_batch_stride, w, w_scale, dtype, B, S, T, H_I, D_I, start_pos, ratio,
                             scores, stream);
   if (rc) return rc;
@@ -466,8 +505,7 @@ int dsa_sparse_attn_step_noalloc(const void* q_idx, const void* k_idx, int64_t k
                 index_topk);
   const int Wc = dsa_window_cols(S, start_pos, W);
   if (Wc < 0) return Wc;
-  const int K = index_topk < T ? index_topk : T;
-  const size_t need = dsa_sparse_attn_workspace_size(dtype, B, S, H, D, Wc + K);
+  const size_t need = dsa_step_workspace_size(dtype, B, S, H, D, T, index_topk, start_pos, W);
   const size_t have = dsa::scratch_bytes();
   if (need > have)
     return fail(DSA_ERR_WORKSPACE,
@@ -494,6 +532,10 @@ int dsa_sparse_attn_step_mxfp4(const uint8_t* q_idx, const uint8_t* q_scale, con
     return fail(DSA_ERR_SHAPE, "dsa_sparse_attn_step_mxfp4: bad sizes B=%d S=%d T=%d index_topk=%d", B, S, T,
                 index_topk);
   if (B == 0 || S == 0) return DSA_OK;
+  const size_t need = dsa_step_workspace_size(dtype, B, S, H, D, T, index_topk, start_pos, W);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(DSA_ERR_WORKSPACE, "dsa_sparse_attn_step_mxfp4: workspace of %zu bytes needed, %zu given", need,
+                workspace_bytes);
   int rc = dsa_index_scores_mxfp4(q_idx, q_scale, k_idx, k_scale, k_batch_rows, w, w_scale, B, S, T, H_I, D_I,
                                   start_pos, ratio, scores, stream);
   if (rc) return rc;

@@ -41,6 +41,72 @@ topk_kernel(const float* __restrict__ scores, int S, int T, int K, int start_pos
   block_topk<NT, KPT>(scores + (int64_t)row * T, T, c, K, offset, sm, [&](int slot, int v) { out[slot] = v; });
 }
 
+// Long rows of few queries (decode at long context): the select is split over the chunks of each
+// row.  Stage 1: workgroup (g, row) keeps the K best visible scores of positions
+// [g*kChunk, (g+1)*kChunk) as candidates (scores and positions, in ascending position order,
+// padded with -inf / -1 to K), or all of them when the chunk has at most K visible positions.
+// The K best of the row are among the chunks' K best (a position beaten by K others in its own
+// chunk cannot be among the row's K best), so stage 2 selects the K best of the G*K candidates;
+// chunks and each chunk's candidates are in position order, so ties between equal scores still
+// go to the lower position.
+constexpr int kChunk = 4096;  // positions per stage-1 workgroup: 256 threads x 16 keys
+
+__global__ void __launch_bounds__(256)
+topk_split_chunk_kernel(const float* __restrict__ scores, int S, int T, int K, int start_pos, int ratio, int G,
+                        float* __restrict__ cand_s, int32_t* __restrict__ cand_p) {
+  __shared__ TopkSmem<256> sm;
+  const int g = blockIdx.x;
+  const int row = blockIdx.y;  // b*S + t
+  const int tid = threadIdx.x;
+  const int c = min(T, visible_rows(start_pos, row % S, ratio));
+  if (c <= K) return;  // the merge writes such rows without candidates
+  const int p0 = g * kChunk;
+  if (p0 >= c) return;  // chunks past the visible positions hold no candidates
+  const int cg = min(kChunk, c - p0);
+  float* cs = cand_s + ((int64_t)row * G + g) * K;
+  int32_t* cp = cand_p + ((int64_t)row * G + g) * K;
+  const float* srow = scores + (int64_t)row * T + p0;
+  if (cg <= K) {
+    for (int s = tid; s < K; s += 256) {
+      cs[s] = s < cg ? srow[s] : -__builtin_inff();
+      cp[s] = s < cg ? p0 + s : -1;
+    }
+    return;
+  }
+  block_topk<256, 16>(srow, T - p0, cg, K, 0, sm, [&](int slot, int v) {
+    cs[slot] = srow[v];
+    cp[slot] = p0 + v;
+  });
+}
+
+// Stage 2: the row's window entries, then its K best candidates (their positions + offset) in
+// ascending position order; rows with at most K visible positions as in topk_kernel.
+template <int NT, int KPT>
+__global__ void __launch_bounds__(NT)
+topk_split_merge_kernel(const float* __restrict__ cand_s, const int32_t* __restrict__ cand_p, int G, int S, int T,
+                        int K, int start_pos, int ratio, int offset, int32_t* __restrict__ idx, int64_t ld_idx, int W,
+                        int Wc) {
+  __shared__ TopkSmem<NT> sm;
+  const int row = blockIdx.x;
+  const int t = row % S;
+  const int tid = threadIdx.x;
+  const int c = min(T, visible_rows(start_pos, t, ratio));
+  for (int s = tid; s < Wc; s += NT) idx[(int64_t)row * ld_idx + s] = window_entry(t, s, start_pos, W);
+  int32_t* out = idx + (int64_t)row * ld_idx + Wc;
+  if (c <= K) {
+    for (int s = tid; s < K; s += NT) out[s] = s < c ? s + offset : -1;
+    return;
+  }
+  const int n = (c + kChunk - 1) / kChunk * K;  // candidates of the chunks holding visible positions
+  const int32_t* cp = cand_p + (int64_t)row * G * K;
+  if (n <= K) {  // one chunk holds every visible position: its K candidates are the answer
+    for (int s = tid; s < K; s += NT) out[s] = cp[s] + offset;
+    return;
+  }
+  block_topk<NT, KPT>(cand_s + (int64_t)row * G * K, n, n, K, 0, sm,
+                      [&](int slot, int i) { out[slot] = cp[i] + offset; });
+}
+
 // Many rows (prefill): one wave per row and no workgroup barriers.  Lane l holds the keys of
 // positions 64g + l (g < KPL) in registers (invisible positions get key 0, below every real
 // key).  The radix select takes 8-bit digits, from the highest bit where the row's keys differ,
@@ -315,8 +381,41 @@ int launch_topk_wave(const float* scores, int B, int S, int T, int K, int sp, in
   return check_launch("topk_block");
 }
 
+// The split select applies to fewer than 1024 rows of more than 4096 scores whose G*K candidates a
+// merge workgroup can hold; returns the workspace payload it needs (0 when it does not apply).
+size_t topk_split_bytes(int B, int S, int T, int K) {
+  const int64_t rows = (int64_t)B * S;
+  if (rows <= 0 || rows >= 1024 || T <= 4096 || K <= 0) return 0;
+  const int64_t G = (T + kChunk - 1) / kChunk;
+  if (G * K > 32768) return 0;
+  return (size_t)(rows * G * K) * (sizeof(float) + sizeof(int32_t));
+}
+
+int topk_split_launch(const float* scores, int B, int S, int T, int K, int sp, int r, int off, int32_t* idx,
+                      int64_t ld, int W, int Wc, void* payload, hipStream_t st) {
+  const int rows = B * S;
+  const int G = (T + kChunk - 1) / kChunk;
+  float* cand_s = (float*)payload;
+  int32_t* cand_p = (int32_t*)(cand_s + (size_t)rows * G * K);
+  hipLaunchKernelGGL(topk_split_chunk_kernel, dim3(G, rows), dim3(256), 0, st, scores, S, T, K, sp, r, G, cand_s,
+                     cand_p);
+  int rc = check_launch("topk_split_chunk");
+  if (rc) return rc;
+  const int n = G * K;
+#define DSA_MERGE(NT_, KPT_)                                                                                      \
+  hipLaunchKernelGGL((topk_split_merge_kernel<NT_, KPT_>), dim3(rows), dim3(NT_), 0, st, cand_s, cand_p, G, S, T, K, \
+                     sp, r, off, idx, ld, W, Wc)
+  if (n <= 2048) DSA_MERGE(256, 8);
+  else if (n <= 4096) DSA_MERGE(512, 8);
+  else if (n <= 8192) DSA_MERGE(1024, 8);
+  else if (n <= 16384) DSA_MERGE(1024, 16);
+  else DSA_MERGE(1024, 32);
+#undef DSA_MERGE
+  return check_launch("topk_split_merge");
+}
+
 // Rows of a top-k call on the one-wave kernel and on the per-row workgroup kernel.
-void topk_plan(int B, int S, int T, int64_t* wave_rows, int64_t* block_rows) {
+void topk_plan(int B, int S, int T, int64_t* wave_rows, int64_t* block_rows) {  // rows without the split select
   const int64_t rows = (int64_t)B * S;
   *wave_rows = 0;
   *block_rows = rows;
@@ -325,8 +424,11 @@ void topk_plan(int B, int S, int T, int64_t* wave_rows, int64_t* block_rows) {
 }
 
 // idx points at the row base; a row gets Wc window entries (W the window) then its K top-k entries.
+// `payload` (may be null) is workspace past its header, of at least topk_split_bytes(B, S, T, K).
 int topk_launch(const float* scores, int B, int S, int T, int K, int start_pos, int ratio, int offset,
-                int32_t* idx, int64_t ld_idx, int W, int Wc, hipStream_t st) {
+                int32_t* idx, int64_t ld_idx, int W, int Wc, void* payload, hipStream_t st) {
+  if (payload && topk_split_bytes(B, S, T, K) > 0)
+    return topk_split_launch(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, payload, st);
   // many rows: one wave per row
   if ((int64_t)B * S >= 1024) {
     if (T <= 2048) return launch_topk_wave<32, 256, 8>(scores, B, S, T, K, start_pos, ratio, offset, idx, ld_idx, W, Wc, st);

@@ -28,7 +28,8 @@ def test_header_declares_the_step():
               "dsa_sparse_attn_select", "dsa_sparse_attn_step", "dsa_last_error",
               "dsa_abi_version", "dsa_sparse_attn_workspace_size", "dsa_window_cols", "dsa_init",
               "dsa_device_errors", "dsa_last_launch_count", "dsa_last_launches", "dsa_set_debug", "dsa_check_idx",
-              "dsa_topk_plan"]:
+              "dsa_topk_plan", "dsa_topk_workspace_size", "dsa_step_workspace_size", "dsa_index_scores_mxfp4",
+              "dsa_sparse_attn_step_mxfp4", "dsa_sparse_attn_step_noalloc"]:
         assert n in names
 
 
@@ -63,17 +64,17 @@ def test_argument_errors_without_launch(dsa):
     assert rc == -1
     # empty work is fine and launches nothing
     assert lib.dsa_index_scores(nul, nul, 0, nul, 1.0, 1, 0, 4, 2, 4, 32, 0, 2, nul, nul) == 0
-    assert lib.dsa_topk(nul, 1, 1, 0, 8, 0, 4, 0, nul, 8, nul) == 0
-    assert lib.dsa_topk(nul, 1, 1, 10, 8, 0, 4, 0, nul, 4, nul) == -2  # ld_idx < K
-    assert lib.dsa_topk(nul, 1, 1, 10, 8, 0, 0, 0, nul, 8, nul) == -2  # ratio 0
-    assert lib.dsa_topk(nul, 1, 1, 10, 8, 0, 4, 0, nul, 8, nul) == -1
+    assert lib.dsa_topk(nul, 1, 1, 0, 8, 0, 4, 0, nul, 8, nul, 0, nul) == 0
+    assert lib.dsa_topk(nul, 1, 1, 10, 8, 0, 4, 0, nul, 4, nul, 0, nul) == -2  # ld_idx < K
+    assert lib.dsa_topk(nul, 1, 1, 10, 8, 0, 0, 0, nul, 8, nul, 0, nul) == -2  # ratio 0
+    assert lib.dsa_topk(nul, 1, 1, 10, 8, 0, 4, 0, nul, 8, nul, 0, nul) == -1
     assert lib.dsa_window_idx(1, 2, 5, 4, nul, 4, nul) == -4
     assert lib.dsa_window_idx(1, 2, 0, 4, nul, 1, nul) == -2
     # whole index rows: ld_idx must hold the window and the top-k columns (2 + 8 here)
-    assert lib.dsa_select(nul, 1, 2, 10, 8, 0, 4, 4, 2, nul, 9, nul) == -2
-    assert lib.dsa_select(nul, 1, 2, 10, 8, 5, 4, 4, 2, nul, 10, nul) == -4  # chunked decode
-    assert lib.dsa_select(nul, 1, 2, 10, 8, 0, 4, 4, 2, nul, 10, nul) == -1
-    assert lib.dsa_select(nul, 0, 2, 10, 8, 0, 4, 4, 2, nul, 10, nul) == 0
+    assert lib.dsa_select(nul, 1, 2, 10, 8, 0, 4, 4, 2, nul, 9, nul, 0, nul) == -2
+    assert lib.dsa_select(nul, 1, 2, 10, 8, 5, 4, 4, 2, nul, 10, nul, 0, nul) == -4  # chunked decode
+    assert lib.dsa_select(nul, 1, 2, 10, 8, 0, 4, 4, 2, nul, 10, nul, 0, nul) == -1
+    assert lib.dsa_select(nul, 0, 2, 10, 8, 0, 4, 4, 2, nul, 10, nul, 0, nul) == 0
     # index rows + attention: sizes, missing window source, chunked decode, empty batch, a shape
     # that needs idx (the fp32 path always runs the two calls)
     src0 = dsa.DsaKvSrc()
@@ -247,3 +248,20 @@ def test_init_and_errors_need_a_device(dsa):
     assert dsa.lib.dsa_device_errors(0, ctypes.byref(v)) == -5
     assert dsa.lib.dsa_device_errors(0, None) == -1
     assert dsa.lib.dsa_init(-1) == -2
+
+
+def test_workspace_sizes(dsa):
+    """Long rows of few queries get the split select's candidate space; many rows (prefill) and
+    short rows none; the step's size covers both the selection and the attention."""
+    assert dsa.dsa_topk_workspace_size(16, 1, 65536, 512) == 4096 + 16 * 16 * 512 * 8
+    assert dsa.dsa_topk_workspace_size(16, 1, 16384, 512) == 4096 + 16 * 4 * 512 * 8
+    assert dsa.dsa_topk_workspace_size(32, 1, 2048, 512) == 0       # short rows: one workgroup each
+    assert dsa.dsa_topk_workspace_size(1, 8192, 8192, 512) == 0     # many rows: one wave each
+    assert dsa.dsa_topk_workspace_size(1, 1, 65536, 8192) == 0      # candidates beyond one merge
+    for args in [(1, 16, 1, 64, 512, 65536, 512, 65535, 128), (1, 32, 1, 64, 512, 2048, 512, 8191, 128),
+                 (1, 1, 8192, 64, 512, 2048, 512, 0, 128)]:
+        dt, B, S, H, D, T, K, sp, W = args
+        step = dsa.dsa_step_workspace_size(*args)
+        L = dsa.dsa_window_cols(S, sp, W) + min(K, T)
+        assert step >= dsa.dsa_sparse_attn_workspace_size(dt, B, S, H, D, L)
+        assert step >= dsa.dsa_topk_workspace_size(B, S, T, K)

@@ -83,6 +83,10 @@ def test_window_idx(B, S, sp, W):
     (2, 1, 65536, 512, 65535, 1, "normal"),
     (1, 1, 65536, 512, 65535, 1, "ties"),
     (3, 1, 40000, 512, 79999, 2, "zeros"),
+    # split select: a chunk boundary inside the visible part, K beyond a chunk's visible count
+    (4, 1, 9000, 512, 9000, 1, "ties"),
+    (2, 1, 5000, 2048, 4999, 1, "normal"),
+    (3, 2, 12000, 700, 23998, 2, "normal"),
     (1, 3, 600, 1, 1797, 3, "normal"),
     # 1024+ rows: one wave per row (2048, 4096 and 8192 keys per lane group)
     (1, 1100, 4000, 512, 0, 1, "ties"),
@@ -114,12 +118,21 @@ def test_topk_bit_exact(B, S, T, K, sp, ratio, kind):
     scores = torch.from_numpy(s).to(DEV)
     off = 5
     Kk = min(K, T)
+    exp = oracle.topk_select(s.astype(np.float64), K, sp, ratio, off)
     out = torch.full((B, S, 2 + Kk), -7, dtype=torch.int32, device=DEV)
     dsa.dsa_topk(scores, K, sp, ratio, off, out=out, col=2)
+    names = _launched()[1]
+    split = dsa.dsa_topk_workspace_size(B, S, T, K) > 0
+    assert ("topk_split_chunk" in names) == split, names
     got = out.cpu().numpy()
     assert np.all(got[..., :2] == -7)
-    exp = oracle.topk_select(s.astype(np.float64), K, sp, ratio, off)
     np.testing.assert_array_equal(got[..., 2:], exp)
+    if split:  # the same rows without a workspace: one workgroup per row
+        out2 = torch.full((B, S, Kk), -7, dtype=torch.int32, device=DEV)
+        rc = dsa.lib.dsa_topk(dsa._ptr(scores), B, S, T, K, sp, ratio, off, dsa._ptr(out2), Kk, None, 0,
+                              dsa._stream(scores.device, None))
+        assert rc == 0 and "topk_block" in _launched()[1]
+        np.testing.assert_array_equal(out2.cpu().numpy(), exp)
 
 
 @pytest.mark.parametrize("B,S,T,K,sp,ratio,W", [
@@ -639,7 +652,8 @@ def test_step_full_real_ratio_decode(name):
     o, idx, scores = _step(w, dev_in)
     n, names = _launched()
     _log(f"  launches: {n} {names}")
-    assert "topk_block" in names and "sparse_attn_decode<NS=16>" in names, names
+    # the long rows of a decode batch: the split select (chunk candidates, then their merge)
+    assert "topk_split_chunk+topk_split_merge" in names and "sparse_attn_decode<NS=16>" in names, names
     torch.cuda.synchronize()
     cpu_in = _device_set_to_cpu(w, dev_in)
     rows = [(b, t) for b in range(w.B) for t in range(w.S)]
