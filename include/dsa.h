@@ -187,7 +187,7 @@ int dsa_index_scores_mxfp4(const uint8_t* q_idx, const uint8_t* q_scale, const u
  *
  *   workspace: device memory of dsa_topk_workspace_size(B, S, T, index_topk) bytes (zero-filled
  *          header as for every workspace; may be NULL when that size is 0).  With it, rows of few
- *          queries and more than 4096 scores are selected in two launches over 4096-score chunks
+ *          queries and more than 16384 scores are selected in two launches over 4096-score chunks
  *          (the chunks' best K as candidates, then the best K of those); without it (NULL), by one
  *          workgroup per row.  Both give the same result.
  *

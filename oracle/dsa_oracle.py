@@ -24,13 +24,21 @@ model pages by the class or function that holds the step:
                       denominator only, -1 slots ignored, all-invalid rows -> 0
 * fp4 compressed KV -- `_compress_kv` (page "reindex-layer/read-weights"): e2m1
                       values with one E4M3 scale per 16 elements
+* candidate blocks  -- `Indexer.forward` with a candidate source: the source layer
+                      picks `candidate_topk_blocks` blocks of `candidate_block_size`
+                      compressed positions from its scores (`select_candidate_blocks`,
+                      body not on the pages), and later indexers mask their scores to
+                      -inf outside those blocks before their own top-k
 * MXFP4 index q/k   -- `Indexer.forward` quantises the index queries and keys to
                       fp4, and `_compress_kv` states the indexer's blocks: 32
                       elements per E8M0 (power-of-two) scale.  The scores are the
                       same definition over the decoded values.
 
 Readings where the pages leave a step open (each also listed with the design
-notes): ties in the top-k go to the lower position; scores are exact (not the
+notes): a candidate block's score is the largest visible score in it, a block
+is visible when any of its positions is, and the chosen blocks are the
+`candidate_topk_blocks` best visible blocks, ties to the lower block; ties in
+the top-k go to the lower position; scores are exact (not the
 eager bf16 rounding of the page's einsum); visibility uses the single formula
 c(t) = (start_pos + t + 1) // ratio, which reproduces both of the page's
 branches (prefill from 0, one-token decode).
@@ -49,6 +57,8 @@ __all__ = [
     "index_scores_rows",
     "topk_select",
     "topk_select_row",
+    "candidate_blocks_row",
+    "candidate_mask",
     "e2m1_decode",
     "e4m3_decode",
     "fp4_rows_decode",
@@ -192,6 +202,44 @@ def topk_select(scores: np.ndarray, index_topk: int, start_pos: int, ratio: int,
     for b in range(B):
         for t in range(S):
             out[b, t] = topk_select_row(scores[b, t], K, int(c[t]), offset)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# two-level selection: candidate blocks of the source layer
+# ----------------------------------------------------------------------------
+def candidate_blocks_row(scores_row: np.ndarray, c: int, n_blocks: int, block_size: int) -> np.ndarray:
+    """Chosen blocks of one query (`select_candidate_blocks`, reading): bool [ceil(T/block_size)].
+
+    Block i covers compressed positions i*block_size .. +block_size-1 and is
+    visible when its first position is (i*block_size < c).  Its score is the
+    largest of its visible scores.  The min(n_blocks, visible blocks) best
+    visible blocks are chosen, equal scores going to the lower block (the same
+    rule as the top-k, applied to blocks).
+    """
+    s = np.asarray(scores_row, dtype=np.float64)
+    nblk = -(-s.shape[0] // block_size)
+    cb = -(-c // block_size)  # visible blocks
+    bs = np.array([s[i * block_size:min((i + 1) * block_size, c)].max() for i in range(cb)])
+    chosen = np.zeros(nblk, dtype=bool)
+    if cb == 0:
+        return chosen
+    pick = topk_select_row(bs, min(n_blocks, cb), cb, 0)
+    chosen[pick[pick >= 0]] = True
+    return chosen
+
+
+def candidate_mask(scores: np.ndarray, start_pos: int, ratio: int, n_blocks: int, block_size: int) -> np.ndarray:
+    """Per-position candidate mask bool [B, S, T] of the source layer's scores: position j of query
+    t is a candidate when its block is chosen (invisible positions are never candidates)."""
+    B, S, T = scores.shape
+    c = visible_count(np.arange(S), start_pos, ratio)
+    out = np.zeros((B, S, T), dtype=bool)
+    for b in range(B):
+        for t in range(S):
+            ct = int(min(T, c[t]))
+            blk = candidate_blocks_row(scores[b, t], ct, n_blocks, block_size)
+            out[b, t] = np.repeat(blk, block_size)[:T] & (np.arange(T) < ct)
     return out
 
 

@@ -254,7 +254,8 @@ def test_workspace_sizes(dsa):
     """Long rows of few queries get the split select's candidate space; many rows (prefill) and
     short rows none; the step's size covers both the selection and the attention."""
     assert dsa.dsa_topk_workspace_size(16, 1, 65536, 512) == 4096 + 16 * 16 * 512 * 8
-    assert dsa.dsa_topk_workspace_size(16, 1, 16384, 512) == 4096 + 16 * 4 * 512 * 8
+    assert dsa.dsa_topk_workspace_size(16, 1, 16384, 512) == 0     # one workgroup per row is as fast
+    assert dsa.dsa_topk_workspace_size(16, 1, 16385, 512) == 4096 + 16 * 5 * 512 * 8
     assert dsa.dsa_topk_workspace_size(32, 1, 2048, 512) == 0       # short rows: one workgroup each
     assert dsa.dsa_topk_workspace_size(1, 8192, 8192, 512) == 0     # many rows: one wave each
     assert dsa.dsa_topk_workspace_size(1, 1, 65536, 8192) == 0      # candidates beyond one merge

@@ -84,9 +84,9 @@ def test_window_idx(B, S, sp, W):
     (1, 1, 65536, 512, 65535, 1, "ties"),
     (3, 1, 40000, 512, 79999, 2, "zeros"),
     # split select: a chunk boundary inside the visible part, K beyond a chunk's visible count
-    (4, 1, 9000, 512, 9000, 1, "ties"),
-    (2, 1, 5000, 2048, 4999, 1, "normal"),
-    (3, 2, 12000, 700, 23998, 2, "normal"),
+    (4, 1, 20000, 512, 20000, 1, "ties"),
+    (2, 1, 17000, 4000, 16999, 1, "normal"),
+    (3, 2, 24000, 700, 47998, 2, "normal"),
     (1, 3, 600, 1, 1797, 3, "normal"),
     # 1024+ rows: one wave per row (2048, 4096 and 8192 keys per lane group)
     (1, 1100, 4000, 512, 0, 1, "ties"),

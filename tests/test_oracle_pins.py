@@ -238,6 +238,80 @@ def test_mxfp4_index_scores_brute():
             assert abs(got[0, t, j] - ws * tot) <= 1e-12 * max(1.0, abs(ws * tot))
 
 
+# ---------------------------------------------------------------- candidate blocks (two-level selection)
+def test_candidate_blocks_hand_golden():
+    lines = _lines("candidate_blocks_hand.txt")
+    row = np.array([float(x) for x in lines[0].split()[1:]])
+    for ln in lines[1:]:
+        lhs, rhs = ln.split("->")
+        c, n = map(int, lhs.split())
+        want = [int(x) for x in rhs.split()]
+        got = np.nonzero(oracle.candidate_blocks_row(row, c, n, 4))[0].tolist()
+        assert got == want, (c, n, got, want)
+
+
+def _blocks_brute(row, c, n, bs):
+    blocks = []
+    for i in range((c + bs - 1) // bs):
+        m = -math.inf
+        for j in range(i * bs, min((i + 1) * bs, c)):
+            m = max(m, row[j])
+        blocks.append((-m, i))
+    blocks.sort()
+    return sorted(i for _, i in blocks[:n])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_candidate_blocks_brute_and_invariants(seed):
+    rng = np.random.default_rng(seed)
+    T, bs = 61, 4
+    for _ in range(60):
+        row = rng.integers(-3, 4, size=T).astype(np.float64) if seed % 2 else rng.standard_normal(T)
+        c = int(rng.integers(0, T + 1))
+        n = int(rng.integers(1, 20))
+        got = oracle.candidate_blocks_row(row, c, n, bs)
+        assert np.nonzero(got)[0].tolist() == _blocks_brute(row.tolist(), c, n, bs)
+        cb = -(-c // bs)
+        assert got.sum() == min(n, cb)
+    # the mask: every visible position when all visible blocks fit; positions of chosen blocks only
+    S, sp, ratio = 5, 30, 2
+    scores = rng.standard_normal((2, S, T))
+    m_all = oracle.candidate_mask(scores, sp, ratio, 100, bs)
+    c = oracle.visible_count(np.arange(S), sp, ratio)
+    for t in range(S):
+        assert np.array_equal(m_all[:, t], np.broadcast_to(np.arange(T) < min(T, c[t]), (2, T)))
+    m = oracle.candidate_mask(scores, sp, ratio, 3, bs)
+    assert np.all(m.reshape(2, S, -1).sum(-1) <= 3 * bs)
+    # the top-k of masked scores lies inside the candidates when they hold at least K positions
+    masked = np.where(m, scores, -np.inf)
+    sel = oracle.topk_select(masked, 6, sp, ratio, 0)
+    for b in range(2):
+        for t in range(S):
+            picked = sel[b, t][sel[b, t] >= 0]
+            assert np.all(m[b, t, picked])
+
+
+def test_planted_candidate_slip_is_caught(monkeypatch):
+    """A block scored by its sum instead of its maximum breaks the hand-worked example."""
+    import oracle.dsa_oracle as od
+
+    monkeypatch.setattr(od, "candidate_blocks_row", _sum_blocks)
+    monkeypatch.setattr(oracle, "candidate_blocks_row", _sum_blocks)
+    with pytest.raises(AssertionError):
+        test_candidate_blocks_hand_golden()
+
+
+def _sum_blocks(row, c, n, bs):
+    nblk = -(-len(row) // bs)
+    cb = -(-c // bs)
+    sums = np.array([row[i * bs:min((i + 1) * bs, c)].sum() for i in range(cb)])
+    out = np.zeros(nblk, dtype=bool)
+    if cb:
+        pick = oracle.topk_select_row(sums, min(n, cb), cb, 0)
+        out[pick[pick >= 0]] = True
+    return out
+
+
 # ---------------------------------------------------------------- index scores
 def test_index_scores_hand_golden():
     d = {ln.split()[0]: ln.split()[1:] for ln in _lines("index_scores_hand.txt")}
