@@ -5,6 +5,7 @@
  * caller's HIP stream, none allocating device memory):
  *
  *   dsa_index_scores  score every compressed KV row for every query
+ *   dsa_candidate_blocks, dsa_index_scores_masked  the two-level selection's candidate blocks
  *   dsa_index_scores_mxfp4  the same with the indexer's fp4 (E8M0 per 32) query and key rows
  *   dsa_topk          keep the index_topk best visible rows per query
  *   dsa_window_idx    the sliding-window part of each query's index row
@@ -152,6 +153,40 @@ int dsa_index_scores(const void* q_idx, const void* k_idx, int64_t k_batch_strid
                      int ratio, float* scores, dsa_stream_t stream);
 
 /*
+ * Candidate blocks of the two-level selection (`Indexer.forward` with a candidate source: the
+ * source layer picks candidate_topk_blocks blocks of candidate_block_size compressed positions
+ * from its scores, `select_candidate_blocks`; later indexers mask their scores outside them).
+ * The pages do not show that function; this library's reading: block i covers positions
+ * i*block_size .. +block_size-1 and is visible to query t when its first position is (i*block_size
+ * < c(t)); its score is the largest of its visible scores; the min(n_blocks, visible blocks) best
+ * visible blocks are chosen, equal scores going to the lower block.
+ */
+typedef struct dsa_candidates {
+  const uint32_t* bits; /* [B, S, ld_bits] words: bit i%32 of word i/32 of query (b,t): block i chosen */
+  int64_t ld_bits;      /* words per query row, >= ceil(ceil(T / block_size) / 32) */
+  int block_size;       /* compressed positions per block, a power of two */
+} dsa_candidates;
+
+/*
+ * The candidate blocks of every query from the source layer's scores [B, S, T] float32 (as
+ * dsa_index_scores writes them; j >= c(t) is not read): bits [B, S, ld_bits] uint32, each row
+ * written in full (words past the last block are zero).  Supported: T / block_size <= 8192.
+ */
+int dsa_candidate_blocks(const float* scores, int B, int S, int T, int start_pos, int ratio, int block_size,
+                         int n_blocks, uint32_t* bits, int64_t ld_bits, dsa_stream_t stream);
+
+/*
+ * dsa_index_scores for a consumer of candidate blocks ("score with our own weights, but only inside
+ * the source's candidate blocks"): the same scores at positions whose block is a candidate of that
+ * query, -inf elsewhere.  For one query per batch (decode) the keys outside the candidate blocks are
+ * not read.  cand may be NULL (no mask).  Errors: those of dsa_index_scores, and DSA_ERR_SHAPE for a
+ * block size that is not a power of two or rows of too few words.
+ */
+int dsa_index_scores_masked(const void* q_idx, const void* k_idx, int64_t k_batch_stride, const void* w,
+                            float w_scale, int dtype, int B, int S, int T, int H_I, int D_I, int start_pos, int ratio,
+                            const dsa_candidates* cand, float* scores, dsa_stream_t stream);
+
+/*
  * Index scores with the indexer's fp4 operands (`Indexer.forward` quantises the index queries and
  * keys to fp4; `_compress_kv` gives the indexer's blocks: 32 elements per E8M0 scale):
  * the same scores as dsa_index_scores over the decoded values
@@ -165,11 +200,12 @@ int dsa_index_scores(const void* q_idx, const void* k_idx, int64_t k_batch_strid
  *
  * Products are exact (block-scaled MFMA on e2m1 operands), sums float32.  Supported: D_I in
  * {64, 128, 256}, H_I in 1..64; q_idx and k_idx 16-byte aligned.  Same visibility rules and errors as
- * dsa_index_scores.
+ * dsa_index_scores.  cand (may be NULL): candidate blocks, as for dsa_index_scores_masked.
  */
 int dsa_index_scores_mxfp4(const uint8_t* q_idx, const uint8_t* q_scale, const uint8_t* k_idx,
                            const uint8_t* k_scale, int64_t k_batch_rows, const void* w, float w_scale, int B, int S,
-                           int T, int H_I, int D_I, int start_pos, int ratio, float* scores, dsa_stream_t stream);
+                           int T, int H_I, int D_I, int start_pos, int ratio, const dsa_candidates* cand,
+                           float* scores, dsa_stream_t stream);
 
 /*
  * Top-k selection (`Indexer.forward`: top-k by score, re-sorted into position
@@ -360,7 +396,7 @@ int dsa_sparse_attn_step(const void* q_idx, const void* k_idx, int64_t k_batch_s
  * The whole step with the indexer's fp4 operands: the same results as
  *
  *   dsa_index_scores_mxfp4(q_idx, q_scale, k_idx, k_scale, k_batch_rows, w, w_scale, B, S, T, H_I, D_I,
- *                          start_pos, ratio, scores, stream)
+ *                          start_pos, ratio, NULL, scores, stream)
  *   dsa_sparse_attn_select(scores, T, index_topk, start_pos, ratio, W, q, win, comp, sink, scale, o,
  *                          dtype, B, S, H, D, idx, workspace, workspace_bytes, stream)
  *

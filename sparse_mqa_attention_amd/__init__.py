@@ -41,6 +41,10 @@ class DsaError(RuntimeError):
         self.code = code
 
 
+class DsaCandidates(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_void_p), ("ld_bits", ctypes.c_int64), ("block_size", ctypes.c_int)]
+
+
 class DsaKvSrc(ctypes.Structure):
     _fields_ = [
         ("rows", ctypes.c_void_p),
@@ -75,7 +79,13 @@ def _load():
     lib.dsa_topk_plan.restype = i32
     lib.dsa_index_scores.argtypes = [vp, vp, i64, vp, f32, i32, i32, i32, i32, i32, i32, i32, i32, vp, vp]
     lib.dsa_index_scores.restype = i32
-    lib.dsa_index_scores_mxfp4.argtypes = [vp, vp, vp, vp, i64, vp, f32, i32, i32, i32, i32, i32, i32, i32, vp, vp]
+    lib.dsa_index_scores_mxfp4.argtypes = [vp, vp, vp, vp, i64, vp, f32, i32, i32, i32, i32, i32, i32, i32,
+                                           ctypes.POINTER(DsaCandidates), vp, vp]
+    lib.dsa_index_scores_masked.argtypes = [vp, vp, i64, vp, f32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                            ctypes.POINTER(DsaCandidates), vp, vp]
+    lib.dsa_index_scores_masked.restype = i32
+    lib.dsa_candidate_blocks.argtypes = [vp, i32, i32, i32, i32, i32, i32, i32, vp, i64, vp]
+    lib.dsa_candidate_blocks.restype = i32
     lib.dsa_index_scores_mxfp4.restype = i32
     lib.dsa_sparse_attn_step_mxfp4.argtypes = [vp, vp, vp, vp, i64, vp, f32, i32, i32, i32, i32, i32, i32, i32, vp,
                                                ctypes.POINTER(DsaKvSrc), ctypes.POINTER(DsaKvSrc), vp, f32, vp, i32,
@@ -281,20 +291,80 @@ def _mx_index_operands(qI, qI_scale, kI, kI_scale, w):
     return B, S, H, D_I, T, rows
 
 
+def _cand(candidates, B, S, T):
+    """The C descriptor of a (bits [B, S, words] int32/uint32 tensor, block_size) pair, or NULL."""
+    if candidates is None:
+        return None
+    bits, bs = candidates
+    if bits.dim() != 3 or tuple(bits.shape[:2]) != (B, S) or bits.element_size() != 4 or bits.stride(2) != 1:
+        raise DsaError(-2, "candidate bits must be a [B, S, words] tensor of 32-bit words")
+    if bits.stride(1) != bits.shape[2] or bits.stride(0) != S * bits.shape[2]:
+        raise DsaError(-2, "candidate bits must be contiguous")
+    c = DsaCandidates()
+    c.bits = bits.data_ptr()
+    c.ld_bits = bits.shape[2]
+    c.block_size = int(bs)
+    return c
+
+
+def dsa_candidate_blocks(scores, start_pos: int, ratio: int, block_size: int, n_blocks: int, out=None, stream=None):
+    """Candidate blocks of the two-level selection (dsa_candidate_blocks): int32 bit words
+    [B, S, ceil(ceil(T / block_size) / 32)], bit i of a row set when block i is chosen."""
+    _need_contig("scores", scores)
+    if scores.dtype != torch.float32 or scores.dim() != 3:
+        raise DsaError(-3, "scores must be float32 [B, S, T]")
+    B, S, T = scores.shape
+    words = ((T + block_size - 1) // block_size + 31) // 32
+    if out is not None:
+        _expect("candidate bits", out, (B, S, words), torch.int32)
+    dev = _dev(scores, out)
+    if out is None:
+        out = torch.empty(B, S, words, dtype=torch.int32, device=dev)
+    _check(lib.dsa_candidate_blocks(_ptr(scores), B, S, T, int(start_pos), int(ratio), int(block_size),
+                                    int(n_blocks), _ptr(out), words, _stream(dev, stream)))
+    return out
+
+
+def dsa_index_scores_masked(q_idx, k_idx, w, w_scale: float, start_pos: int, ratio: int, candidates, out=None,
+                            stream=None):
+    """dsa_index_scores with candidate blocks (bits, block_size) from dsa_candidate_blocks: -inf outside them."""
+    _need_contig("q_idx", q_idx)
+    _need_contig("w", w)
+    B, S, H, Dd = q_idx.shape
+    T = k_idx.shape[1]
+    kbs, krs = _batched_rows("k_idx", k_idx)
+    if krs != Dd:
+        raise DsaError(-2, "k_idx rows must be dense")
+    _expect("k_idx", k_idx, (B, T, Dd), q_idx.dtype)
+    _expect("w", w, (B, S, H), q_idx.dtype)
+    if out is not None:
+        _expect("scores", out, (B, S, T), torch.float32)
+    cand = _cand(candidates, B, S, T)
+    dev = _dev(q_idx, k_idx, w, out, None if candidates is None else candidates[0])
+    if out is None:
+        out = torch.empty(B, S, T, dtype=torch.float32, device=dev)
+    _check(lib.dsa_index_scores_masked(_ptr(q_idx), _ptr(k_idx), kbs, _ptr(w), float(w_scale), _dtype_code(q_idx), B,
+                                       S, T, H, Dd, int(start_pos), int(ratio),
+                                       None if cand is None else ctypes.byref(cand), _ptr(out), _stream(dev, stream)))
+    return out
+
+
 def dsa_index_scores_mxfp4(qI, qI_scale, kI, kI_scale, w, w_scale: float, start_pos: int, ratio: int, out=None,
-                           stream=None):
+                           candidates=None, stream=None):
     """Index scores [B, S, T] float32 from MXFP4 index operands; see `dsa_index_scores_mxfp4` in
     include/dsa.h.  qI [B,S,H_I,D_I/2] uint8, qI_scale [B,S,H_I,D_I/32] uint8, kI [B,T,D_I/2] uint8,
     kI_scale [B,T,D_I/32] uint8 (cache slices allowed), w [B,S,H_I] bf16."""
     B, S, H, D_I, T, rows = _mx_index_operands(qI, qI_scale, kI, kI_scale, w)
     if out is not None:
         _expect("scores", out, (B, S, T), torch.float32)
-    dev = _dev(qI, qI_scale, kI, kI_scale, w, out)
+    cand = _cand(candidates, B, S, T)
+    dev = _dev(qI, qI_scale, kI, kI_scale, w, out, None if candidates is None else candidates[0])
     if out is None:
         out = torch.empty(B, S, T, dtype=torch.float32, device=dev)
     _need_contig("scores", out)
     _check(lib.dsa_index_scores_mxfp4(_ptr(qI), _ptr(qI_scale), _ptr(kI), _ptr(kI_scale), rows, _ptr(w),
-                                      float(w_scale), B, S, T, H, D_I, int(start_pos), int(ratio), _ptr(out),
+                                      float(w_scale), B, S, T, H, D_I, int(start_pos), int(ratio),
+                                      None if cand is None else ctypes.byref(cand), _ptr(out),
                                       _stream(dev, stream)))
     return out
 
@@ -616,6 +686,9 @@ __all__ = [
     "DsaKvSrc",
     "dsa_index_scores",
     "dsa_index_scores_mxfp4",
+    "dsa_index_scores_masked",
+    "dsa_candidate_blocks",
+    "DsaCandidates",
     "dsa_sparse_attn_step_mxfp4",
     "dsa_topk",
     "dsa_select",

@@ -117,11 +117,12 @@ static int debug_check_idx(const int32_t* idx, int64_t count, int64_t n_rows, hi
 }
 
 int index_scores_launch(const void*, const void*, int64_t, const void*, float, int, int, int, int, int, int, int, int,
-                        float*, hipStream_t);
+                        float*, const CandMask&, hipStream_t);
+int candidate_blocks_launch(const float*, int, int, int, int, int, int, int, uint32_t*, int64_t, hipStream_t);
 int topk_launch(const float*, int, int, int, int, int, int, int, int32_t*, int64_t, int, int, void*, hipStream_t);
 size_t topk_split_bytes(int, int, int, int);
 int index_scores_mxfp4_launch(const uint8_t*, const uint8_t*, const uint8_t*, const uint8_t*, int64_t, const void*,
-                              float, int, int, int, int, int, int, int, float*, hipStream_t);
+                              float, int, int, int, int, int, int, int, float*, const CandMask&, hipStream_t);
 void topk_plan(int, int, int, int64_t*, int64_t*);
 int window_idx_launch(int, int, int, int, int, int32_t*, int64_t, hipStream_t);
 int sparse_attn_bf16_launch(const void*, const dsa_kv_src*, const dsa_kv_src*, const float*, const int32_t*, int,
@@ -192,34 +193,90 @@ int dsa_check_idx(const int32_t* idx, int64_t count, int64_t n_rows, int64_t* fi
   return DSA_OK;
 }
 
+// dsa_index_scores with an optional candidate mask: argument checks, then the launch
+static int index_scores_impl(const char* who, const void* q_idx, const void* k_idx, int64_t k_batch_stride,
+                             const void* w, float w_scale, int dtype, int B, int S, int T, int H_I, int D_I,
+                             int start_pos, int ratio, float* scores, const dsa::CandMask& cm, hipStream_t st) {
+  if (dtype != DSA_F32 && dtype != DSA_BF16) return fail(DSA_ERR_DTYPE, "%s: dtype %d", who, dtype);
+  if (B < 0 || S < 0 || T < 0 || H_I <= 0 || D_I <= 0 || start_pos < 0 || ratio <= 0)
+    return fail(DSA_ERR_SHAPE, "%s: bad sizes B=%d S=%d T=%d H_I=%d D_I=%d start_pos=%d ratio=%d", who, B, S, T, H_I,
+                D_I, start_pos, ratio);
+  if ((int64_t)T > ((int64_t)start_pos + S) / ratio)
+    return fail(DSA_ERR_SHAPE, "%s: T=%d exceeds (start_pos+S)/ratio=%lld", who, T,
+                (long long)(((int64_t)start_pos + S) / ratio));
+  if (H_I > 64) return fail(DSA_ERR_UNSUPPORTED, "%s: H_I=%d > 64", who, H_I);
+  if (B == 0 || S == 0 || T == 0) return DSA_OK;
+  if (!q_idx || !k_idx || !w || !scores) return fail(DSA_ERR_NULL, "%s: NULL tensor pointer", who);
+  if (k_batch_stride < (int64_t)T * D_I)
+    return fail(DSA_ERR_SHAPE, "%s: k_batch_stride %lld < T*D_I", who, (long long)k_batch_stride);
+  if (dtype == DSA_BF16 && (((uintptr_t)q_idx | (uintptr_t)k_idx) & 15))
+    return fail(DSA_ERR_SHAPE, "%s: q_idx and k_idx must be 16-byte aligned", who);
+  if (dtype == DSA_BF16 && (k_batch_stride % 8))
+    return fail(DSA_ERR_SHAPE, "%s: k_batch_stride must be a multiple of 8 elements", who);
+  return dsa::index_scores_launch(q_idx, k_idx, k_batch_stride, w, w_scale, dtype, B, S, T, H_I, D_I, start_pos,
+                                  ratio, scores, cm, st);
+}
+
 int dsa_index_scores(const void* q_idx, const void* k_idx, int64_t k_batch_stride, const void* w, float w_scale,
                      int dtype, int B, int S, int T, int H_I, int D_I, int start_pos, int ratio, float* scores,
                      dsa_stream_t stream) {
   dsa::Entry entry_;
-  if (dtype != DSA_F32 && dtype != DSA_BF16) return fail(DSA_ERR_DTYPE, "dsa_index_scores: dtype %d", dtype);
-  if (B < 0 || S < 0 || T < 0 || H_I <= 0 || D_I <= 0 || start_pos < 0 || ratio <= 0)
-    return fail(DSA_ERR_SHAPE, "dsa_index_scores: bad sizes B=%d S=%d T=%d H_I=%d D_I=%d start_pos=%d ratio=%d", B, S,
-                T, H_I, D_I, start_pos, ratio);
-  if ((int64_t)T > ((int64_t)start_pos + S) / ratio)
-    return fail(DSA_ERR_SHAPE, "dsa_index_scores: T=%d exceeds (start_pos+S)/ratio=%lld", T,
-                (long long)(((int64_t)start_pos + S) / ratio));
-  if (H_I > 64) return fail(DSA_ERR_UNSUPPORTED, "dsa_index_scores: H_I=%d > 64", H_I);
+  return index_scores_impl("dsa_index_scores", q_idx, k_idx, k_batch_stride, w, w_scale, dtype, B, S, T, H_I, D_I,
+                           start_pos, ratio, scores, dsa::CandMask{nullptr, 0, 0}, (hipStream_t)stream);
+}
+
+// the candidate mask of a call: checked, with the block size as its log2
+static int cand_mask(const dsa_candidates* cand, int T, dsa::CandMask* out, const char* who) {
+  *out = dsa::CandMask{nullptr, 0, 0};
+  if (!cand) return DSA_OK;
+  if (!cand->bits) return fail(DSA_ERR_NULL, "%s: candidate bits NULL", who);
+  const int bs = cand->block_size;
+  if (bs <= 0 || (bs & (bs - 1)))
+    return fail(DSA_ERR_SHAPE, "%s: candidate block size %d is not a power of two", who, bs);
+  const int64_t words = (((int64_t)T + bs - 1) / bs + 31) / 32;
+  if (cand->ld_bits < words)
+    return fail(DSA_ERR_SHAPE, "%s: candidate rows of %lld words, %lld needed", who, (long long)cand->ld_bits,
+                (long long)words);
+  *out = dsa::CandMask{cand->bits, cand->ld_bits, __builtin_ctz(bs)};
+  return DSA_OK;
+}
+
+int dsa_index_scores_masked(const void* q_idx, const void* k_idx, int64_t k_batch_stride, const void* w,
+                            float w_scale, int dtype, int B, int S, int T, int H_I, int D_I, int start_pos, int ratio,
+                            const dsa_candidates* cand, float* scores, dsa_stream_t stream) {
+  dsa::Entry entry_;
+  dsa::CandMask cm;
+  const int crc = cand_mask(cand, T, &cm, "dsa_index_scores_masked");
+  if (crc) return crc;
+  return index_scores_impl("dsa_index_scores_masked", q_idx, k_idx, k_batch_stride, w, w_scale, dtype, B, S, T, H_I,
+                           D_I, start_pos, ratio, scores, cm, (hipStream_t)stream);
+}
+
+int dsa_candidate_blocks(const float* scores, int B, int S, int T, int start_pos, int ratio, int block_size,
+                         int n_blocks, uint32_t* bits, int64_t ld_bits, dsa_stream_t stream) {
+  dsa::Entry entry_;
+  if (B < 0 || S < 0 || T < 0 || start_pos < 0 || ratio <= 0 || n_blocks <= 0)
+    return fail(DSA_ERR_SHAPE, "dsa_candidate_blocks: bad sizes B=%d S=%d T=%d n_blocks=%d", B, S, T, n_blocks);
+  if (block_size <= 0 || (block_size & (block_size - 1)))
+    return fail(DSA_ERR_SHAPE, "dsa_candidate_blocks: block size %d is not a power of two", block_size);
+  const int64_t words = (((int64_t)T + block_size - 1) / block_size + 31) / 32;
+  if (ld_bits < words)
+    return fail(DSA_ERR_SHAPE, "dsa_candidate_blocks: rows of %lld words, %lld needed", (long long)ld_bits,
+                (long long)words);
   if (B == 0 || S == 0 || T == 0) return DSA_OK;
-  if (!q_idx || !k_idx || !w || !scores) return fail(DSA_ERR_NULL, "dsa_index_scores: NULL tensor pointer");
-  if (k_batch_stride < (int64_t)T * D_I)
-    return fail(DSA_ERR_SHAPE, "dsa_index_scores: k_batch_stride %lld < T*D_I", (long long)k_batch_stride);
-  if (dtype == DSA_BF16 && (((uintptr_t)q_idx | (uintptr_t)k_idx) & 15))
-    return fail(DSA_ERR_SHAPE, "dsa_index_scores: q_idx and k_idx must be 16-byte aligned");
-  if (dtype == DSA_BF16 && (k_batch_stride % 8))
-    return fail(DSA_ERR_SHAPE, "dsa_index_scores: k_batch_stride must be a multiple of 8 elements");
-  return dsa::index_scores_launch(q_idx, k_idx, k_batch_stride, w, w_scale, dtype, B, S, T, H_I, D_I, start_pos,
-                                  ratio, scores, (hipStream_t)stream);
+  if (!scores || !bits) return fail(DSA_ERR_NULL, "dsa_candidate_blocks: NULL pointer");
+  return dsa::candidate_blocks_launch(scores, B, S, T, start_pos, ratio, __builtin_ctz(block_size), n_blocks, bits,
+                                      ld_bits, (hipStream_t)stream);
 }
 
 int dsa_index_scores_mxfp4(const uint8_t* q_idx, const uint8_t* q_scale, const uint8_t* k_idx,
                            const uint8_t* k_scale, int64_t k_batch_rows, const void* w, float w_scale, int B, int S,
-                           int T, int H_I, int D_I, int start_pos, int ratio, float* scores, dsa_stream_t stream) {
+                           int T, int H_I, int D_I, int start_pos, int ratio, const dsa_candidates* cand,
+                           float* scores, dsa_stream_t stream) {
   dsa::Entry entry_;
+  dsa::CandMask cm;
+  const int crc = cand_mask(cand, T, &cm, "dsa_index_scores_mxfp4");
+  if (crc) return crc;
   if (B < 0 || S < 0 || T < 0 || H_I <= 0 || D_I <= 0 || start_pos < 0 || ratio <= 0)
     return fail(DSA_ERR_SHAPE, "dsa_index_scores_mxfp4: bad sizes B=%d S=%d T=%d H_I=%d D_I=%d start_pos=%d ratio=%d",
                 B, S, T, H_I, D_I, start_pos, ratio);
@@ -236,7 +293,7 @@ int dsa_index_scores_mxfp4(const uint8_t* q_idx, const uint8_t* q_scale, const u
   if (((uintptr_t)q_idx | (uintptr_t)k_idx) & 15)
     return fail(DSA_ERR_SHAPE, "dsa_index_scores_mxfp4: q_idx and k_idx must be 16-byte aligned");
   return dsa::index_scores_mxfp4_launch(q_idx, q_scale, k_idx, k_scale, k_batch_rows, w, w_scale, B, S, T, H_I, D_I,
-                                        start_pos, ratio, scores, (hipStream_t)stream);
+                                        start_pos, ratio, scores, cm, (hipStream_t)stream);
 }
 
 size_t dsa_topk_workspace_size(int B, int S, int T, int index_topk) {
@@ -537,7 +594,7 @@ int dsa_sparse_attn_step_mxfp4(const uint8_t* q_idx, const uint8_t* q_scale, con
     return fail(DSA_ERR_WORKSPACE, "dsa_sparse_attn_step_mxfp4: workspace of %zu bytes needed, %zu given", need,
                 workspace_bytes);
   int rc = dsa_index_scores_mxfp4(q_idx, q_scale, k_idx, k_scale, k_batch_rows, w, w_scale, B, S, T, H_I, D_I,
-                                  start_pos, ratio, scores, stream);
+                                  start_pos, ratio, nullptr, scores, stream);
   if (rc) return rc;
   return dsa_sparse_attn_select(scores, T, index_topk, start_pos, ratio, W, q, win, comp, sink, scale, o, dtype, B, S,
                                 H, D, idx, workspace, workspace_bytes, stream);

@@ -137,6 +137,21 @@ __device__ __forceinline__ int visible_rows(int start_pos, int t, int ratio) {
   return (start_pos + t + 1) / ratio;
 }
 
+// Candidate blocks of the two-level selection as the scoring kernels read them: bit i of word
+// i/32 of query row r (words ld apart) is set when block i of 2^lbs compressed positions is a
+// candidate.  bits == nullptr: every position is a candidate.
+struct CandMask {
+  const uint32_t* bits;
+  int64_t ld;
+  int lbs;
+};
+
+__device__ __forceinline__ bool cand_ok(const CandMask& m, int64_t row, int j) {
+  if (m.bits == nullptr) return true;
+  const int blk = j >> m.lbs;
+  return ((m.bits[row * m.ld + (blk >> 5)] >> (blk & 31)) & 1u) != 0u;
+}
+
 }  // namespace dsa
 
 namespace dsa {

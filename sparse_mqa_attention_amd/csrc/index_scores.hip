@@ -25,7 +25,7 @@ template <int DI, int MT, int QB>
 __global__ void __launch_bounds__(kIdxThreads)
 index_scores_bf16_kernel(const __bf16* __restrict__ q_idx, const __bf16* __restrict__ k_idx,
                          int64_t k_bstride, const __bf16* __restrict__ w, float w_scale, int S,
-                         int T, int H, int start_pos, int ratio, float* __restrict__ scores) {
+                         int T, int H, int start_pos, int ratio, float* __restrict__ scores, CandMask cm) {
   constexpr int NCH = DI / 8;   // 16-byte chunks per index row
   constexpr int KS = DI / 16;   // MFMA k-steps
   constexpr int HP = 32 * MT;   // padded heads
@@ -62,14 +62,17 @@ index_scores_bf16_kernel(const __bf16* __restrict__ q_idx, const __bf16* __restr
   const int c_last = min(T, visible_rows(start_pos, t0 + nq - 1, ratio));
   bf16x8 kreg[2][KS];
   const bool wave_live = jw < c_last;
+  // one query per block (decode): keys outside its candidate blocks are not read
+  const int64_t row0 = (int64_t)b * S + t0;
   if (wave_live) {
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       const int j = jw + 32 * n + c;
       const __bf16* kp = k_idx + (int64_t)b * k_bstride + (int64_t)j * DI + hf * 8;
+      const bool need = j < T && (QB > 1 || cand_ok(cm, row0, j));
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
-        if (j < T) {
+        if (need) {
           kreg[n][s] = *reinterpret_cast<const bf16x8*>(kp + s * 16);
         } else {
           kreg[n][s] = bf16x8{};
@@ -93,8 +96,13 @@ index_scores_bf16_kernel(const __bf16* __restrict__ q_idx, const __bf16* __restr
         if (hf == 0 && j < T) out_row[j] = ninf;
         continue;
       }
+      const bool ok = j < ct && cand_ok(cm, row0 + q, j);
+      if (QB == 1 && __builtin_amdgcn_ballot_w64(ok) == 0ull) {  // no candidate in the tile: no multiply
+        if (hf == 0 && j < T) out_row[j] = ninf;
+        continue;
+      }
       const float sum = index_tile_sum<DI, MT>(q_lds + q * HP * DI, w_lds + q * HP, kreg[n], hf, c);
-      if (hf == 0 && j < T) out_row[j] = j < ct ? w_scale * sum : ninf;
+      if (hf == 0 && j < T) out_row[j] = ok ? w_scale * sum : ninf;
     }
   }
   // rows of this wave never loaded (all invisible for the whole block): still write -inf
@@ -105,14 +113,14 @@ index_scores_bf16_kernel(const __bf16* __restrict__ q_idx, const __bf16* __restr
 __global__ void index_scores_f32_kernel(const float* __restrict__ q_idx, const float* __restrict__ k_idx,
                                         int64_t k_bstride, const float* __restrict__ w, float w_scale,
                                         int S, int T, int H, int DI, int start_pos, int ratio,
-                                        float* __restrict__ scores) {
+                                        float* __restrict__ scores, CandMask cm) {
   const int j = blockIdx.x * blockDim.x + threadIdx.x;
   const int t = blockIdx.y;
   const int b = blockIdx.z;
   if (j >= T) return;
   const int ct = min(T, visible_rows(start_pos, t, ratio));
   float* out = scores + ((int64_t)b * S + t) * T + j;
-  if (j >= ct) {
+  if (j >= ct || !cand_ok(cm, (int64_t)b * S + t, j)) {
     *out = -__builtin_inff();
     return;
   }
@@ -129,10 +137,10 @@ __global__ void index_scores_f32_kernel(const float* __restrict__ q_idx, const f
 
 template <int DI, int MT, int QB>
 int launch_bf16(const void* q, const void* k, int64_t kbs, const void* w, float ws, int B, int S, int T,
-                int H, int sp, int r, float* scores, hipStream_t st) {
+                int H, int sp, int r, float* scores, const CandMask& cm, hipStream_t st) {
   dim3 grid((T + kRowsPerBlock - 1) / kRowsPerBlock, (S + QB - 1) / QB, B);
   hipLaunchKernelGGL((index_scores_bf16_kernel<DI, MT, QB>), grid, dim3(kIdxThreads), 0, st,
-                     (const __bf16*)q, (const __bf16*)k, kbs, (const __bf16*)w, ws, S, T, H, sp, r, scores);
+                     (const __bf16*)q, (const __bf16*)k, kbs, (const __bf16*)w, ws, S, T, H, sp, r, scores, cm);
   return check_launch("index_scores_bf16");
 }
 
@@ -144,43 +152,43 @@ constexpr int prefill_qb() {
 
 template <int DI, int MT>
 int launch_bf16_qb(const void* q, const void* k, int64_t kbs, const void* w, float ws, int B, int S, int T,
-                   int H, int sp, int r, float* scores, hipStream_t st) {
-  if (S == 1) return launch_bf16<DI, MT, 1>(q, k, kbs, w, ws, B, S, T, H, sp, r, scores, st);
-  return launch_bf16<DI, MT, prefill_qb<DI, MT>()>(q, k, kbs, w, ws, B, S, T, H, sp, r, scores, st);
+                   int H, int sp, int r, float* scores, const CandMask& cm, hipStream_t st) {
+  if (S == 1) return launch_bf16<DI, MT, 1>(q, k, kbs, w, ws, B, S, T, H, sp, r, scores, cm, st);
+  return launch_bf16<DI, MT, prefill_qb<DI, MT>()>(q, k, kbs, w, ws, B, S, T, H, sp, r, scores, cm, st);
 }
 
 template <int DI>
 int launch_bf16_mt(const void* q, const void* k, int64_t kbs, const void* w, float ws, int B, int S, int T,
-                   int H, int sp, int r, float* scores, hipStream_t st) {
-  if (H <= 32) return launch_bf16_qb<DI, 1>(q, k, kbs, w, ws, B, S, T, H, sp, r, scores, st);
-  return launch_bf16_qb<DI, 2>(q, k, kbs, w, ws, B, S, T, H, sp, r, scores, st);
+                   int H, int sp, int r, float* scores, const CandMask& cm, hipStream_t st) {
+  if (H <= 32) return launch_bf16_qb<DI, 1>(q, k, kbs, w, ws, B, S, T, H, sp, r, scores, cm, st);
+  return launch_bf16_qb<DI, 2>(q, k, kbs, w, ws, B, S, T, H, sp, r, scores, cm, st);
 }
 
 }  // namespace
 
 int index_scores_prefill_launch(const void* q_idx, const void* k_idx, int64_t kbs, const void* w, float w_scale,
                                 int B, int S, int T, int H, int DI, int start_pos, int ratio, float* scores,
-                                hipStream_t st);
+                                const CandMask& cm, hipStream_t st);
 
 int index_scores_launch(const void* q_idx, const void* k_idx, int64_t kbs, const void* w, float w_scale,
                         int dtype, int B, int S, int T, int H, int DI, int start_pos, int ratio,
-                        float* scores, hipStream_t st) {
+                        float* scores, const CandMask& cm, hipStream_t st) {
   if (dtype == DSA_F32) {
     dim3 grid((T + 63) / 64, S, B);
     hipLaunchKernelGGL(index_scores_f32_kernel, grid, dim3(64), 0, st, (const float*)q_idx,
                        (const float*)k_idx, kbs, (const float*)w, w_scale, S, T, H, DI, start_pos, ratio,
-                       scores);
+                       scores, cm);
     return check_launch("index_scores_f32");
   }
   // prefill at index head dim 128: keys streamed past queries held in registers
   const int prc = index_scores_prefill_launch(q_idx, k_idx, kbs, w, w_scale, B, S, T, H, DI, start_pos, ratio,
-                                              scores, st);
+                                              scores, cm, st);
   if (prc != 0) return prc < 0 ? prc : 0;
   switch (DI) {
-    case 32: return launch_bf16_mt<32>(q_idx, k_idx, kbs, w, w_scale, B, S, T, H, start_pos, ratio, scores, st);
-    case 64: return launch_bf16_mt<64>(q_idx, k_idx, kbs, w, w_scale, B, S, T, H, start_pos, ratio, scores, st);
-    case 128: return launch_bf16_mt<128>(q_idx, k_idx, kbs, w, w_scale, B, S, T, H, start_pos, ratio, scores, st);
-    case 256: return launch_bf16_mt<256>(q_idx, k_idx, kbs, w, w_scale, B, S, T, H, start_pos, ratio, scores, st);
+    case 32: return launch_bf16_mt<32>(q_idx, k_idx, kbs, w, w_scale, B, S, T, H, start_pos, ratio, scores, cm, st);
+    case 64: return launch_bf16_mt<64>(q_idx, k_idx, kbs, w, w_scale, B, S, T, H, start_pos, ratio, scores, cm, st);
+    case 128: return launch_bf16_mt<128>(q_idx, k_idx, kbs, w, w_scale, B, S, T, H, start_pos, ratio, scores, cm, st);
+    case 256: return launch_bf16_mt<256>(q_idx, k_idx, kbs, w, w_scale, B, S, T, H, start_pos, ratio, scores, cm, st);
     default: return fail(DSA_ERR_UNSUPPORTED, "dsa_index_scores: D_I=%d has no bf16 kernel (32, 64, 128, 256)", DI);
   }
 }

@@ -48,7 +48,7 @@ __global__ void __launch_bounds__(kMxThreads)
 index_scores_mxfp4_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __restrict__ q_scale,
                           const uint8_t* __restrict__ k_idx, const uint8_t* __restrict__ k_scale,
                           int64_t k_brows, const __bf16* __restrict__ w, float w_scale, int S, int T, int H,
-                          int start_pos, int ratio, float* __restrict__ scores) {
+                          int start_pos, int ratio, float* __restrict__ scores, CandMask cm) {
   constexpr int RB = DI / 2;     // packed bytes per row
   constexpr int NCH = RB / 16;   // 16-byte chunks per row
   constexpr int NB = DI / 32;    // scale bytes per row
@@ -95,10 +95,12 @@ index_scores_mxfp4_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __re
   const int c_last = min(T, visible_rows(start_pos, t0 + nq - 1, ratio));
   u32x4 kreg[2][KS];
   int ksc[2][KS];
+  // one query per block (decode): keys outside its candidate blocks are not read
+  const int64_t row0 = (int64_t)b * S + t0;
 #pragma unroll
   for (int n = 0; n < 2; ++n) {
     const int j = jw + 32 * n + c;
-    const bool live = jw + 32 * n < c_last && j < T;
+    const bool live = jw + 32 * n < c_last && j < T && (QB > 1 || cand_ok(cm, row0, j));
     const uint8_t* kp = k_idx + ((int64_t)b * k_brows + j) * RB + 16 * hf;
     const uint8_t* sp = k_scale + ((int64_t)b * k_brows + j) * NB + hf;
 #pragma unroll
@@ -123,6 +125,11 @@ index_scores_mxfp4_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __re
         if (hf == 0 && j < T) out_row[j] = ninf;
         continue;
       }
+      const bool ok = j < ct && cand_ok(cm, row0 + q, j);
+      if (QB == 1 && __builtin_amdgcn_ballot_w64(ok) == 0ull) {  // no candidate in the tile: no multiply
+        if (hf == 0 && j < T) out_row[j] = ninf;
+        continue;
+      }
       float sum = 0.f;
 #pragma unroll
       for (int m = 0; m < MT; ++m) {
@@ -143,43 +150,46 @@ index_scores_mxfp4_kernel(const uint8_t* __restrict__ q_idx, const uint8_t* __re
         }
       }
       sum += shfl_xor(sum, 32);
-      if (hf == 0 && j < T) out_row[j] = j < ct ? w_scale * sum : ninf;
+      if (hf == 0 && j < T) out_row[j] = ok ? w_scale * sum : ninf;
     }
   }
 }
 
 template <int DI, int MT, int QB>
 int launch_mx(const uint8_t* q, const uint8_t* qs, const uint8_t* k, const uint8_t* ks, int64_t kbr, const void* w,
-              float ws, int B, int S, int T, int H, int sp, int r, float* scores, hipStream_t st) {
+              float ws, int B, int S, int T, int H, int sp, int r, float* scores, const CandMask& cm, hipStream_t st) {
   dim3 grid((T + kMxRowsPerBlock - 1) / kMxRowsPerBlock, (S + QB - 1) / QB, B);
   hipLaunchKernelGGL((index_scores_mxfp4_kernel<DI, MT, QB>), grid, dim3(kMxThreads), 0, st, q, qs, k, ks, kbr,
-                     (const __bf16*)w, ws, S, T, H, sp, r, scores);
+                     (const __bf16*)w, ws, S, T, H, sp, r, scores, cm);
   return check_launch("index_scores_mxfp4");
 }
 
 template <int DI, int MT>
 int launch_mx_qb(const uint8_t* q, const uint8_t* qs, const uint8_t* k, const uint8_t* ks, int64_t kbr,
-                 const void* w, float ws, int B, int S, int T, int H, int sp, int r, float* scores, hipStream_t st) {
-  if (S == 1) return launch_mx<DI, MT, 1>(q, qs, k, ks, kbr, w, ws, B, S, T, H, sp, r, scores, st);
-  return launch_mx<DI, MT, 16>(q, qs, k, ks, kbr, w, ws, B, S, T, H, sp, r, scores, st);
+                 const void* w, float ws, int B, int S, int T, int H, int sp, int r, float* scores, const CandMask& cm,
+                 hipStream_t st) {
+  if (S == 1) return launch_mx<DI, MT, 1>(q, qs, k, ks, kbr, w, ws, B, S, T, H, sp, r, scores, cm, st);
+  return launch_mx<DI, MT, 16>(q, qs, k, ks, kbr, w, ws, B, S, T, H, sp, r, scores, cm, st);
 }
 
 template <int DI>
 int launch_mx_mt(const uint8_t* q, const uint8_t* qs, const uint8_t* k, const uint8_t* ks, int64_t kbr,
-                 const void* w, float ws, int B, int S, int T, int H, int sp, int r, float* scores, hipStream_t st) {
-  if (H <= 32) return launch_mx_qb<DI, 1>(q, qs, k, ks, kbr, w, ws, B, S, T, H, sp, r, scores, st);
-  return launch_mx_qb<DI, 2>(q, qs, k, ks, kbr, w, ws, B, S, T, H, sp, r, scores, st);
+                 const void* w, float ws, int B, int S, int T, int H, int sp, int r, float* scores, const CandMask& cm,
+                 hipStream_t st) {
+  if (H <= 32) return launch_mx_qb<DI, 1>(q, qs, k, ks, kbr, w, ws, B, S, T, H, sp, r, scores, cm, st);
+  return launch_mx_qb<DI, 2>(q, qs, k, ks, kbr, w, ws, B, S, T, H, sp, r, scores, cm, st);
 }
 
 }  // namespace
 
 int index_scores_mxfp4_launch(const uint8_t* q_idx, const uint8_t* q_scale, const uint8_t* k_idx,
                               const uint8_t* k_scale, int64_t k_brows, const void* w, float w_scale, int B, int S,
-                              int T, int H, int DI, int start_pos, int ratio, float* scores, hipStream_t st) {
+                              int T, int H, int DI, int start_pos, int ratio, float* scores, const CandMask& cm,
+                              hipStream_t st) {
   switch (DI) {
-    case 64: return launch_mx_mt<64>(q_idx, q_scale, k_idx, k_scale, k_brows, w, w_scale, B, S, T, H, start_pos, ratio, scores, st);
-    case 128: return launch_mx_mt<128>(q_idx, q_scale, k_idx, k_scale, k_brows, w, w_scale, B, S, T, H, start_pos, ratio, scores, st);
-    case 256: return launch_mx_mt<256>(q_idx, q_scale, k_idx, k_scale, k_brows, w, w_scale, B, S, T, H, start_pos, ratio, scores, st);
+    case 64: return launch_mx_mt<64>(q_idx, q_scale, k_idx, k_scale, k_brows, w, w_scale, B, S, T, H, start_pos, ratio, scores, cm, st);
+    case 128: return launch_mx_mt<128>(q_idx, q_scale, k_idx, k_scale, k_brows, w, w_scale, B, S, T, H, start_pos, ratio, scores, cm, st);
+    case 256: return launch_mx_mt<256>(q_idx, q_scale, k_idx, k_scale, k_brows, w, w_scale, B, S, T, H, start_pos, ratio, scores, cm, st);
     default: return fail(DSA_ERR_UNSUPPORTED, "dsa_index_scores_mxfp4: D_I=%d not in {64, 128, 256}", DI);
   }
 }

@@ -38,7 +38,7 @@ __device__ __forceinline__ float relu1(float x) { return __int_as_float(max(__fl
 __global__ void __launch_bounds__(256, 2)
 index_scores_prefill_kernel(const __bf16* __restrict__ q_idx, const __bf16* __restrict__ k_idx, int64_t k_bstride,
                             const __bf16* __restrict__ w, float w_scale, int S, int T, int H, int start_pos,
-                            int ratio, int nqb, float* __restrict__ scores) {
+                            int ratio, int nqb, float* __restrict__ scores, CandMask cm) {
   __shared__ __attribute__((aligned(1024))) unsigned char ring[kXNST * kXTileB];
 
   const int tid = threadIdx.x;
@@ -155,7 +155,8 @@ index_scores_prefill_kernel(const __bf16* __restrict__ q_idx, const __bf16* __re
         const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(sum), false, false);
         sum = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
         const int j = i * kXKT + 32 * kb + c;
-        if (live[m] && hf == 0 && j < T) out_row[j] = j < ct[m] ? w_scale * sum : ninf;
+        if (live[m] && hf == 0 && j < T)
+          out_row[j] = (j < ct[m] && cand_ok(cm, (int64_t)b * S + t0 + 2 * wave + m, j)) ? w_scale * sum : ninf;
       }
     }
   }
@@ -175,12 +176,12 @@ index_scores_prefill_kernel(const __bf16* __restrict__ q_idx, const __bf16* __re
 // heads, enough queries, 16-byte aligned key rows); returns 1 if launched, 0 if not, <0 on error.
 int index_scores_prefill_launch(const void* q_idx, const void* k_idx, int64_t kbs, const void* w, float w_scale,
                                 int B, int S, int T, int H, int DI, int start_pos, int ratio, float* scores,
-                                hipStream_t st) {
+                                const CandMask& cm, hipStream_t st) {
   if (DI != kXDI || H > 32 || S < 64 || T < 1) return 0;
   if (((uintptr_t)k_idx & 15) != 0 || ((kbs * 2) & 15) != 0) return 0;
   const int nqb = (S + kXQ - 1) / kXQ;
   hipLaunchKernelGGL(index_scores_prefill_kernel, dim3(B * nqb), dim3(256), 0, st, (const __bf16*)q_idx,
-                     (const __bf16*)k_idx, kbs, (const __bf16*)w, w_scale, S, T, H, start_pos, ratio, nqb, scores);
+                     (const __bf16*)k_idx, kbs, (const __bf16*)w, w_scale, S, T, H, start_pos, ratio, nqb, scores, cm);
   const int rc = check_launch("index_scores_prefill");
   return rc ? rc : 1;
 }

@@ -107,6 +107,45 @@ topk_split_merge_kernel(const float* __restrict__ cand_s, const int32_t* __restr
                       [&](int slot, int i) { out[slot] = cp[i] + offset; });
 }
 
+// Candidate blocks of the two-level selection (`Indexer.forward` with a candidate source:
+// `select_candidate_blocks` picks the source layer's best blocks of compressed positions; its body
+// is not on the pages, so a block scores its largest visible score, a block is visible when its
+// first position is, and the best n_sel visible blocks are kept, ties to the lower block).  One
+// workgroup per query: block maxima into LDS, the block select of the top-k on them, and the chosen
+// blocks as a bitmap row (bit i of word i/32).
+constexpr int kCandMaxBlocks = 8192;
+
+__global__ void __launch_bounds__(1024)
+candidate_blocks_kernel(const float* __restrict__ scores, int S, int T, int start_pos, int ratio, int lbs, int n_sel,
+                        uint32_t* __restrict__ bits, int64_t ld_bits) {
+  __shared__ TopkSmem<1024> sm;
+  __shared__ __attribute__((aligned(16))) float bmax[kCandMaxBlocks];
+  __shared__ uint32_t bw[kCandMaxBlocks / 32];
+  const int row = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int bs = 1 << lbs;
+  const int c = min(T, visible_rows(start_pos, row % S, ratio));
+  const int nblk = (T + bs - 1) >> lbs;
+  const int cb = (c + bs - 1) >> lbs;  // visible blocks
+  const int nw = (nblk + 31) >> 5;
+  for (int i = tid; i < nw; i += 1024) bw[i] = 0u;
+  const float* srow = scores + (int64_t)row * T;
+  for (int i = tid; i < cb; i += 1024) {
+    const int e = min((i + 1) << lbs, c);
+    float m = srow[i << lbs];
+    for (int j = (i << lbs) + 1; j < e; ++j) m = fmaxf(m, srow[j]);
+    bmax[i] = m;
+  }
+  __syncthreads();
+  if (cb <= n_sel) {
+    for (int i = tid; i < cb; i += 1024) atomicOr(&bw[i >> 5], 1u << (i & 31));
+  } else {
+    block_topk<1024, 8>(bmax, cb, cb, n_sel, 0, sm, [&](int slot, int i) { atomicOr(&bw[i >> 5], 1u << (i & 31)); });
+  }
+  __syncthreads();
+  for (int i = tid; i < nw; i += 1024) bits[(int64_t)row * ld_bits + i] = bw[i];
+}
+
 // Many rows (prefill): one wave per row and no workgroup barriers.  Lane l holds the keys of
 // positions 64g + l (g < KPL) in registers (invisible positions get key 0, below every real
 // key).  The radix select takes 8-bit digits, from the highest bit where the row's keys differ,
@@ -414,6 +453,15 @@ int topk_split_launch(const float* scores, int B, int S, int T, int K, int sp, i
   else DSA_MERGE(1024, 32);
 #undef DSA_MERGE
   return check_launch("topk_split_merge");
+}
+
+int candidate_blocks_launch(const float* scores, int B, int S, int T, int start_pos, int ratio, int lbs, int n_sel,
+                            uint32_t* bits, int64_t ld_bits, hipStream_t st) {
+  if (((T + (1 << lbs) - 1) >> lbs) > kCandMaxBlocks)
+    return fail(DSA_ERR_UNSUPPORTED, "dsa_candidate_blocks: more than %d blocks per row", kCandMaxBlocks);
+  hipLaunchKernelGGL(candidate_blocks_kernel, dim3(B * S), dim3(1024), 0, st, scores, S, T, start_pos, ratio, lbs,
+                     n_sel, bits, ld_bits);
+  return check_launch("candidate_blocks");
 }
 
 // Rows of a top-k call on the one-wave kernel and on the per-row workgroup kernel.

@@ -741,3 +741,179 @@ def test_step_mxfp4(name, full):
     rows = [(b, t) for b in range(w.B) for t in range(w.S)] if full else sample_rows(w, n_random=12)
     _check_step(w, cpu_in, o, idx, scores, rows)
     assert _dsa().dsa_device_errors() == 0
+
+
+# ------------------------------------------------------------------------ two-level selection (candidate blocks)
+def _unpack_bits(words, nblk):
+    w = np.asarray(words).astype(np.int64) & 0xFFFFFFFF
+    bits = (w[..., :, None] >> np.arange(32)) & 1
+    flat = bits.reshape(*w.shape[:-1], -1).astype(bool)
+    return flat[..., :nblk], flat[..., nblk:]
+
+
+def _pack_bits(blocks):
+    """bool [..., nblk] -> int32 words [..., ceil(nblk/32)] (bit i%32 of word i/32)."""
+    nblk = blocks.shape[-1]
+    nw = (nblk + 31) // 32
+    pad = np.zeros(blocks.shape[:-1] + (nw * 32,), dtype=np.uint64)
+    pad[..., :nblk] = blocks
+    words = (pad.reshape(*blocks.shape[:-1], nw, 32) << np.arange(32, dtype=np.uint64)).sum(-1)
+    return words.astype(np.uint32).view(np.int32)
+
+
+@pytest.mark.parametrize("B,S,T,sp,ratio,bs,nsel,kind", [
+    (4, 1, 65536, 65535, 1, 8, 2048, "normal"),  # the page's candidate source: ratio 1 at 64K context
+    (2, 1, 32768, 65535, 2, 8, 2048, "ties"),
+    (1, 300, 1000, 0, 1, 8, 20, "normal"),       # prefill rows: blocks partly visible
+    (3, 2, 777, 3099, 4, 4, 50, "ties"),
+    (2, 1, 100, 399, 4, 8, 100, "normal"),       # every visible block fits
+])
+def test_candidate_blocks(B, S, T, sp, ratio, bs, nsel, kind):
+    """Given the same float32 scores, the chosen blocks equal the oracle's bit for bit (padding bits
+    of a row's last word stay zero)."""
+    dsa = _dsa()
+    _log(f"candidate blocks B={B} S={S} T={T} sp={sp} r={ratio} bs={bs} nsel={nsel} {kind}")
+    rng = np.random.default_rng(T + nsel)
+    s = (rng.integers(-4, 5, size=(B, S, T)).astype(np.float32) if kind == "ties"
+         else rng.standard_normal((B, S, T)).astype(np.float32))
+    c = np.minimum(oracle.visible_count(np.arange(S), sp, ratio), T)
+    s[:, np.arange(T)[None, :] >= c[:, None]] = -np.inf
+    bits = dsa.dsa_candidate_blocks(torch.from_numpy(s).to(DEV), sp, ratio, bs, nsel)
+    assert _launched()[1] == "candidate_blocks"
+    nblk = -(-T // bs)
+    got, padbits = _unpack_bits(bits.cpu().numpy(), nblk)
+    assert not padbits.any()
+    for b in range(B):
+        for t in range(S):
+            exp = oracle.candidate_blocks_row(s[b, t].astype(np.float64), int(c[t]), nsel, bs)
+            np.testing.assert_array_equal(got[b, t], exp, err_msg=f"row ({b},{t})")
+
+
+@pytest.mark.parametrize("B,S,sp,T,H,DI,ratio,bs,nsel,fmt", [
+    (4, 1, 65535, 16384, 32, 128, 4, 8, 300, "bf16"),  # decode: keys outside the candidates are not read
+    (2, 70, 0, 70, 32, 128, 1, 8, 5, "bf16"),          # 16 queries per block
+    (1, 200, 37, 130, 20, 128, 1, 4, 10, "bf16"),      # the key-streaming prefill kernel
+    (1, 9, 0, 9, 4, 32, 1, 2, 2, "f32"),
+    (3, 1, 4000, 1000, 32, 128, 4, 8, 30, "mxfp4"),
+    (1, 100, 0, 100, 32, 128, 1, 8, 4, "mxfp4"),
+])
+def test_index_scores_masked(B, S, sp, T, H, DI, ratio, bs, nsel, fmt):
+    """A consumer layer's scores inside the candidate blocks (the oracle's scores there, -inf
+    elsewhere), with candidates the oracle chose from another layer's scores."""
+    dsa = _dsa()
+    _log(f"masked index scores B={B} S={S} sp={sp} T={T} H={H} DI={DI} r={ratio} bs={bs} nsel={nsel} {fmt}")
+    g = torch.Generator().manual_seed(T * 3 + S + nsel)
+    src = torch.randn(B, S, T, generator=g).double().numpy()
+    mask = oracle.candidate_mask(src, sp, ratio, nsel, bs)
+    nblk = -(-T // bs)
+    blocks = np.zeros((B, S, nblk), dtype=bool)
+    c = oracle.visible_count(np.arange(S), sp, ratio)
+    for b in range(B):
+        for t in range(S):
+            blocks[b, t] = oracle.candidate_blocks_row(src[b, t], int(min(T, c[t])), nsel, bs)
+    cand = (torch.from_numpy(_pack_bits(blocks)).to(DEV), bs)
+    w = (torch.randn(B, S, H, generator=g) * 0.5)
+    w_scale = DI ** -0.5 * H ** -0.5
+    if fmt == "mxfp4":
+        qp, qs = dsa_synth.encode_mxfp4_e8m0(torch.randn(B, S, H, DI, generator=g), 32)
+        kp, ks = dsa_synth.encode_mxfp4_e8m0(torch.randn(B, T, DI, generator=g), 32)
+        wb = w.to(torch.bfloat16)
+        got = dsa.dsa_index_scores_mxfp4(qp.to(DEV), qs.to(DEV), kp.to(DEV), ks.to(DEV), wb.to(DEV), w_scale, sp,
+                                         ratio, candidates=cand).cpu().numpy()
+        q64, k64 = oracle.mxfp4_rows_decode(qp, qs), oracle.mxfp4_rows_decode(kp, ks)
+        w64 = wb.float().numpy().astype(np.float64)
+    else:
+        dt = torch.float32 if fmt == "f32" else torch.bfloat16
+        qI = torch.randn(B, S, H, DI, generator=g).to(dt)
+        kI = torch.randn(B, T, DI, generator=g).to(dt)
+        wd = w.to(dt)
+        got = dsa.dsa_index_scores_masked(qI.to(DEV), kI.to(DEV), wd.to(DEV), w_scale, sp, ratio, cand).cpu().numpy()
+        q64, k64 = qI.float().numpy().astype(np.float64), kI.float().numpy().astype(np.float64)
+        w64 = wd.float().numpy().astype(np.float64)
+    _log(f"  launches: {_launched()}")
+    exp = np.where(mask, oracle.index_scores(q64, k64, w64, w_scale, sp, ratio), -np.inf)
+    for b in range(B):
+        for t in range(S):
+            e = exp[b, t]
+            inv = np.isinf(e)
+            assert np.all(np.isneginf(got[b, t][inv])), f"({b},{t}): outside the candidates must be -inf"
+            bound = score_bound(q64[b, t][None], k64[b], w64[b, t][None], w_scale)[0]
+            assert np.all(np.abs(got[b, t][~inv] - e[~inv]) <= 1e-5 * bound[~inv] + 1e-30), (b, t)
+
+
+def _check_blocks_banded(chosen, scores_row, c, nsel, bs, ctx):
+    """The chosen blocks are a valid pick for oracle scores that differ from the GPU's by rounding:
+    exactly min(nsel, visible blocks) of them, and blocks on either side of the threshold only
+    within 1e-3 relative of it."""
+    cb = -(-c // bs)
+    bmax = np.array([scores_row[i * bs:min((i + 1) * bs, c)].max() for i in range(cb)])
+    n = min(nsel, cb)
+    assert chosen[:cb].sum() == n and not chosen[cb:].any(), ctx
+    if cb <= nsel:
+        return
+    order = np.sort(bmax)[::-1]
+    sk, sk1 = order[n - 1], order[n]
+    delta = 1e-3 * max(abs(sk), abs(sk1))
+    assert np.all(bmax[chosen[:cb]] >= sk - delta), ctx
+    assert np.all(bmax[~chosen[:cb]] <= sk + delta), ctx
+
+
+@pytest.mark.parametrize("name", ["decode_b16_ctx64k_r1", "decode_b16_ctx64k_r1_mxfp4"])
+def test_two_level_step(name):
+    """The page's two-level selection at its real shape (ratio 1, 64K context, 2048 blocks of 8):
+    the source layer's scores give the candidate blocks; a consumer layer scores inside them with
+    its own index queries and weights, selects and attends.  Candidates are checked against the
+    oracle's source scores by the banded rule, the consumer's index rows and attention against the
+    oracle given those candidates."""
+    dsa = _dsa()
+    w = dsa_synth.get(name)
+    bs, nsel = 8, 2048
+    _log(f"two-level step {name}: T={w.T}, {nsel} blocks of {bs}")
+    src = dsa_synth.generate(w, seed=0, device=DEV)   # the candidate source layer
+    con = dsa_synth.generate(w, seed=1, device=DEV)   # a consumer layer (own q, index q, weights)
+    w_scale = w.D_I ** -0.5 * w.H_I ** -0.5
+    mx = w.index_fmt == "mxfp4"
+    if mx:
+        s_src = dsa.dsa_index_scores_mxfp4(src["qI_fp4"], src["qI_scale"], src["kI_fp4"], src["kI_scale"], src["w"],
+                                           w_scale, w.start_pos, w.ratio)
+    else:
+        s_src = dsa.dsa_index_scores(src["qI"], src["kI"], src["w"], w_scale, w.start_pos, w.ratio)
+    bits = dsa.dsa_candidate_blocks(s_src, w.start_pos, w.ratio, bs, nsel)
+    # the consumer reads the source's index keys and compressed KV (shared caches) with its own queries
+    if mx:
+        s_con = dsa.dsa_index_scores_mxfp4(con["qI_fp4"], con["qI_scale"], src["kI_fp4"], src["kI_scale"], con["w"],
+                                           w_scale, w.start_pos, w.ratio, candidates=(bits, bs))
+    else:
+        s_con = dsa.dsa_index_scores_masked(con["qI"], src["kI"], con["w"], w_scale, w.start_pos, w.ratio, (bits, bs))
+    o, idx = dsa.dsa_sparse_attn_select(s_con, con["q"], con["kv_win"], src["kv_comp"], con["sink"],
+                                        index_topk=w.index_topk, start_pos=w.start_pos, ratio=w.ratio, W=w.W,
+                                        scale=w.D ** -0.5)
+    torch.cuda.synchronize()
+    cpu_src = _device_set_to_cpu(w, src)
+    cpu_con = _device_set_to_cpu(w, con)
+    q64s, k64 = _index_f64(cpu_src)
+    q64c, _ = _index_f64(cpu_con)
+    c = int(min(w.T, oracle.visible_count(0, w.start_pos, w.ratio)))
+    nblk = -(-w.T // bs)
+    got_blocks, _ = _unpack_bits(bits.cpu().numpy(), nblk)
+    exp_src = oracle.index_scores(q64s, k64, cpu_src["w"].float().numpy().astype(np.float64), w_scale, w.start_pos,
+                                  w.ratio)
+    exp_con = oracle.index_scores(q64c, k64, cpu_con["w"].float().numpy().astype(np.float64), w_scale, w.start_pos,
+                                  w.ratio)
+    idx_cpu = idx.cpu().numpy()
+    win = oracle.window_rows(w.W, w.B, w.S, w.start_pos)
+    rules = {}
+    for b in range(w.B):
+        _check_blocks_banded(got_blocks[b, 0], exp_src[b, 0], c, nsel, bs, f"({b},0) blocks")
+        mask = np.repeat(got_blocks[b, 0], bs)[:w.T] & (np.arange(w.T) < c)
+        masked = np.where(mask, exp_con[b, 0], -np.inf)
+        np.testing.assert_array_equal(idx_cpu[b, 0, :w.Wc], win[b, 0])
+        sel = idx_cpu[b, 0, w.Wc:]
+        assert np.all(mask[sel[sel >= 0] - w.n_win]), "a selected row outside the candidate blocks"
+        rule = check_topk_row(sel, masked, w.K, c, w.n_win, ctx=f"{name} ({b},0)")
+        rules[rule] = rules.get(rule, 0) + 1
+    kv = oracle.kv_concat(cpu_con["kv_win"], cpu_src["kv_comp"])
+    exp_o = oracle.sparse_attn(cpu_con["q"], kv, cpu_con["sink"], idx_cpu, w.D ** -0.5)
+    err = max_abs_err(o.float().cpu().numpy(), exp_o)
+    _log(f"  top-k rules {rules}, attention max abs err {err:.3e}")
+    assert err <= ATTN_TOL["bf16"], err
