@@ -51,6 +51,9 @@ LINE_WORKLOADS = ["decode_b32_ctx8k", "prefill_s8k", "decode_b16_ctx64k", "prefi
 # rows (the page's index sources sit every 4 layers from layer 20 on, all reading layer 20's
 # compressed KV), each layer with its own queries, window KV and sinks
 GROUP_LAYERS = 4
+# workloads where the two-level selection is timed: the page's candidate source (layer 20, ratio 1)
+# keeps 2048 blocks of 8 compressed positions, and the later index sources score only inside them
+TWO_LEVEL = {"decode_b16_ctx64k_r1": (8, 2048), "decode_b16_ctx64k_r1_mxfp4": (8, 2048)}
 GROUP_WORKLOADS = ["decode_b32_ctx8k", "decode_b16_ctx64k_r2", "decode_b16_ctx64k_r1", "prefill_s8k_r1",
                    "decode_b16_ctx64k_r1_mxfp4"]
 HOST_CORES = 16  # the CPU share of one GPU on the benchmark machines
@@ -374,6 +377,36 @@ def run_workload(w, a, log):
         rest_ms = _graph_time_ms(lambda: rest(0), reps=2, inner=20)
         index_ms = _graph_time_ms(lambda: index(0), reps=2, inner=20)
 
+    # the two-level selection: candidate blocks from this step's scores, then a consumer layer's
+    # index scores inside them (the same index queries here; only the keys read differ)
+    two_level = None
+    if w.name in TWO_LEVEL:
+        bs, nsel = TWO_LEVEL[w.name]
+        s0, b0 = sets[0], bufs[0]
+        nw = ((w.T + bs - 1) // bs + 31) // 32
+        bits = torch.empty(w.B, w.S, nw, dtype=torch.int32, device=dev)
+        masked = torch.empty_like(b0["scores"])
+
+        def cand_blocks():
+            dsa.dsa_candidate_blocks(b0["scores"], w.start_pos, w.ratio, bs, nsel, out=bits)
+
+        def consumer():
+            if mx:
+                dsa.dsa_index_scores_mxfp4(s0["qI_fp4"], s0["qI_scale"], s0["kI_fp4"], s0["kI_scale"], s0["w"], w_scale,
+                                           w.start_pos, w.ratio, out=masked, candidates=(bits, bs))
+            else:
+                dsa.dsa_index_scores_masked(s0["qI"], s0["kI"], s0["w"], w_scale, w.start_pos, w.ratio, (bits, bs),
+                                            out=masked)
+
+        step(0)
+        cb_ms = _graph_time_ms(cand_blocks, reps=2, inner=20)
+        cons_ms = _graph_time_ms(consumer, reps=2, inner=20)
+        kept = float(torch.stack([((bits >> k) & 1).sum() for k in range(32)]).sum().item()) / (w.B * w.S)
+        two_level = {"block_size": bs, "blocks_kept": nsel, "candidate_blocks_us": round(cb_ms * 1e3, 2),
+                     "masked_index_us": round(cons_ms * 1e3, 2), "full_index_us": round(index_ms * 1e3, 2),
+                     "blocks_chosen_per_query": kept}
+        del bits, masked
+
     # a layer group: the step on the index source layer, then the attention of the layers that reuse
     # its index rows (own queries, window KV and sinks; the shared compressed KV)
     group = None
@@ -467,6 +500,7 @@ def run_workload(w, a, log):
                                                           + w.B * w.S * w.T * 4) / (index_ms * 1e-3) / 1e9, 1),
             "index_rows": "mxfp4 e2m1 + E8M0/32" if mx else w.dtype},
         "layer_group": group,
+        "two_level": two_level,
         "config": {"workload": w.name, "mode": w.mode, "batch": w.B, "query_tokens": w.S, "context": w.end_pos,
                    "heads": w.H, "head_dim": w.D, "window": w.W, "compress_ratio": w.ratio, "index_heads": w.H_I,
                    "index_head_dim": w.D_I, "index_topk": w.index_topk,
@@ -479,7 +513,9 @@ def run_workload(w, a, log):
         f"{roof['achieved']} {roof['unit']} = {roof['frac'] * 100:.1f}% of peak"
         + ("" if rest_ms is None else f"; index+select {rest_ms * 1e3:.2f} us")
         + ("" if group is None else f"; {GROUP_LAYERS}-layer group {group['us']} us "
-           f"({group['speedup_vs_a_step_per_layer']}x a step per layer)"))
+           f"({group['speedup_vs_a_step_per_layer']}x a step per layer)")
+        + ("" if two_level is None else f"; candidate blocks {two_level['candidate_blocks_us']} us, masked index "
+           f"{two_level['masked_index_us']} us (full {two_level['full_index_us']} us)"))
     for bf in bufs:
         bf.clear()
     keep = set0

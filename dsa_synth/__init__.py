@@ -31,6 +31,7 @@ __all__ = [
     "generate",
     "encode_fp4_e2m1_e4m3",
     "encode_mxfp4_e8m0",
+    "rope_freqs",
     "scaled",
     "nbytes",
 ]
@@ -238,6 +239,19 @@ def encode_mxfp4_e8m0(x: torch.Tensor, block: int = 32):
     packed = code[..., 0::2] | (code[..., 1::2] << 4)
     scales = (e + 127).to(torch.uint8).reshape(*x.shape[:-1], x.shape[-1] // block)
     return packed.contiguous(), scales.contiguous()
+
+
+def rope_freqs(positions, rope_dim: int, theta: float = 160000.0, device="cpu") -> torch.Tensor:
+    """A rotary table float32 [n, rope_dim/2, 2] of (cos, sin) for the given positions.
+
+    The pages build theirs with `precompute_freqs_cis` (YaRN; body not shown) from the config's
+    compress_rope_theta = 160000; this generator uses the plain angles position * theta**(-2i/rope_dim).
+    The table is an input of the epilogue and cache-write kernels, so parity does not depend on it.
+    """
+    pos = torch.as_tensor(positions, dtype=torch.float64, device=device)
+    inv = theta ** (-torch.arange(0, rope_dim, 2, dtype=torch.float64, device=device) / rope_dim)
+    ang = pos[:, None] * inv[None, :]
+    return torch.stack([torch.cos(ang), torch.sin(ang)], dim=-1).to(torch.float32).contiguous()
 
 
 def generate(w: Workload, seed: int = 0, device="cpu") -> dict:

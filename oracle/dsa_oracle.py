@@ -29,6 +29,11 @@ model pages by the class or function that holds the step:
                       compressed positions from its scores (`select_candidate_blocks`,
                       body not on the pages), and later indexers mask their scores to
                       -inf outside those blocks before their own top-k
+* output epilogue   -- `Attention.forward`: the inverse rotary embedding on the last
+                      rope_head_dim dims of o, at the query's position
+* cache write       -- `_compress_kv`: rotary embedding of the latent's last
+                      rope_head_dim dims at the group's position, fp4 with E4M3 scales
+                      per 16, written into the compressed cache
 * MXFP4 index q/k   -- `Indexer.forward` quantises the index queries and keys to
                       fp4, and `_compress_kv` states the indexer's blocks: 32
                       elements per E8M0 (power-of-two) scale.  The scores are the
@@ -63,6 +68,12 @@ __all__ = [
     "e4m3_decode",
     "fp4_rows_decode",
     "e8m0_decode",
+    "rope_rotate",
+    "bf16_rne",
+    "e4m3_rne",
+    "rope_rotate_bf16",
+    "fp4_quant_e4m3_g16",
+    "compress_kv_write",
     "mxfp4_rows_decode",
     "kv_concat",
     "sparse_attn",
@@ -311,6 +322,118 @@ def mxfp4_rows_decode(packed, scales, block: int = 32) -> np.ndarray:
     vals[..., 0::2] = e2m1_decode(p & 0xF)
     vals[..., 1::2] = e2m1_decode(p >> 4)
     return vals * np.repeat(e8m0_decode(sc), block, axis=-1)
+
+
+# ----------------------------------------------------------------------------
+# rotary embedding and the compressed-cache write
+# ----------------------------------------------------------------------------
+def rope_rotate(x, freqs, inverse: bool = False) -> np.ndarray:
+    """Rotary embedding of the last 2*P dims of x [..., S, H, D] by freqs [S, P, 2] (cos, sin) of
+    each row's position (`apply_rotary_emb`, body not on the pages; reading: dims 2i, 2i+1 of the
+    rotated part are the real and imaginary parts of one complex number, multiplied by
+    cos + i sin, or by its conjugate for the inverse).  Exact, float64."""
+    x = np.array(x, dtype=np.float64)
+    f = np.asarray(freqs, dtype=np.float64)
+    P = f.shape[-2]
+    cos = f[..., 0][:, None, :]  # [S, 1, P]: the same angle for every head
+    sin = f[..., 1][:, None, :]
+    if inverse:
+        sin = -sin
+    a = x[..., -2 * P::2].copy()
+    b = x[..., -2 * P + 1::2].copy()
+    x[..., -2 * P::2] = a * cos - b * sin
+    x[..., -2 * P + 1::2] = a * sin + b * cos
+    return x
+
+
+def bf16_rne(x) -> np.ndarray:
+    """float32 values rounded to bfloat16, to nearest with ties to even (returned as float32)."""
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    nan = np.isnan(np.asarray(x, dtype=np.float32))
+    out = (r & 0xFFFFFFFF).astype(np.uint32).view(np.float32)
+    return np.where(nan, np.float32(np.nan), out)
+
+
+def e4m3_rne(x) -> np.ndarray:
+    """Non-negative float32 values rounded to the nearest FP8 E4M3 value, ties to the even code,
+    saturating at 448 (reading: a scale past the largest E4M3 value would otherwise be NaN).
+    Returned as float64 (exact)."""
+    v = np.asarray(x, dtype=np.float64)
+    e = np.floor(np.log2(np.where(v > 0, v, 1.0)))
+    e = np.clip(e, -6, 8)                     # subnormals share the step of exponent -6
+    step = np.ldexp(1.0, (e - 3).astype(np.int64))  # 3 mantissa bits
+    q = v / step                              # exact: a power-of-two division
+    r = np.floor(q)
+    frac = q - r
+    r = np.where((frac > 0.5) | ((frac == 0.5) & (np.mod(r, 2) == 1)), r + 1, r)
+    return np.minimum(r * step, 448.0)
+
+
+_E2M1_MAG = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def rope_rotate_bf16(x_bf16, freqs) -> np.ndarray:
+    """The page's rotation of a bf16 tensor (`apply_rotary_emb` on a bf16 view): float32 products and
+    sums (no fused multiply-add), rounded back to bf16.  x [..., S, H, D] as float values, freqs
+    [S, P, 2] float32.  Returns float32 values that are bf16."""
+    x = np.array(x_bf16, dtype=np.float32)
+    f = np.asarray(freqs, dtype=np.float32)
+    P = f.shape[-2]
+    cos = f[..., 0][:, None, :]
+    sin = f[..., 1][:, None, :]
+    a = x[..., -2 * P::2].copy()
+    b = x[..., -2 * P + 1::2].copy()
+    re = np.float32(a * cos) - np.float32(b * sin)
+    im = np.float32(a * sin) + np.float32(b * cos)
+    x[..., -2 * P::2] = bf16_rne(re)
+    x[..., -2 * P + 1::2] = bf16_rne(im)
+    return x
+
+
+def fp4_quant_e4m3_g16(x) -> tuple:
+    """fp4 e2m1 with one E4M3 scale per 16 consecutive elements (`_compress_kv`: groups of 16 with
+    E4M3 scales; the quantiser's body is not on the pages).  Reading, each step in float32 as a
+    kernel would take it: scale = E4M3(amax / 6); code = the e2m1 value nearest x / scale (ties to
+    the even code, 6 at most, sign kept); a zero scale gives zero codes.  Returns (packed uint8
+    [..., D/2] with element 2k in the low nibble of byte k, scale codes uint8 [..., D/16])."""
+    x = np.asarray(x, dtype=np.float32)
+    g = x.reshape(*x.shape[:-1], x.shape[-1] // 16, 16)
+    amax = np.abs(g).max(axis=-1)
+    scale = e4m3_rne(np.float32(amax) / np.float32(6.0)).astype(np.float32)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        y = np.where(scale[..., None] > 0, g / scale[..., None], np.float32(0.0)).astype(np.float32)
+    m = np.abs(y).astype(np.float64)
+    code = np.zeros(m.shape, dtype=np.int64)
+    for i in range(7):
+        mid = 0.5 * (_E2M1_MAG[i] + _E2M1_MAG[i + 1])
+        code += (m > mid) | ((m == mid) & ((i + 1) % 2 == 0))
+    code = np.minimum(code, 7) | np.where(y < 0, 8, 0)
+    code = code.reshape(x.shape).astype(np.uint8)
+    packed = (code[..., 0::2] | (code[..., 1::2] << 4)).astype(np.uint8)
+    # scale codes: E4M3 bit patterns of the (non-negative) scale values
+    sc = _e4m3_code(scale.astype(np.float64))
+    return packed, sc
+
+
+def _e4m3_code(v) -> np.ndarray:
+    """E4M3 code of non-negative values on the E4M3 grid."""
+    v = np.asarray(v, dtype=np.float64)
+    e = np.floor(np.log2(np.where(v > 0, v, 1.0))).astype(np.int64)
+    normal = v >= 2.0 ** -6
+    exp_field = np.where(normal, e + 7, 0)
+    mant = np.where(normal, v / np.ldexp(1.0, e) - 1.0, v / 2.0 ** -6) * 8
+    code = (exp_field << 3) | np.rint(mant).astype(np.int64)
+    return np.where(v > 0, code, 0).astype(np.uint8)
+
+
+def compress_kv_write(latent_bf16, freqs, rope_dim: int) -> tuple:
+    """`_compress_kv` after the compressor: the latent rows [B, n, D] (bf16 values) rotated on their
+    last rope_dim dims by freqs [n, rope_dim/2, 2] of each group's position (in the page's precision),
+    then fp4 with E4M3 scales per 16.  Returns (packed [B, n, D/2], scales [B, n, D/16])."""
+    x = np.asarray(latent_bf16, dtype=np.float32)
+    rot = rope_rotate_bf16(x[:, :, None, :], freqs)[:, :, 0, :]  # one 'head'
+    return fp4_quant_e4m3_g16(rot)
 
 
 # ----------------------------------------------------------------------------

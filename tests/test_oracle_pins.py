@@ -608,3 +608,99 @@ def test_planted_mxfp4_slips_are_caught(monkeypatch):
     with pytest.raises(AssertionError):
         test_e8m0_golden_and_library()
     monkeypatch.undo()
+
+
+# ---------------------------------------------------------------- output epilogue and cache write
+def test_bf16_rne_against_torch():
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal(20000) * np.exp(rng.standard_normal(20000) * 8)).astype(np.float32)
+    # exact ties: a bf16 value plus half of its last place, for even and odd last bits
+    base = torch.randn(2000).to(torch.bfloat16).float().numpy()
+    half = (base.view(np.uint32) | np.uint32(0x8000)).view(np.float32)
+    x = np.concatenate([x, half, np.array([0.0, -0.0, np.inf, -np.inf], dtype=np.float32)])
+    lib = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    np.testing.assert_array_equal(oracle.bf16_rne(x), lib)
+    assert np.isnan(oracle.bf16_rne(np.array([np.nan], dtype=np.float32))[0])
+
+
+def test_e4m3_rne_against_torch():
+    rng = np.random.default_rng(12)
+    v = np.abs(rng.standard_normal(20000) * np.exp(rng.uniform(-9, 6, 20000))).astype(np.float32)
+    v = v[v <= 448]
+    # exact ties between neighbouring E4M3 values, subnormal and normal
+    grid = np.unique(oracle.e4m3_decode(np.arange(0, 0x7F)))
+    mids = ((grid[1:] + grid[:-1]) / 2).astype(np.float32)
+    v = np.concatenate([v, mids, np.array([0.0, 2.0 ** -10, 2.0 ** -9, 448.0], dtype=np.float32)])
+    lib = torch.from_numpy(v).to(torch.float8_e4m3fn).double().numpy()
+    np.testing.assert_array_equal(oracle.e4m3_rne(v), lib)
+    # reading: past the largest finite value the scale saturates at 448 (torch gives NaN)
+    assert oracle.e4m3_rne(np.array([500.0, 1e6], dtype=np.float32)).tolist() == [448.0, 448.0]
+
+
+def test_rope_rotate_complex_and_inverse():
+    rng = np.random.default_rng(13)
+    S, H, D, P = 6, 4, 24, 5
+    x = rng.standard_normal((2, S, H, D))
+    ang = rng.standard_normal((S, P)) * 4
+    freqs = np.stack([np.cos(ang), np.sin(ang)], -1)
+    y = oracle.rope_rotate(x, freqs)
+    np.testing.assert_array_equal(y[..., : D - 2 * P], x[..., : D - 2 * P])  # leading dims untouched
+    z = x[..., D - 2 * P:].reshape(2, S, H, P, 2)
+    zc = (z[..., 0] + 1j * z[..., 1]) * np.exp(1j * ang)[None, :, None, :]
+    np.testing.assert_allclose(y[..., D - 2 * P::2], zc.real, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(y[..., D - 2 * P + 1::2], zc.imag, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(oracle.rope_rotate(y, freqs, inverse=True), x, rtol=0, atol=1e-13)
+
+
+def test_rope_rotate_bf16_against_torch_complex():
+    """The page's rotation of a bf16 view: complex64 product, written back as bf16."""
+    rng = np.random.default_rng(14)
+    S, H, D, P = 7, 3, 64, 16
+    x = torch.randn(S, H, D).to(torch.bfloat16)
+    ang = (rng.standard_normal((S, P)) * 3).astype(np.float32)
+    freqs = np.stack([np.cos(ang), np.sin(ang)], -1).astype(np.float32)
+    ours = oracle.rope_rotate_bf16(x.float().numpy(), freqs)
+    xc = torch.view_as_complex(x[..., -2 * P:].float().unflatten(-1, (-1, 2)).contiguous())
+    fc = torch.complex(torch.from_numpy(freqs[..., 0]), torch.from_numpy(freqs[..., 1]))[:, None, :]
+    lib = torch.view_as_real(xc * fc).flatten(-2).to(torch.bfloat16).float().numpy()
+    np.testing.assert_array_equal(ours[..., -2 * P:], lib)
+    np.testing.assert_array_equal(ours[..., : D - 2 * P], x[..., : D - 2 * P].float().numpy())
+
+
+def test_fp4_quantiser_against_generator_encoder():
+    """The oracle's fp4/E4M3 quantiser (numpy, float32 steps) and the generator's encoder (torch)
+    are independent codings of one rule: the same bytes."""
+    import dsa_synth
+
+    g = torch.Generator().manual_seed(15)
+    x = torch.randn(6, 33, 512, generator=g) * torch.exp(torch.randn(6, 33, 1, generator=g) * 2)
+    x[0, 0, :16] = 0.0
+    p1, s1 = dsa_synth.encode_fp4_e2m1_e4m3(x, 16)
+    p2, s2 = oracle.fp4_quant_e4m3_g16(x.numpy())
+    np.testing.assert_array_equal(p2, p1.numpy())
+    np.testing.assert_array_equal(s2, s1.numpy())
+    # decoding gives values within the widest half step (1 x scale) of the input, or past the largest
+    # e2m1 value when the scale rounded down; a zero scale only for blocks whose amax/6 rounds to 0
+    dec = oracle.fp4_rows_decode(p2, s2)
+    sc = np.repeat(oracle.e4m3_decode(s2), 16, axis=-1)
+    xs = x.double().numpy()
+    pos = sc > 0
+    assert np.all(np.abs(dec - xs)[pos] <= np.maximum(sc, np.abs(xs) - 6 * sc)[pos])
+    assert np.all(np.abs(xs[~pos]) < 6 * 2.0 ** -10)
+
+
+def test_compress_kv_write_composition():
+    rng = np.random.default_rng(16)
+    B, n, D, rd = 2, 5, 64, 16
+    lat = torch.randn(B, n, D).to(torch.bfloat16).float().numpy()
+    ang = (rng.standard_normal((n, rd // 2)) * 3).astype(np.float32)
+    freqs = np.stack([np.cos(ang), np.sin(ang)], -1).astype(np.float32)
+    packed, scales = oracle.compress_kv_write(lat, freqs, rd)
+    assert packed.shape == (B, n, D // 2) and scales.shape == (B, n, D // 16)
+    rot = oracle.rope_rotate_bf16(lat[:, :, None, :], freqs)[:, :, 0, :]
+    p2, s2 = oracle.fp4_quant_e4m3_g16(rot)
+    np.testing.assert_array_equal(packed, p2)
+    np.testing.assert_array_equal(scales, s2)
+    # the first D - rd dims are quantised unrotated
+    p3, _ = oracle.fp4_quant_e4m3_g16(lat)
+    np.testing.assert_array_equal(packed[..., : (D - rd) // 2], p3[..., : (D - rd) // 2])
