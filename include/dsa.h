@@ -11,6 +11,8 @@
  *   dsa_window_idx    the sliding-window part of each query's index row
  *   dsa_select        window part and top-k part of the index rows in one launch
  *   dsa_sparse_attn   attend all heads over the rows an index row names
+ *   dsa_sparse_attn_rope, dsa_rope_inverse  the output's inverse rotary embedding (fused)
+ *   dsa_compress_kv_write  rotary embedding + fp4 quantisation of new compressed-cache rows
  *   dsa_sparse_attn_select  dsa_select then dsa_sparse_attn, one launch where the decode
  *                     attention kernel can select its own index rows
  *   dsa_sparse_attn_step  the whole step: dsa_index_scores then dsa_sparse_attn_select, one
@@ -335,6 +337,44 @@ size_t dsa_sparse_attn_workspace_size(int dtype, int B, int S, int H, int D, int
    L = dsa_window_cols(S, start_pos, W) + min(index_topk, T) entries (0 when none). */
 size_t dsa_step_workspace_size(int dtype, int B, int S, int H, int D, int T, int index_topk, int start_pos,
                                int W);
+
+/*
+ * Sparse attention followed by the inverse rotary embedding of its output (`Attention.forward`:
+ * `apply_rotary_emb(o[..., -rope_head_dim:], freqs_cis, True)` right after `sparse_attn`): the
+ * results of dsa_sparse_attn, then for each query t (positions of this call) and head, the pairs
+ * (o[2i], o[2i+1]) of its last rope_dim dims replaced by (o[2i] + i o[2i+1]) (cos - i sin), with
+ * (cos, sin) = freqs[t][i].  The decode and prefill kernels rotate in their epilogue (before the
+ * output is rounded to bf16); other shapes run dsa_rope_inverse after the attention.
+ *
+ *   freqs [S, rope_dim/2, 2] float32 (cos, sin), 16-byte aligned; rope_dim a multiple of 16, <= D.
+ *   Other arguments and errors: those of dsa_sparse_attn.
+ */
+int dsa_sparse_attn_rope(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
+                         const int32_t* idx, int L, float scale, void* o, int dtype, int B, int S, int H, int D,
+                         const float* freqs, int rope_dim, void* workspace, size_t workspace_bytes,
+                         dsa_stream_t stream);
+
+/* The inverse rotary embedding alone, in place on o [B, S, H, D] (dtype), as dsa_sparse_attn_rope
+   applies it. */
+int dsa_rope_inverse(void* o, int dtype, int B, int S, int H, int D, const float* freqs, int rope_dim,
+                     dsa_stream_t stream);
+
+/*
+ * The compressed-cache write of `_compress_kv`: the latent rows are rotated on their last rope_dim
+ * dims (freqs of each row's group position), fp4-quantised with one E4M3 scale per 16 elements and
+ * stored at rows row0 .. row0+n-1 of the fp4 cache (the layout DSA_KV_FP4_E4M3_G16 reads).  Each
+ * step is taken in the precision of the page's bf16 tensors: float32 products and sums without
+ * fused multiply-adds, rounded to bf16; scale = E4M3(amax / 6) to nearest-even, saturated at 448;
+ * code = the e2m1 value nearest x / scale (ties to the even code, at most 6).
+ *
+ *   latent [B, n, D] bf16, batch stride latent_batch_stride (elements)
+ *   freqs  [n, rope_dim/2, 2] float32 (cos, sin), 16-byte aligned; rope_dim a multiple of 16, <= D
+ *   rows   [B, >= row0 + n, D/2] uint8 (batch stride in bytes, 8-byte aligned rows)
+ *   scales [B, >= row0 + n, D/16] uint8 (batch stride in bytes)
+ */
+int dsa_compress_kv_write(const void* latent, int64_t latent_batch_stride, int B, int n, int D, const float* freqs,
+                          int rope_dim, uint8_t* rows, int64_t rows_batch_stride, uint8_t* scales,
+                          int64_t scales_batch_stride, int64_t row0, dsa_stream_t stream);
 
 /*
  * The index rows and the attention over them (`Indexer.forward`, `get_window_topk_idxs` and

@@ -118,6 +118,13 @@ def _load():
                                                  ctypes.POINTER(DsaKvSrc), ctypes.POINTER(DsaKvSrc), vp, f32, vp,
                                                  i32, i32, i32, i32, i32, vp, vp, vp]
     lib.dsa_sparse_attn_step_noalloc.restype = i32
+    lib.dsa_sparse_attn_rope.argtypes = [vp, ctypes.POINTER(DsaKvSrc), ctypes.POINTER(DsaKvSrc), vp, vp, i32, f32, vp,
+                                         i32, i32, i32, i32, i32, vp, i32, vp, ctypes.c_size_t, vp]
+    lib.dsa_sparse_attn_rope.restype = i32
+    lib.dsa_rope_inverse.argtypes = [vp, i32, i32, i32, i32, i32, vp, i32, vp]
+    lib.dsa_rope_inverse.restype = i32
+    lib.dsa_compress_kv_write.argtypes = [vp, i64, i32, i32, i32, vp, i32, vp, i64, vp, i64, i64, vp]
+    lib.dsa_compress_kv_write.restype = i32
     lib.dsa_sparse_attn_workspace_size.argtypes = [i32, i32, i32, i32, i32, i32]
     lib.dsa_sparse_attn_workspace_size.restype = ctypes.c_size_t
     return lib
@@ -546,6 +553,59 @@ def dsa_sparse_attn(q, kv_win, kv_comp, sink, idx, scale: float, comp_scales=Non
     return out
 
 
+def dsa_sparse_attn_rope(q, kv_win, kv_comp, sink, idx, scale: float, freqs, comp_scales=None, out=None,
+                         workspace=None, stream=None):
+    """dsa_sparse_attn followed by the inverse rotary embedding of o's last 2*freqs.shape[1] dims
+    (freqs [S, rope_dim/2, 2] float32 cos/sin of the queries' positions), fused where the kernel can."""
+    B, S, H, D, dt, win, comp, out = _attn_operands(q, kv_win, kv_comp, sink, comp_scales, out)
+    _need_contig("idx", idx)
+    if idx.dim() != 3 or tuple(idx.shape[:2]) != (B, S) or idx.dtype != torch.int32:
+        raise DsaError(-2, "idx must be int32 [B, S, L]")
+    if freqs.dim() != 3 or freqs.shape[0] != S or freqs.shape[2] != 2 or freqs.dtype != torch.float32:
+        raise DsaError(-2, "freqs must be float32 [S, rope_dim/2, 2]")
+    _need_contig("freqs", freqs)
+    L = idx.shape[-1]
+    dev = _dev(q, kv_win, kv_comp, sink, idx, out, freqs)
+    workspace = _workspace(dsa_sparse_attn_workspace_size(dt, B, S, H, D, L), workspace, dev)
+    _check(lib.dsa_sparse_attn_rope(_ptr(q), ctypes.byref(win), ctypes.byref(comp), _ptr(sink), _ptr(idx), L,
+                                    float(scale), _ptr(out), dt, B, S, H, D, _ptr(freqs), 2 * freqs.shape[1],
+                                    _ptr(workspace), _wbytes(workspace), _stream(dev, stream)))
+    return out
+
+
+def dsa_rope_inverse(o, freqs, stream=None):
+    """In place: the inverse rotary embedding of o [B, S, H, D]'s last 2*freqs.shape[1] dims."""
+    _need_contig("o", o)
+    B, S, H, D = o.shape
+    if freqs.dim() != 3 or freqs.shape[0] != S or freqs.dtype != torch.float32:
+        raise DsaError(-2, "freqs must be float32 [S, rope_dim/2, 2]")
+    _need_contig("freqs", freqs)
+    dev = _dev(o, freqs)
+    _check(lib.dsa_rope_inverse(_ptr(o), _dtype_code(o), B, S, H, D, _ptr(freqs), 2 * freqs.shape[1],
+                                _stream(dev, stream)))
+    return o
+
+
+def dsa_compress_kv_write(latent, freqs, rows, scales, row0: int, stream=None):
+    """Rotate, fp4-quantise and store latent [B, n, D] bf16 at rows row0.. of the fp4 cache
+    (rows [B, R, D/2] uint8, scales [B, R, D/16] uint8; cache slices allowed)."""
+    if latent.dtype != torch.bfloat16 or latent.dim() != 3 or latent.stride(2) != 1 or latent.stride(1) != latent.shape[2]:
+        raise DsaError(-3, "latent must be bf16 [B, n, D] with dense rows")
+    B, n, D = latent.shape
+    if freqs.dim() != 3 or freqs.shape[0] != n or freqs.dtype != torch.float32:
+        raise DsaError(-2, "freqs must be float32 [n, rope_dim/2, 2]")
+    _need_contig("freqs", freqs)
+    for name, t, w in (("rows", rows, D // 2), ("scales", scales, D // 16)):
+        if t.dtype != torch.uint8 or t.dim() != 3 or t.shape[0] != B or t.shape[2] != w or t.stride(2) != 1 \
+                or t.stride(1) != w or t.shape[1] < row0 + n:
+            raise DsaError(-2, f"{name} must be uint8 [B, >= row0 + n, {w}] with dense rows")
+    dev = _dev(latent, freqs, rows, scales)
+    _check(lib.dsa_compress_kv_write(_ptr(latent), latent.stride(0), B, n, D, _ptr(freqs), 2 * freqs.shape[1],
+                                     _ptr(rows), rows.stride(0), _ptr(scales), scales.stride(0), int(row0),
+                                     _stream(dev, stream)))
+    return rows, scales
+
+
 def dsa_sparse_attn_select(scores, q, kv_win, kv_comp, sink, *, index_topk: int, start_pos: int, ratio: int,
                            W: int, scale: float, comp_scales=None, out=None, idx=None, workspace=None, stream=None):
     """Index rows (window + top-k, as dsa_select with offset kv_win.shape[1]) and the sparse attention
@@ -696,6 +756,9 @@ __all__ = [
     "dsa_window_idx",
     "dsa_sparse_attn",
     "dsa_sparse_attn_select",
+    "dsa_sparse_attn_rope",
+    "dsa_rope_inverse",
+    "dsa_compress_kv_write",
     "dsa_sparse_attn_step",
     "dsa_sparse_attn_step_noalloc",
     "dsa_sparse_attn_workspace_size",

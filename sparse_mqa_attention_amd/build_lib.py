@@ -11,7 +11,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
 SOURCES = ["abi.cpp", "index_scores.hip", "index_scores_prefill.hip", "index_scores_mxfp4.hip", "topk.hip", "sparse_attn.hip", "sparse_attn_decode.hip",
-           "sparse_attn_prefill_h16.hip", "sparse_attn_f32.hip", "noalloc.hip"]
+           "sparse_attn_prefill_h16.hip", "sparse_attn_f32.hip", "noalloc.hip",
+           "epilogue.hip"]
 ARCH = "gfx950"
 # packed fp32 VALU forms are kept out of the generated code
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",

@@ -126,7 +126,10 @@ int index_scores_mxfp4_launch(const uint8_t*, const uint8_t*, const uint8_t*, co
 void topk_plan(int, int, int, int64_t*, int64_t*);
 int window_idx_launch(int, int, int, int, int, int32_t*, int64_t, hipStream_t);
 int sparse_attn_bf16_launch(const void*, const dsa_kv_src*, const dsa_kv_src*, const float*, const int32_t*, int,
-                            float, void*, int, int, int, int, void*, hipStream_t);
+                            float, void*, int, int, int, int, void*, const float*, int, hipStream_t);
+int rope_inverse_launch(void*, int, int, int, int, int, const float*, int, hipStream_t);
+int compress_kv_write_launch(const void*, int64_t, int, int, int, int, const float*, uint8_t*, int64_t, uint8_t*,
+                             int64_t, int64_t, hipStream_t);
 int sparse_attn_f32_launch(const void*, const dsa_kv_src*, const dsa_kv_src*, const float*, const int32_t*, int,
                            float, void*, int, int, int, int, hipStream_t);
 size_t sparse_attn_bf16_workspace(int, int, int, int, int, bool);
@@ -404,10 +407,11 @@ static int check_src(const dsa_kv_src* s, const char* name, int dtype, int D, in
   return DSA_OK;
 }
 
-int dsa_sparse_attn(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
-                    const int32_t* idx, int L, float scale, void* o, int dtype, int B, int S, int H, int D,
-                    void* workspace, size_t workspace_bytes, dsa_stream_t stream) {
-  dsa::Entry entry_;
+// dsa_sparse_attn, with the output's inverse rotary embedding when rope is set
+static int sparse_attn_impl(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
+                            const int32_t* idx, int L, float scale, void* o, int dtype, int B, int S, int H, int D,
+                            void* workspace, size_t workspace_bytes, const float* rope, int rope_dim,
+                            dsa_stream_t stream) {
   if (dtype != DSA_F32 && dtype != DSA_BF16) return fail(DSA_ERR_DTYPE, "dsa_sparse_attn: dtype %d", dtype);
   if (B < 0 || S < 0 || H <= 0 || D <= 0 || L < 0)
     return fail(DSA_ERR_SHAPE, "dsa_sparse_attn: bad sizes B=%d S=%d H=%d D=%d L=%d", B, S, H, D, L);
@@ -440,9 +444,71 @@ int dsa_sparse_attn(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp
   dsa_kv_src empty{};
   const dsa_kv_src* cs = (comp && comp->n_rows > 0) ? comp : &empty;
   if (dtype == DSA_BF16)
-    return dsa::sparse_attn_bf16_launch(q, win, cs, sink, idx, L, scale, o, B, S, H, D, workspace,
+    return dsa::sparse_attn_bf16_launch(q, win, cs, sink, idx, L, scale, o, B, S, H, D, workspace, rope, rope_dim,
                                         (hipStream_t)stream);
-  return dsa::sparse_attn_f32_launch(q, win, cs, sink, idx, L, scale, o, B, S, H, D, (hipStream_t)stream);
+  rc = dsa::sparse_attn_f32_launch(q, win, cs, sink, idx, L, scale, o, B, S, H, D, (hipStream_t)stream);
+  if (rc || !rope) return rc;
+  return dsa::rope_inverse_launch(o, DSA_F32, B, S, H, D, rope, rope_dim, (hipStream_t)stream);
+}
+
+int dsa_sparse_attn(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
+                    const int32_t* idx, int L, float scale, void* o, int dtype, int B, int S, int H, int D,
+                    void* workspace, size_t workspace_bytes, dsa_stream_t stream) {
+  dsa::Entry entry_;
+  return sparse_attn_impl(q, win, comp, sink, idx, L, scale, o, dtype, B, S, H, D, workspace, workspace_bytes,
+                          nullptr, 0, stream);
+}
+
+static int check_rope(const float* freqs, int rope_dim, int D, const char* who) {
+  if (!freqs) return fail(DSA_ERR_NULL, "%s: NULL rotary table", who);
+  if (rope_dim <= 0 || rope_dim > D || rope_dim % 16)
+    return fail(DSA_ERR_SHAPE, "%s: rope_dim %d must be a multiple of 16 in (0, D=%d]", who, rope_dim, D);
+  if ((uintptr_t)freqs & 15) return fail(DSA_ERR_SHAPE, "%s: the rotary table must be 16-byte aligned", who);
+  return DSA_OK;
+}
+
+int dsa_sparse_attn_rope(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
+                         const int32_t* idx, int L, float scale, void* o, int dtype, int B, int S, int H, int D,
+                         const float* freqs, int rope_dim, void* workspace, size_t workspace_bytes,
+                         dsa_stream_t stream) {
+  dsa::Entry entry_;
+  if (B > 0 && S > 0) {
+    const int rc = check_rope(freqs, rope_dim, D, "dsa_sparse_attn_rope");
+    if (rc) return rc;
+  }
+  return sparse_attn_impl(q, win, comp, sink, idx, L, scale, o, dtype, B, S, H, D, workspace, workspace_bytes, freqs,
+                          rope_dim, stream);
+}
+
+int dsa_rope_inverse(void* o, int dtype, int B, int S, int H, int D, const float* freqs, int rope_dim,
+                     dsa_stream_t stream) {
+  dsa::Entry entry_;
+  if (dtype != DSA_F32 && dtype != DSA_BF16) return fail(DSA_ERR_DTYPE, "dsa_rope_inverse: dtype %d", dtype);
+  if (B < 0 || S < 0 || H <= 0 || D <= 0) return fail(DSA_ERR_SHAPE, "dsa_rope_inverse: bad sizes");
+  if (B == 0 || S == 0) return DSA_OK;
+  int rc = check_rope(freqs, rope_dim, D, "dsa_rope_inverse");
+  if (rc) return rc;
+  if (!o) return fail(DSA_ERR_NULL, "dsa_rope_inverse: NULL output");
+  return dsa::rope_inverse_launch(o, dtype, B, S, H, D, freqs, rope_dim, (hipStream_t)stream);
+}
+
+int dsa_compress_kv_write(const void* latent, int64_t latent_batch_stride, int B, int n, int D, const float* freqs,
+                          int rope_dim, uint8_t* rows, int64_t rows_batch_stride, uint8_t* scales,
+                          int64_t scales_batch_stride, int64_t row0, dsa_stream_t stream) {
+  dsa::Entry entry_;
+  if (B < 0 || n < 0 || D <= 0 || row0 < 0) return fail(DSA_ERR_SHAPE, "dsa_compress_kv_write: bad sizes");
+  if (D % 16) return fail(DSA_ERR_SHAPE, "dsa_compress_kv_write: D=%d is not a multiple of 16", D);
+  if (B == 0 || n == 0) return DSA_OK;
+  int rc = check_rope(freqs, rope_dim, D, "dsa_compress_kv_write");
+  if (rc) return rc;
+  if (!latent || !rows || !scales) return fail(DSA_ERR_NULL, "dsa_compress_kv_write: NULL pointer");
+  if (latent_batch_stride < (int64_t)n * D || rows_batch_stride < (row0 + n) * (int64_t)(D / 2) ||
+      scales_batch_stride < (row0 + n) * (int64_t)(D / 16))
+    return fail(DSA_ERR_SHAPE, "dsa_compress_kv_write: a batch stride is smaller than the rows it must hold");
+  if (((uintptr_t)rows & 7) || (rows_batch_stride & 7))
+    return fail(DSA_ERR_SHAPE, "dsa_compress_kv_write: cache rows must be 8-byte aligned");
+  return dsa::compress_kv_write_launch(latent, latent_batch_stride, B, n, D, rope_dim, freqs, rows, rows_batch_stride,
+                                       scales, scales_batch_stride, row0, (hipStream_t)stream);
 }
 
 int dsa_sparse_attn_select(const float* scores, int T, int index_topk, int start_pos, int ratio, int W,

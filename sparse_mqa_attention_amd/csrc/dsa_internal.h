@@ -133,6 +133,15 @@ struct DecIndex {
   float* scores_out;
 };
 
+// Inverse rotary embedding of the output pair (x, y) by (c, s) (`Attention.forward` rotates o's
+// last rope_head_dim dims back after the attention): (x + iy)(c - is).
+__device__ __forceinline__ void rope_rot_inv(float& x, float& y, float c, float s) {
+  const float nx = x * c + y * s;
+  const float ny = y * c - x * s;
+  x = nx;
+  y = ny;
+}
+
 __device__ __forceinline__ int visible_rows(int start_pos, int t, int ratio) {
   return (start_pos + t + 1) / ratio;
 }

@@ -435,15 +435,20 @@ int sparse_attn_decode_launch(const __bf16* q, const unsigned char* win, int64_t
                               int64_t win_rs, const unsigned char* comp, int64_t comp_n, int64_t comp_bs,
                               int64_t comp_rs, const float* sink, const int32_t* idx, int L, float scale_log2,
                               __bf16* o, int B, int S, int H, int D, bool fp4, void* workspace,
-                              const DecSelect* sel, const DecIndex* ix, hipStream_t st);
+                              const DecSelect* sel, const DecIndex* ix, const float* rope, int rope_dim,
+                              hipStream_t st);
 
 int sparse_attn_prefill_h16_launch(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
                                    const int32_t* idx, int L, float scale, void* o, int B, int S, int H, int D,
-                                   hipStream_t st);
+                                   const float* rope, int rope_dim, hipStream_t st);
+int rope_inverse_launch(void* o, int dtype, int B, int S, int H, int D, const float* freqs, int rope_dim,
+                        hipStream_t st);
 
+// rope (may be null): the inverse rotary table [S][rope_dim/2][2] applied to o's last rope_dim dims,
+// in the decode and prefill kernels' epilogue, otherwise as a pass after the attention
 int sparse_attn_bf16_launch(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
                             const int32_t* idx, int L, float scale, void* o, int B, int S, int H, int D,
-                            void* workspace, hipStream_t st) {
+                            void* workspace, const float* rope, int rope_dim, hipStream_t st) {
   AttnArgs a{};
   a.q = (const __bf16*)q;
   a.win = (const unsigned char*)win->rows;
@@ -471,19 +476,23 @@ int sparse_attn_bf16_launch(const void* q, const dsa_kv_src* win, const dsa_kv_s
   const int drc = sparse_attn_decode_launch(a.q, a.win, a.win_n, a.win_bs, a.win_rs, a.comp,
                                             comp && comp->rows ? comp->n_rows : 0, a.comp_bs, a.comp_rs, sink, idx,
                                             L, a.scale_log2, a.o, B, S, H, D, fp4, workspace, nullptr, nullptr,
-                                            st);
+                                            rope, rope_dim, st);
   if (drc != 0) return drc < 0 ? drc : 0;
   // prefill batches at head_dim 512 (bf16 or fp4 compressed rows): one workgroup per query
-  const int prc = sparse_attn_prefill_h16_launch(q, win, comp, sink, idx, L, scale, o, B, S, H, D, st);
+  const int prc = sparse_attn_prefill_h16_launch(q, win, comp, sink, idx, L, scale, o, B, S, H, D, rope, rope_dim,
+                                                 st);
   if (prc != 0) return prc < 0 ? prc : 0;
   sparse_attn_split(B, S, L, &a.nsplit, &a.split_slots);
+  int rc;
   switch (D) {
-    case 64: return fp4 ? launch_attn_h<64, true>(a, B, st) : launch_attn_h<64, false>(a, B, st);
-    case 128: return fp4 ? launch_attn_h<128, true>(a, B, st) : launch_attn_h<128, false>(a, B, st);
-    case 256: return fp4 ? launch_attn_h<256, true>(a, B, st) : launch_attn_h<256, false>(a, B, st);
-    case 512: return fp4 ? launch_attn_h<512, true>(a, B, st) : launch_attn_h<512, false>(a, B, st);
+    case 64: rc = fp4 ? launch_attn_h<64, true>(a, B, st) : launch_attn_h<64, false>(a, B, st); break;
+    case 128: rc = fp4 ? launch_attn_h<128, true>(a, B, st) : launch_attn_h<128, false>(a, B, st); break;
+    case 256: rc = fp4 ? launch_attn_h<256, true>(a, B, st) : launch_attn_h<256, false>(a, B, st); break;
+    case 512: rc = fp4 ? launch_attn_h<512, true>(a, B, st) : launch_attn_h<512, false>(a, B, st); break;
     default: return fail(DSA_ERR_UNSUPPORTED, "dsa_sparse_attn: bf16 head_dim %d not in {64,128,256,512}", D);
   }
+  if (rc || !rope) return rc;
+  return rope_inverse_launch(o, DSA_BF16, B, S, H, D, rope, rope_dim, st);
 }
 
 // Decode batches whose index rows the attention kernel can select itself (bf16 rows, the
@@ -499,7 +508,7 @@ int sparse_attn_bf16_select_launch(const void* q, const dsa_kv_src* win, const d
                                    win->batch_stride * 2, win->row_stride * 2, comp_rows,
                                    comp_rows ? comp->n_rows : 0, comp_rows ? comp->batch_stride * 2 : 0,
                                    comp_rows ? comp->row_stride * 2 : 0, sink, nullptr, L, scale * kLog2e,
-                                   (__bf16*)o, B, S, H, D, false, workspace, sel, ix, st);
+                                   (__bf16*)o, B, S, H, D, false, workspace, sel, ix, nullptr, 0, st);
 }
 
 size_t sparse_attn_bf16_workspace(int B, int S, int H, int D, int L, bool fp4) {

@@ -65,6 +65,8 @@ struct DecArgs {
   float* stats;    // [Q][NS][64][2] phase-A (max, sum)
   uint32_t* sync;  // [Qp][4] per query: score-exchange arrivals, rendezvous arrivals, departures
   int S, Q, Qp, RPS, Lp;
+  const float* rope;  // inverse rotary table of the output [S][rope_P][2] (cos, sin), or null
+  int rope_P;
   // index rows selected in the kernel (instead of read from idx): the query's scores [T], the
   // top-k size K, visibility (start_pos, ratio), window W with Wc columns, top-k offset; s == 0
   // writes the row to idx_out when that is set
@@ -518,6 +520,8 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
   if (kh == 0) {
     const float inv = flags[0] ? __builtin_nanf("") : 1.f / den;
     __bf16* op = a.o + ((int64_t)q * kDH + headB) * kDD + d0 + 4 * hf;
+    const int rope0 = kDD - 2 * a.rope_P;  // first rotated dim, kDD without a table
+    const float* rrow = a.rope ? a.rope + (int64_t)(q % a.S) * a.rope_P * 2 : nullptr;
 #pragma unroll
     for (int mb = 0; mb < C::NMB; ++mb)
 #pragma unroll
@@ -527,6 +531,13 @@ __global__ void __launch_bounds__(256) sparse_attn_decode_kernel(DecArgs a) {
         for (int i = 0; i < 4; ++i) {
           const int e = 4 * g + i;
           v[i] = (tot[mb][e] + red[((hb * C::NMB + mb) * 16 + e) * 64 + lane]) * inv;
+        }
+        // the lane's four dims d .. d+3 are two whole rotary pairs
+        const int d = d0 + 32 * mb + 8 * g + 4 * hf;
+        if (rrow && d >= rope0) {
+          const float4 cs = *reinterpret_cast<const float4*>(rrow + (d - rope0));
+          rope_rot_inv(v[0], v[1], cs.x, cs.y);
+          rope_rot_inv(v[2], v[3], cs.z, cs.w);
         }
         const bf16x4 ov = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
         *reinterpret_cast<bf16x4*>(op + 32 * mb + 8 * g) = ov;
@@ -631,7 +642,8 @@ int sparse_attn_decode_launch(const __bf16* q, const unsigned char* win, int64_t
                               int64_t win_rs, const unsigned char* comp, int64_t comp_n, int64_t comp_bs,
                               int64_t comp_rs, const float* sink, const int32_t* idx, int L, float scale_log2,
                               __bf16* o, int B, int S, int H, int D, bool fp4, void* workspace,
-                              const DecSelect* sel, const DecIndex* ix, hipStream_t st) {
+                              const DecSelect* sel, const DecIndex* ix, const float* rope, int rope_dim,
+                              hipStream_t st) {
   const DecPlan p = plan_decode(B * S, H, D, L, fp4);
   if (!p.ok) return 0;
   if (sel && (sel->T > 2048 || sel->T < 1 || sel->Wc + sel->K != L)) return 0;
@@ -670,6 +682,8 @@ int sparse_attn_decode_launch(const __bf16* q, const unsigned char* win, int64_t
   a.Qp = Qp;
   a.RPS = p.rps;
   a.Lp = p.lp;
+  a.rope = rope;
+  a.rope_P = rope ? rope_dim / 2 : 0;
   if (sel) {
     a.scores = sel->scores;
     a.T = sel->T;

@@ -65,6 +65,8 @@ struct H16Args {
   float scale_log2;
   __bf16* o;
   int S, H;
+  const float* rope;  // inverse rotary table [S][rope_P][2] (cos, sin), or null
+  int rope_P;         // rotated pairs at the end of each head's dims
 };
 
 // Source of the copies for -1 slots: a zero row, so every slot costs exactly one copy.
@@ -423,13 +425,20 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
   const float mf = fmaxf(m_run, sink2);
   const float f = exp2f(m_run - mf);
   const float rn = f / (l_tot * f + exp2f(sink2 - mf));
-  // lane (g, c) holds dims 16d + 4g .. 16d + 4g + 3 of head c
+  // lane (g, c) holds dims 16d + 4g .. 16d + 4g + 3 of head c: two whole rotary pairs
   __bf16* op = a.o + ((int64_t)qi * a.H + head) * kHD + 4 * g;
+  const int rope0 = kHD - 2 * a.rope_P;  // first rotated dim (a multiple of 16), kHD without a table
+  const float* rrow = a.rope ? a.rope + (int64_t)(qi % a.S) * a.rope_P * 2 : nullptr;
 #pragma unroll
   for (int d = 0; d < 32; ++d) {
-    const bf16x4 v = {(__bf16)(acc[d][0] * rn), (__bf16)(acc[d][1] * rn), (__bf16)(acc[d][2] * rn),
-                      (__bf16)(acc[d][3] * rn)};
-    *reinterpret_cast<bf16x4*>(op + 16 * d) = v;
+    float v[4] = {acc[d][0] * rn, acc[d][1] * rn, acc[d][2] * rn, acc[d][3] * rn};
+    if (rrow && 16 * d >= rope0) {
+      const float4 cs = *reinterpret_cast<const float4*>(rrow + (16 * d + 4 * g - rope0));
+      rope_rot_inv(v[0], v[1], cs.x, cs.y);
+      rope_rot_inv(v[2], v[3], cs.z, cs.w);
+    }
+    const bf16x4 ov = {(__bf16)v[0], (__bf16)v[1], (__bf16)v[2], (__bf16)v[3]};
+    *reinterpret_cast<bf16x4*>(op + 16 * d) = ov;
   }
 }
 
@@ -441,7 +450,7 @@ __global__ void __launch_bounds__(256) sparse_attn_prefill_h16_kernel(H16Args a)
 // launched, 0 if not, <0 on error.
 int sparse_attn_prefill_h16_launch(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
                                    const int32_t* idx, int L, float scale, void* o, int B, int S, int H, int D,
-                                   hipStream_t st) {
+                                   const float* rope, int rope_dim, hipStream_t st) {
   const int Q = B * S;
   if (D != kHD || H > 64 || L > kHMaxSlots || Q < 256) return 0;
   const bool fp4 = comp && comp->rows && comp->format == DSA_KV_FP4_E4M3_G16;
@@ -480,6 +489,8 @@ int sparse_attn_prefill_h16_launch(const void* q, const dsa_kv_src* win, const d
   a.o = (__bf16*)o;
   a.S = S;
   a.H = H;
+  a.rope = rope;
+  a.rope_P = rope ? rope_dim / 2 : 0;
   if (fp4)
     hipLaunchKernelGGL(sparse_attn_prefill_h16_kernel<true>, dim3(Q), dim3(256), 0, st, a);
   else

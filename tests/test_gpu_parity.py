@@ -917,3 +917,72 @@ def test_two_level_step(name):
     err = max_abs_err(o.float().cpu().numpy(), exp_o)
     _log(f"  top-k rules {rules}, attention max abs err {err:.3e}")
     assert err <= ATTN_TOL["bf16"], err
+
+
+# ------------------------------------------------------------------------ output epilogue and cache write
+@pytest.mark.parametrize("B,S,H,D,nw,nc,L,rd,dtype,fp4,kernel", [
+    (4, 1, 64, 512, 128, 600, 640, 64, "bf16", False, "sparse_attn_decode<NS=16>"),  # fused epilogue
+    (32, 1, 64, 512, 128, 2048, 640, 64, "bf16", False, "sparse_attn_decode<NS=8>"),
+    (1, 300, 64, 512, 300, 75, 200, 64, "bf16", False, "sparse_attn_prefill_h16"),    # fused epilogue
+    (1, 260, 64, 512, 260, 65, 100, 128, "bf16", True, "sparse_attn_prefill_h16"),
+    (2, 3, 16, 512, 40, 30, 77, 64, "bf16", False, "sparse_attn_bf16"),               # separate pass
+    (1, 5, 4, 64, 20, 16, 24, 16, "f32", False, "sparse_attn_f32"),
+])
+def test_sparse_attn_rope(B, S, H, D, nw, nc, L, rd, dtype, fp4, kernel):
+    """The attention output with its inverse rotary embedding (`Attention.forward`) against the
+    oracle's exact attention followed by its exact inverse rotation."""
+    dsa = _dsa()
+    _log(f"attention + inverse rope B={B} S={S} H={H} D={D} L={L} rd={rd} {dtype} fp4={fp4}")
+    g = torch.Generator().manual_seed(B + S + L + rd)
+    dt = torch.float32 if dtype == "f32" else torch.bfloat16
+    q = torch.randn(B, S, H, D, generator=g).to(dt)
+    kv_win = torch.randn(B, nw, D, generator=g).to(dt)
+    sink = torch.randn(H, generator=g)
+    if fp4:
+        packed, scales = dsa_synth.encode_fp4_e2m1_e4m3(torch.randn(B, nc, D, generator=g), 16)
+        comp64, comp_dev, sc_dev = oracle.fp4_rows_decode(packed, scales), packed.to(DEV), scales.to(DEV)
+    else:
+        comp = torch.randn(B, nc, D, generator=g).to(dt)
+        comp64, comp_dev, sc_dev = comp, comp.to(DEV), None
+    idx = _rand_idx(np.random.default_rng(L), B, S, L, nw + nc)
+    freqs = dsa_synth.rope_freqs(np.arange(S) + 1000 * (S == 1) * 8 + 17, rd)
+    o = dsa.dsa_sparse_attn_rope(q.to(DEV), kv_win.to(DEV), comp_dev, sink.to(DEV), torch.from_numpy(idx).to(DEV),
+                                 D ** -0.5, freqs.to(DEV), comp_scales=sc_dev)
+    n, names = _launched()
+    _log(f"  launches: {n} {names}")
+    assert names.startswith(kernel), names
+    if kernel in ("sparse_attn_decode<NS=16>", "sparse_attn_decode<NS=8>", "sparse_attn_prefill_h16"):
+        assert n == 1, names  # rotated in the attention kernel's epilogue
+    else:
+        assert names.endswith("rope_inverse"), names
+    exp = oracle.rope_rotate(oracle.sparse_attn(q, oracle.kv_concat(kv_win, comp64), sink, idx, D ** -0.5),
+                             freqs.numpy(), inverse=True)
+    err = max_abs_err(o.float().cpu().numpy(), exp)
+    _log(f"  max abs err {err:.3e}")
+    assert err <= ATTN_TOL[dtype], err
+
+
+@pytest.mark.parametrize("B,n,D,rd,row0,R", [(2, 37, 512, 64, 5, 50), (1, 8192, 512, 64, 0, 8192),
+                                             (3, 3, 64, 16, 11, 20)])
+def test_compress_kv_write(B, n, D, rd, row0, R):
+    """`_compress_kv`'s cache write: rotated, quantised and stored bytes equal the oracle's bit for
+    bit (every code is decided in the page's float32 steps), rows outside [row0, row0+n) untouched."""
+    dsa = _dsa()
+    _log(f"compress kv write B={B} n={n} D={D} rd={rd} rows {row0}..{row0 + n} of {R}")
+    g = torch.Generator().manual_seed(n + D + row0)
+    lat = (torch.randn(B, n, D, generator=g) * torch.exp(torch.randn(B, n, 1, generator=g))).to(torch.bfloat16)
+    # a group of exact e2m1 midpoints (scale 2^-1 from amax 3): the ties go to the even code
+    if D - rd >= 16:
+        lat[0, 0, :16] = torch.tensor([3.0, 0.125, 0.375, 0.625, 0.875, 1.25, 1.75, 2.5,
+                                       -0.125, -0.375, -1.25, -2.5, 0.0, -0.0, 1.0, -3.0]).to(torch.bfloat16)
+    freqs = dsa_synth.rope_freqs(np.arange(n) * 4 + 3, rd)
+    rows = torch.full((B, R, D // 2), 0xAB, dtype=torch.uint8, device=DEV)
+    scales = torch.full((B, R, D // 16), 0xCD, dtype=torch.uint8, device=DEV)
+    dsa.dsa_compress_kv_write(lat.to(DEV), freqs.to(DEV), rows, scales, row0)
+    assert _launched()[1] == "compress_kv_write"
+    exp_p, exp_s = oracle.compress_kv_write(lat.float().numpy(), freqs.numpy(), rd)
+    got_p, got_s = rows.cpu().numpy(), scales.cpu().numpy()
+    np.testing.assert_array_equal(got_p[:, row0:row0 + n], exp_p)
+    np.testing.assert_array_equal(got_s[:, row0:row0 + n], exp_s)
+    assert np.all(got_p[:, :row0] == 0xAB) and np.all(got_p[:, row0 + n:] == 0xAB)
+    assert np.all(got_s[:, :row0] == 0xCD) and np.all(got_s[:, row0 + n:] == 0xCD)
