@@ -130,7 +130,21 @@ candidate_blocks_kernel(const float* __restrict__ scores, int S, int T, int star
   const int nw = (nblk + 31) >> 5;
   for (int i = tid; i < nw; i += 1024) bw[i] = 0u;
   const float* srow = scores + (int64_t)row * T;
-  for (int i = tid; i < cb; i += 1024) {
+  // whole visible blocks of 4k positions in 16-byte loads (consecutive threads, consecutive blocks),
+  // the rest one score at a time
+  const bool vec = lbs >= 2 && (T & 3) == 0 && ((uintptr_t)srow & 15) == 0;
+  const int full = vec ? c >> lbs : 0;  // blocks wholly visible
+  for (int i = tid; i < full; i += 1024) {
+    const float4* p = reinterpret_cast<const float4*>(srow + (i << lbs));
+    float4 v = p[0];
+    float m = fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w));
+    for (int k = 1; k < (1 << (lbs - 2)); ++k) {
+      v = p[k];
+      m = fmaxf(m, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+    }
+    bmax[i] = m;
+  }
+  for (int i = full + tid; i < cb; i += 1024) {
     const int e = min((i + 1) << lbs, c);
     float m = srow[i << lbs];
     for (int j = (i << lbs) + 1; j < e; ++j) m = fmaxf(m, srow[j]);
