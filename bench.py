@@ -62,7 +62,7 @@ HOST_CORES = 16  # the CPU share of one GPU on the benchmark machines
 KERNEL_SOURCES = {
     "decode": ["sparse_mqa_attention_amd/csrc/sparse_attn_decode.hip", "sparse_mqa_attention_amd/csrc/dsa_internal.h",
                "sparse_mqa_attention_amd/csrc/topk_block.h", "sparse_mqa_attention_amd/csrc/index_tile.h"],
-    "prefill": ["sparse_mqa_attention_amd/csrc/sparse_attn_prefill_h16.hip",
+    "prefill": ["sparse_mqa_attention_amd/csrc/sparse_attn_prefill.hip",
                 "sparse_mqa_attention_amd/csrc/dsa_internal.h"],
 }
 

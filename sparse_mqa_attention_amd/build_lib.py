@@ -11,17 +11,16 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libdsa.so")
 SOURCES = ["abi.cpp", "index_scores.hip", "index_scores_prefill.hip", "index_scores_mxfp4.hip", "topk.hip", "sparse_attn.hip", "sparse_attn_decode.hip",
-           "sparse_attn_prefill_h16.hip", "sparse_attn_f32.hip", "noalloc.hip",
+           "sparse_attn_prefill.hip", "sparse_attn_f32.hip", "noalloc.hip",
            "epilogue.hip"]
 ARCH = "gfx950"
 # packed fp32 VALU forms are kept out of the generated code
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
              "-packed-fp32-ops", "-Wall", "-Wno-unused-result"]
-# per-source additions: kernels whose MFMA accumulators feed VALU work every tile keep them in
-# VGPRs (the prefill attention rescales them; the prefill index epilogue rectifies and weights
-# them), since AGPR accumulators would be copied out first
-EXTRA_FLAGS = {"sparse_attn_prefill_h16.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"],
-               "index_scores_prefill.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
+# per-source additions: the prefill index kernel's MFMA accumulators feed VALU work every tile
+# (its epilogue rectifies and weights them), so they stay in VGPRs rather than AGPRs that would be
+# copied out first
+EXTRA_FLAGS = {"index_scores_prefill.hip": ["-mllvm", "--amdgpu-mfma-vgpr-form"]}
 
 
 def _hipcc() -> str:

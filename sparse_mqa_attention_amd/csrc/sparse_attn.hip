@@ -438,9 +438,9 @@ int sparse_attn_decode_launch(const __bf16* q, const unsigned char* win, int64_t
                               const DecSelect* sel, const DecIndex* ix, const float* rope, int rope_dim,
                               hipStream_t st);
 
-int sparse_attn_prefill_h16_launch(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
-                                   const int32_t* idx, int L, float scale, void* o, int B, int S, int H, int D,
-                                   const float* rope, int rope_dim, hipStream_t st);
+int sparse_attn_prefill_launch(const void* q, const dsa_kv_src* win, const dsa_kv_src* comp, const float* sink,
+                               const int32_t* idx, int L, float scale, void* o, int B, int S, int H, int D,
+                               const float* rope, int rope_dim, hipStream_t st);
 int rope_inverse_launch(void* o, int dtype, int B, int S, int H, int D, const float* freqs, int rope_dim,
                         hipStream_t st);
 
@@ -479,8 +479,7 @@ int sparse_attn_bf16_launch(const void* q, const dsa_kv_src* win, const dsa_kv_s
                                             rope, rope_dim, st);
   if (drc != 0) return drc < 0 ? drc : 0;
   // prefill batches at head_dim 512 (bf16 or fp4 compressed rows): one workgroup per query
-  const int prc = sparse_attn_prefill_h16_launch(q, win, comp, sink, idx, L, scale, o, B, S, H, D, rope, rope_dim,
-                                                 st);
+  const int prc = sparse_attn_prefill_launch(q, win, comp, sink, idx, L, scale, o, B, S, H, D, rope, rope_dim, st);
   if (prc != 0) return prc < 0 ? prc : 0;
   sparse_attn_split(B, S, L, &a.nsplit, &a.split_slots);
   int rc;

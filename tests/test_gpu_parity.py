@@ -540,8 +540,8 @@ def test_sparse_attn_decode_path(B, S, L, nc, inval, kernel):
 # ------------------------------------------------------------------------ KV sources sliced from larger caches
 @pytest.mark.parametrize("B,S,sp,nw,nc,L,fp4,kind", [
     (4, 1, 4095, 128, 1024, 640, False, "sparse_attn_decode<NS="),  # decode kernel
-    (2, 200, 0, 200, 75, 200, False, "sparse_attn_prefill_h16"),   # one workgroup per query
-    (2, 160, 0, 160, 65, 100, True, "sparse_attn_prefill_h16"),     # fp4 rows and scales sliced
+    (2, 200, 0, 200, 75, 200, False, "sparse_attn_prefill"),   # one workgroup per query
+    (2, 160, 0, 160, 65, 100, True, "sparse_attn_prefill"),     # fp4 rows and scales sliced
     (2, 2, 0, 40, 30, 77, False, "sparse_attn_bf16"),              # general kernel (H=16)
 ])
 def test_sparse_attn_cache_slices(B, S, sp, nw, nc, L, fp4, kind):
@@ -923,8 +923,8 @@ def test_two_level_step(name):
 @pytest.mark.parametrize("B,S,H,D,nw,nc,L,rd,dtype,fp4,kernel", [
     (4, 1, 64, 512, 128, 600, 640, 64, "bf16", False, "sparse_attn_decode<NS=16>"),  # fused epilogue
     (32, 1, 64, 512, 128, 2048, 640, 64, "bf16", False, "sparse_attn_decode<NS=8>"),
-    (1, 300, 64, 512, 300, 75, 200, 64, "bf16", False, "sparse_attn_prefill_h16"),    # fused epilogue
-    (1, 260, 64, 512, 260, 65, 100, 128, "bf16", True, "sparse_attn_prefill_h16"),
+    (1, 300, 64, 512, 300, 75, 200, 64, "bf16", False, "sparse_attn_prefill"),    # fused epilogue
+    (1, 260, 64, 512, 260, 65, 100, 128, "bf16", True, "sparse_attn_prefill"),
     (2, 3, 16, 512, 40, 30, 77, 64, "bf16", False, "sparse_attn_bf16"),               # separate pass
     (1, 5, 4, 64, 20, 16, 24, 16, "f32", False, "sparse_attn_f32"),
 ])
@@ -951,7 +951,7 @@ def test_sparse_attn_rope(B, S, H, D, nw, nc, L, rd, dtype, fp4, kernel):
     n, names = _launched()
     _log(f"  launches: {n} {names}")
     assert names.startswith(kernel), names
-    if kernel in ("sparse_attn_decode<NS=16>", "sparse_attn_decode<NS=8>", "sparse_attn_prefill_h16"):
+    if kernel in ("sparse_attn_decode<NS=16>", "sparse_attn_decode<NS=8>", "sparse_attn_prefill"):
         assert n == 1, names  # rotated in the attention kernel's epilogue
     else:
         assert names.endswith("rope_inverse"), names
