@@ -5,21 +5,22 @@
 // One workgroup of two waves per query; wave w owns heads 32w..32w+31 over the whole head_dim, so
 // a wave's logits are complete without any exchange and the only barrier per tile is the one that
 // hands a ring slot over.  Each KV row staged in LDS is read by the two waves twice (as K and as
-// V), and every read feeds 32 heads.  A workgroup takes ~76 KiB of LDS and one SIMD per wave, so
-// two queries share a CU: one query's fixed costs (index row, q, the first copies, the output)
+// V), and every read feeds 32 heads.  A workgroup takes under 80 KiB of LDS and one SIMD per wave,
+// so two queries share a CU: one query's fixed costs (index row, q, the first copies, the output)
 // overlap the other's tiles.
 //  * rows are gathered with 16-byte direct global->LDS copies into a ring of two 32-row tiles; the
 //    copies of tile k+1 go out as soon as tile k-1 has left the ring; each wave copies 16 rows per
 //    tile, one wave instruction per row, with the row address formed in scalar registers from the
 //    index row;
-//  * tile rows are 1056 bytes apart, which keeps both operand reads below free of bank conflicts;
-//  * S^T = K . Q^T on v_mfma_f32_32x32x16_bf16 (32 rows x 32 heads per instruction, two chains):
-//    K from LDS (ds_read_b128), the wave's 32 query heads resident in registers as the B operand.
-//    Lane (hf, c) of the accumulator holds 16 rows of head c, which is the B operand of
-//    O^T = V^T . P^T once the tile rows are taken in the matching order (k-step 0: rows 4hf..+3
-//    and 8+4hf..+3; k-step 1: those plus 16), so the probabilities never leave their lane;
-//  * V^T comes from two ds_read_b64_tr_b16 per operand; O^T is 16 accumulators of 32 dims x
-//    32 heads (the wave's AGPRs);
+//  * tile rows are 1088 bytes apart with the chunks of each 64-byte block XOR-permuted per row
+//    (p_swz), which keeps both operand reads below free of bank conflicts;
+//  * S^T = K . Q^T as four v_mfma_f32_16x16x32_bf16 blocks per k-step (row half x head half, one
+//    chain each): K from LDS (ds_read_b128), the wave's 32 query heads resident in VGPRs as the B
+//    operand.  Lane (g, c) of the accumulators holds rows 4g..4g+3 (+16) of heads c and 16 + c;
+//  * O^T = V^T . P^T on v_mfma_f32_32x32x16_bf16: one permlane16 swap per register pair between
+//    16-lane groups turns the probabilities into its B operand (rows 8hf..8hf+7 of head lane%32 per
+//    k-step), so they never go through LDS; V^T comes from two ds_read_b64_tr_b16 per operand; O^T
+//    is 16 accumulators of 32 dims x 32 heads (the wave's AGPRs);
 //  * online softmax in base 2 with a lazily raised running max (the accumulators are rescaled only
 //    when a tile raises a head's max by more than 8);
 //  * fp4 compressed rows (e2m1 nibbles + one E4M3 scale per 16) are copied as they lie (256 nibble
@@ -73,7 +74,9 @@ __device__ __forceinline__ uint32_t p_swz(int r) { return (uint32_t)((r >> 2) & 
 //  * a dependent MFMA reading its own accumulator as SrcC (same opcode, same registers) needs none;
 //  * VALU reads of an MFMA result wait s_nop 15 (16 states, more than the 8-pass 16x16x32 MFMA
 //    requires) or s_nop 15 + s_nop 3 (20 states, for the 16-pass 32x32x16);
-//  * an MFMA reading a VGPR (or AGPR) written by a VALU instruction waits s_nop 1 (2 states).
+//  * an MFMA reading a VGPR (or AGPR) written by a VALU instruction waits s_nop 1 (2 states): an
+//    empty-bodied statement that emits it and takes the written registers as in-out operands
+//    stands between the writes and every MFMA that reads them.
 // Operands loaded from LDS or memory are covered by the s_waitcnt the compiler places before the
 // statement that reads them.
 __device__ __forceinline__ f32x4 qk_first(bf16x8 a, bf16x8 b) {
@@ -86,9 +89,6 @@ __device__ __forceinline__ void qk_next(f32x4& d, bf16x8 a, bf16x8 b) {
 }
 __device__ __forceinline__ void pv_mfma(f32x16& d, bf16x8 a, bf16x8 b) {
   asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
-}
-__device__ __forceinline__ void pv_mfma_first(f32x16& d, bf16x8 a, bf16x8 b) {
-  asm("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(d) : "v"(a), "v"(b));
 }
 
 typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2;
@@ -432,7 +432,7 @@ __global__ void __launch_bounds__(kPThreads) sparse_attn_prefill_kernel(PArgs a)
           t *= ao;
           asm volatile("" : "+v"(t));
           acc[d] = t;
-          asm volatile("" : "+a"(acc[d]));
+          asm volatile("s_nop 1" : "+a"(acc[d]));
         }
       }
     }
@@ -471,6 +471,7 @@ __global__ void __launch_bounds__(kPThreads) sparse_attn_prefill_kernel(PArgs a)
       swap16(xs[ks][1], ys[ks][1]);
       const u32x4 w = {xs[ks][0], xs[ks][1], ys[ks][0], ys[ks][1]};
       pb[ks] = __builtin_bit_cast(bf16x8, w);
+      asm("s_nop 1" : "+v"(pb[ks]));  // VALU writes above, MFMA reads below
     }
 
     // ---- O^T += V^T . P^T over the whole head_dim: 16 chains ----
@@ -478,11 +479,7 @@ __global__ void __launch_bounds__(kPThreads) sparse_attn_prefill_kernel(PArgs a)
     for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
       for (int d = 0; d < 16; ++d) {
-        const bf16x8 v = (ks == 0 && d < kVPre) ? vpre[d] : vread(vp, ks, d);
-        if (ks == 0 && d == 0)
-          pv_mfma_first(acc[d], v, pb[ks]);
-        else
-          pv_mfma(acc[d], v, pb[ks]);
+        pv_mfma(acc[d], (ks == 0 && d < kVPre) ? vpre[d] : vread(vp, ks, d), pb[ks]);
       }
     }
   }
