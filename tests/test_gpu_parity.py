@@ -241,7 +241,7 @@ def _rand_idx(rng, B, S, L, n, frac_invalid=0.15):
     (1, 256, 40, 512, 256, 100, 77, "bf16", True),
     (1, 264, 16, 512, 264, 50, 33, "bf16", False),
     (1, 256, 64, 512, 256, 1000, 1025, "bf16", False),
-    (1, 288, 40, 512, 288, 90, 70, "bf16", False),  # a wave with half of its 16 heads
+    (1, 288, 40, 512, 288, 90, 70, "bf16", False),  # heads 32..39: a wave with 8 of its 32 heads
     # 1024+ queries, a count no workgroup size divides
     (1, 1027, 64, 512, 1027, 80, 160, "bf16", False),
     (1, 1030, 40, 512, 1030, 60, 70, "bf16", True),
