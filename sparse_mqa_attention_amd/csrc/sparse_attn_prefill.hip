@@ -125,8 +125,9 @@ __device__ __forceinline__ void p_dma16(const void* sbase, uint32_t voff, const 
 }
 
 // Workgroup i runs on XCD i mod 8, and each XCD has its own L2.  Runs of 64 consecutive queries
-// (whose window rows and most top-k rows coincide) go to one XCD, and the runs are taken from the
-// last query down: later queries see more rows, so the heaviest go first.
+// (whose window rows coincide, and whose top-k rows tend to overlap in real sequences) go to one
+// XCD, and the runs are taken from the last query down: later queries see more rows, so the
+// heaviest go first.
 __device__ __forceinline__ int prefill_query(int bid, int Q) {
   constexpr int kRun = 64;
   const int full = Q / (8 * kRun) * (8 * kRun);
